@@ -1,0 +1,215 @@
+/*
+ * moev.h -- C ABI of the MI355X (gfx950) library for the FastMTP verify step
+ * through a Jina-OCR-v1 style mixture-of-experts decoder.
+ *
+ * Sources (web pages on Jina-OCR-v1):
+ *   [P1] "Jina AI's jina-ocr-v1 Is Selling Throughput, Not the OCR Crown"
+ *        (kg.zhiyong.dev explainer);
+ *   [P2] aipolix.com news analysis of Jina-OCR-v1 (document parsing, FastMTP,
+ *        non-commercial weights);
+ *   [P3] "Jina-OCR-v1: Efficient Document Parsing with Speculative Decoding and
+ *        Dense Verifiable Rewards" (evolve.pub review of the arXiv paper).
+ *
+ * Conventions for every entry point
+ *   - Device pointers are caller-owned device memory (for example torch
+ *     tensors), row-major and contiguous, 16-byte aligned.  The library
+ *     allocates nothing and keeps no state between calls; scratch space comes
+ *     from a caller-provided workspace sized by the matching *_workspace_size.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     the call returns without synchronising.  No entry point synchronises the
+ *     host, so a step can be captured in a HIP graph.
+ *   - Arguments are validated before any HIP call.  A failed check returns a
+ *     status code and enqueues nothing; moev_last_error() then describes it.
+ *     T == 0 (or B == 0) is a valid no-op.  Indices a kernel reads from device
+ *     memory (token ids, expert ids, pair ids) are a caller contract: a value
+ *     out of range is clamped so that every memory access stays in bounds, and
+ *     the result is then unspecified.
+ *   - After the launches, a failure reported by hipGetLastError() is returned
+ *     as MOEV_ERR_HIP.
+ *   - Calls on one stream run in order; concurrent calls on different streams
+ *     must not share output or workspace buffers.
+ *
+ * Shapes: T tokens, H hidden, E routed experts, k routed experts per token,
+ * ns shared experts, G = E + ns expert groups (routed 0..E-1, shared E..G-1),
+ * S = k + ns slots per token, I expert intermediate width, V vocabulary.
+ * Limits: 1 <= E <= 64, 1 <= k <= E, 0 <= ns <= 8, H and I multiples of 64,
+ * 64 <= H <= 4032, 64 <= I <= 8192, T * S < 2^31.
+ * Weight/operand type `dt`: MOEV_BF16 (bf16 bit patterns, GEMMs on bf16 MFMA
+ * with fp32 accumulation) or MOEV_F32 (fp32 MFMA).  Residual stream, router
+ * weights out, expert outputs and logits are always fp32.
+ */
+#ifndef MOEV_H
+#define MOEV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOEV_OK = 0,
+  MOEV_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or shape */
+  MOEV_ERR_UNSUPPORTED = 2, /* shape outside the limits above, unknown dtype */
+  MOEV_ERR_WORKSPACE = 3,   /* workspace pointer null or too small */
+  MOEV_ERR_HIP = 4          /* the HIP runtime reported an error */
+} moev_status;
+
+typedef enum { MOEV_F32 = 0, MOEV_BF16 = 1 } moev_dtype;
+
+/* Text for a status code (static storage). */
+const char* moev_status_string(int status);
+/* Detail of the last failed call on this host thread ("" if none). */
+const char* moev_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int moev_version(void);
+
+/*
+ * moe_embed -- residual stream input: h_out[t, :] = emb[tokens[t], :] as fp32.
+ *   tokens  int32 [T] device, each in [0, V)
+ *   emb     dt [V, H] device
+ *   h_out   fp32 [T, H] device (written)
+ * Glue in front of the decoder layers; the pages do not describe the
+ * embedding, and the synthetic decoder uses an untied table.
+ */
+moev_status moe_embed(const int32_t* tokens, const void* emb, int T, int H, int V, int dt,
+                      float* h_out, void* stream);
+
+/*
+ * moe_route -- pre-norm RMSNorm and the top-k router of one MoE layer.
+ * [P1] "The speed comes from three layers working together": each token is
+ * routed to the top 6 of 64 routed experts.
+ *   x = h / sqrt(mean(h^2) + eps) * norm_w          (fp32)
+ *   logits = x . w_router^T (+ bias)                (fp32, x unrounded)
+ *   topk_idx[t, r] = expert with the r-th largest logit (ties: lower index),
+ *   topk_w[t, r]   = softmax(logits)[that expert] renormalised over the k
+ *                    chosen experts (the k weights sum to 1).
+ *   h        fp32 [T, H]
+ *   norm_w   dt [H] or NULL (gain 1)
+ *   w_router dt [E, H]
+ *   bias     fp32 [E] or NULL (added to the logits before softmax)
+ *   x_out    dt [T, H] (written): x rounded to dt, the expert GEMM operand
+ *   topk_idx int32 [T, k], topk_w fp32 [T, k] (written, rank order)
+ *   logits_out fp32 [T, E] or NULL (written when non-NULL; for checking)
+ */
+moev_status moe_route(const float* h, const void* norm_w, float eps, const void* w_router,
+                      const float* bias, int T, int H, int E, int k, int dt, void* x_out,
+                      int32_t* topk_idx, float* topk_w, float* logits_out, void* stream);
+
+/*
+ * moe_permute -- group the (token, slot) pairs by expert.
+ * Pair p = t*S + slot.  Slot r < k belongs to routed expert topk_idx[t, r];
+ * slot k+s to shared expert s (group E+s), which therefore holds every token.
+ *   group_offsets int32 [G+1] (written): exclusive prefix sum of group sizes
+ *   sorted_src    int32 [T*S] (written): pair ids, group by group, increasing
+ *                 pair id within a group (a stable counting sort)
+ */
+moev_status moe_permute(const int32_t* topk_idx, int T, int k, int E, int ns,
+                        int32_t* group_offsets, int32_t* sorted_src, void* stream);
+
+/*
+ * moe_grouped_ffn -- SwiGLU experts over the permuted pairs, weighted.
+ * [P1] same section: 64 routed and two shared experts; shared experts are
+ * always on.  For every pair (t, slot) in group g:
+ *   a = SiLU(w_gate[g] . x[t]) * (w_up[g] . x[t])   (a rounded to dt)
+ *   y_slots[t, slot, :] = wgt * (w_down[g] . a)
+ * with wgt = topk_w[t, slot] for a routed slot and 1 for a shared slot.
+ *   x        dt [T, H] (moe_route's x_out)
+ *   sorted_src, group_offsets from moe_permute
+ *   topk_w   fp32 [T, k]
+ *   w_gate, w_up  dt [G, I, H];  w_down dt [G, H, I]  (shared experts last)
+ *   y_slots  fp32 [T, S, H] (written, every slot)
+ *   ws       workspace of moe_grouped_ffn_workspace_size() bytes
+ * Each output element is a fixed-order fp32 sum, so a token's result does not
+ * depend on the other tokens in the batch.
+ */
+size_t moe_grouped_ffn_workspace_size(int T, int I, int k, int ns, int dt);
+moev_status moe_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* group_offsets,
+                            const float* topk_w, const void* w_gate, const void* w_up,
+                            const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
+                            float* y_slots, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- residual add of every slot's expert output:
+ *   h_out[t, :] = h_in[t, :] + sum_{slot = 0..S-1} y_slots[t, slot, :]
+ * summed in slot order (routed by rank, then shared).  h_in NULL: no residual.
+ * h_out may alias h_in.
+ */
+moev_status moe_combine(const float* y_slots, const float* h_in, int T, int H, int S,
+                        float* h_out, void* stream);
+
+/*
+ * lmhead_argmax -- final RMSNorm, LM head and greedy token.
+ * Greedy decoding is the rule the verification must reproduce ([P1] "Why
+ * FastMTP fits OCR particularly well"; [P2] "What the speed claims actually
+ * measure").
+ *   x = RMSNorm(h) * norm_f rounded to dt;  logits = w_lm . x  (fp32 acc)
+ *   argmax_out[t] = lowest index of the largest logit
+ *   h        fp32 [T, H];  norm_f dt [H] or NULL;  w_lm dt [V, H]
+ *   argmax_out int32 [T] (written);  max_out fp32 [T] or NULL
+ *   logits_out fp32 [T, V] or NULL (written when non-NULL; for checking)
+ *   ws       workspace of lmhead_argmax_workspace_size() bytes
+ */
+size_t lmhead_argmax_workspace_size(int T, int H, int V, int dt);
+moev_status lmhead_argmax(const float* h, const void* norm_f, float eps, const void* w_lm,
+                          int T, int H, int V, int dt, int32_t* argmax_out, float* max_out,
+                          float* logits_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mtp_verify -- FastMTP greedy prefix acceptance ([P1] "The speed comes from
+ * three layers working together" and "Why FastMTP fits OCR particularly
+ * well"; [P3] "Scope & Claims", Section 3.1 / Eq. 2).
+ *   tokens[b, :] = (last committed token, d_1 .. d_K)   int32 [B, K+1]
+ *   greedy[b, j] = greedy token after tokens[b, j]        int32 [B, K+1]
+ *   n_accept[b]  = largest n <= K with d_i == greedy[b, i-1] for all i <= n
+ *   commit[b, :] = d_1 .. d_n, greedy[b, n], then -1 padding   int32 [B, K+1]
+ *   commit_len[b] = n + 1;  next_last[b] = greedy[b, n]
+ * commit_len / next_last may be NULL.
+ */
+moev_status mtp_verify(const int32_t* tokens, const int32_t* greedy, int B, int K,
+                       int32_t* n_accept, int32_t* commit, int32_t* commit_len,
+                       int32_t* next_last, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Whole verify step: embed -> n_layers x (route, permute, grouped FFN,
+ * combine) -> lmhead_argmax -> mtp_verify, enqueued on one stream.          */
+
+typedef struct moev_layer_weights {
+  const void* norm;     /* dt [H] or NULL */
+  const void* w_router; /* dt [E, H] */
+  const float* bias;    /* fp32 [E] or NULL */
+  const void* w_gate;   /* dt [G, I, H] */
+  const void* w_up;     /* dt [G, I, H] */
+  const void* w_down;   /* dt [G, H, I] */
+} moev_layer_weights;
+
+typedef struct moev_model {
+  int hidden, n_routed, inter, top_k, n_shared, vocab, n_layers;
+  int dtype;    /* moev_dtype */
+  float eps;    /* RMSNorm epsilon */
+  const void* emb;    /* dt [V, H] */
+  const void* norm_f; /* dt [H] or NULL */
+  const void* w_lm;   /* dt [V, H] */
+  const moev_layer_weights* layers; /* host array of n_layers entries */
+} moev_model;
+
+/*
+ * moev_verify_step -- one FastMTP verification pass of B sequences, each
+ * bringing its last committed token and K drafts (T = B*(K+1) tokens).
+ *   tokens   int32 [B, K+1] device
+ *   greedy   int32 [B, K+1] (written): greedy token after every input token
+ *   n_accept, commit, commit_len, next_last: as mtp_verify
+ *   ws       workspace of moev_verify_step_workspace_size() bytes
+ * K = 0 is plain greedy decoding of one token per sequence.
+ */
+size_t moev_verify_step_workspace_size(const moev_model* m, int B, int K);
+moev_status moev_verify_step(const moev_model* m, const int32_t* tokens, int B, int K,
+                             int32_t* greedy, int32_t* n_accept, int32_t* commit,
+                             int32_t* commit_len, int32_t* next_last, void* ws, size_t ws_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEV_H */

@@ -1,0 +1,83 @@
+"""ctypes loader for libmoev.so, the C-ABI HIP library.
+
+Fails loudly: if the shared library is missing or does not export a symbol
+the header declares, importing the binding raises.  There is no fallback
+path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoev.so")
+
+c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("norm", c_void_p), ("w_router", c_void_p), ("bias", c_void_p),
+                ("w_gate", c_void_p), ("w_up", c_void_p), ("w_down", c_void_p)]
+
+
+class Model(ctypes.Structure):
+    _fields_ = [("hidden", c_int), ("n_routed", c_int), ("inter", c_int), ("top_k", c_int),
+                ("n_shared", c_int), ("vocab", c_int), ("n_layers", c_int), ("dtype", c_int),
+                ("eps", c_float), ("emb", c_void_p), ("norm_f", c_void_p), ("w_lm", c_void_p),
+                ("layers", ctypes.POINTER(LayerWeights))]
+
+
+# name -> (restype, argtypes); mirrors include/moev.h
+SIGNATURES = {
+    "moev_status_string": (ctypes.c_char_p, [c_int]),
+    "moev_last_error": (ctypes.c_char_p, []),
+    "moev_version": (c_int, []),
+    "moe_embed": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "moe_route": (c_int, [c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_int, c_int, c_int,
+                          c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_permute": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "moe_grouped_ffn_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "moe_grouped_ffn": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_combine": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "lmhead_argmax_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "lmhead_argmax": (c_int, [c_void_p, c_void_p, c_float, c_void_p, c_int, c_int, c_int, c_int,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mtp_verify": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                           c_void_p, c_void_p]),
+    "moev_verify_step_workspace_size": (c_size_t, [ctypes.POINTER(Model), c_int, c_int]),
+    "moev_verify_step": (c_int, [ctypes.POINTER(Model), c_void_p, c_int, c_int, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                 c_void_p]),
+}
+
+_lib = None
+
+
+class MoevError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = load()
+        detail = lib.moev_last_error().decode()
+        super().__init__(f"{fn}: {lib.moev_status_string(status).decode()} ({status}): {detail}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libmoev.so once and bind every exported entry point."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m moe_decoder_greedy_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)  # AttributeError if the symbol is not exported
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoevError(fn, status)

@@ -1,0 +1,31 @@
+// Internal launchers and validators shared between the per-call entry points
+// and the whole-step driver.  Launchers do no validation.
+#pragma once
+
+#include "common.h"
+
+namespace moev {
+
+void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, int dt, float* h,
+                  hipStream_t s);
+void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,
+                  const float* bias, int T, int H, int E, int k, int dt, void* x_out,
+                  int32_t* topk_idx, float* topk_w, float* logits_out, hipStream_t s);
+void launch_permute(const int32_t* topk_idx, int T, int k, int E, int ns, int32_t* offsets,
+                    int32_t* sorted_src, hipStream_t s);
+void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,
+                        const float* topk_w, const void* w_gate, const void* w_up,
+                        const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
+                        float* y_slots, void* ws, hipStream_t s);
+void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
+                    hipStream_t s);
+void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,
+                   int V, int dt, int32_t* argmax_out, float* max_out, float* logits_out,
+                   void* ws, hipStream_t s);
+void launch_verify(const int32_t* tokens, const int32_t* greedy, int B, int K, int32_t* n_accept,
+                   int32_t* commit, int32_t* commit_len, int32_t* next_last, hipStream_t s);
+
+size_t grouped_ffn_ws_bytes(int T, int I, int k, int ns, int dt);
+size_t lmhead_ws_bytes(int T, int H, int V, int dt);
+
+}  // namespace moev

@@ -1,0 +1,135 @@
+// Whole FastMTP verify step on one stream: embedding gather, the decoder's
+// MoE layers (route -> permute -> grouped FFN -> combine), the greedy head and
+// the prefix-accept kernel.  All scratch lives in one caller-provided
+// workspace; nothing here allocates or synchronises, so a step can be
+// captured into a HIP graph and replayed.
+//
+// The verification itself follows "The speed comes from three layers working
+// together" (Jina-OCR-v1 explainer, kg.zhiyong.dev): the K drafted tokens are
+// checked by the main decoder in one pass, here as T = B*(K+1) rows of one
+// batch.
+#include "launch.h"
+
+namespace moev {
+namespace {
+
+struct StepLayout {
+  size_t h, x, idx, w, offsets, sorted, y, ffn, head, total;
+};
+
+size_t esz(int dt) { return dt == MOEV_BF16 ? 2 : 4; }
+
+StepLayout layout(const moev_model& m, int T) {
+  const int S = m.top_k + m.n_shared;
+  const int G = m.n_routed + m.n_shared;
+  const size_t P = static_cast<size_t>(T) * S;
+  StepLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes, 256);
+    return at;
+  };
+  L.h = take(static_cast<size_t>(T) * m.hidden * 4);
+  L.x = take(static_cast<size_t>(T) * m.hidden * esz(m.dtype));
+  L.idx = take(static_cast<size_t>(T) * m.top_k * 4);
+  L.w = take(static_cast<size_t>(T) * m.top_k * 4);
+  L.offsets = take(static_cast<size_t>(G + 1) * 4);
+  L.sorted = take(P * 4);
+  L.y = take(P * m.hidden * 4);
+  L.ffn = take(grouped_ffn_ws_bytes(T, m.inter, m.top_k, m.n_shared, m.dtype));
+  L.head = take(lmhead_ws_bytes(T, m.hidden, m.vocab, m.dtype));
+  L.total = o;
+  return L;
+}
+
+moev_status validate_model(const moev_model* m, int B, int K) {
+  MOEV_REQUIRE(m != nullptr, MOEV_ERR_INVALID_ARG, "model must not be NULL");
+  MOEV_CHECK(check_dtype(m->dtype), MOEV_ERR_UNSUPPORTED);
+  MOEV_REQUIRE(B >= 0 && K >= 0, MOEV_ERR_INVALID_ARG, "need B >= 0 and K >= 0 (B=%d K=%d)", B, K);
+  MOEV_REQUIRE(K <= 64, MOEV_ERR_UNSUPPORTED, "K=%d drafts exceeds 64", K);
+  MOEV_REQUIRE(m->hidden >= 64 && m->hidden <= 4032 && m->hidden % 64 == 0, MOEV_ERR_UNSUPPORTED,
+               "hidden size %d must be a multiple of 64 in [64, 4032]", m->hidden);
+  MOEV_REQUIRE(m->inter >= 64 && m->inter <= 8192 && m->inter % 64 == 0, MOEV_ERR_UNSUPPORTED,
+               "intermediate size %d must be a multiple of 64 in [64, 8192]", m->inter);
+  MOEV_REQUIRE(m->n_routed >= 1 && m->n_routed <= 64, MOEV_ERR_UNSUPPORTED,
+               "routed experts E=%d must be in [1, 64]", m->n_routed);
+  MOEV_REQUIRE(m->top_k >= 1 && m->top_k <= m->n_routed, MOEV_ERR_UNSUPPORTED,
+               "top-k k=%d must be in [1, E=%d]", m->top_k, m->n_routed);
+  MOEV_REQUIRE(m->n_shared >= 0 && m->n_shared <= 8, MOEV_ERR_UNSUPPORTED,
+               "shared experts ns=%d must be in [0, 8]", m->n_shared);
+  MOEV_REQUIRE(m->vocab >= 1, MOEV_ERR_INVALID_ARG, "vocabulary must be >= 1");
+  MOEV_REQUIRE(m->n_layers >= 0, MOEV_ERR_INVALID_ARG, "n_layers must be >= 0");
+  const long long T = static_cast<long long>(B) * (K + 1);
+  MOEV_REQUIRE(T * (m->top_k + m->n_shared) < (1ll << 31), MOEV_ERR_UNSUPPORTED,
+               "B*(K+1)*(k+ns) must be < 2^31");
+  MOEV_CHECK(need_ptr(m->emb, "model.emb") && opt_ptr(m->norm_f, "model.norm_f") &&
+                 need_ptr(m->w_lm, "model.w_lm"),
+             MOEV_ERR_INVALID_ARG);
+  MOEV_REQUIRE(m->n_layers == 0 || m->layers != nullptr, MOEV_ERR_INVALID_ARG,
+               "model.layers must not be NULL");
+  for (int l = 0; l < m->n_layers; ++l) {
+    const moev_layer_weights& lw = m->layers[l];
+    if (!(opt_ptr(lw.norm, "layer.norm") && need_ptr(lw.w_router, "layer.w_router") &&
+          opt_ptr(lw.bias, "layer.bias") && need_ptr(lw.w_gate, "layer.w_gate") &&
+          need_ptr(lw.w_up, "layer.w_up") && need_ptr(lw.w_down, "layer.w_down"))) {
+      set_error("layer %d: %s", l, moev_last_error());
+      return MOEV_ERR_INVALID_ARG;
+    }
+  }
+  return MOEV_OK;
+}
+
+}  // namespace
+}  // namespace moev
+
+extern "C" size_t moev_verify_step_workspace_size(const moev_model* m, int B, int K) {
+  if (m == nullptr || B < 0 || K < 0) return 0;
+  return moev::layout(*m, B * (K + 1)).total;
+}
+
+extern "C" moev_status moev_verify_step(const moev_model* m, const int32_t* tokens, int B, int K,
+                                        int32_t* greedy, int32_t* n_accept, int32_t* commit,
+                                        int32_t* commit_len, int32_t* next_last, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  using namespace moev;
+  if (moev_status st = validate_model(m, B, K)) return st;
+  if (B == 0) return MOEV_OK;
+  MOEV_CHECK(need_ptr(tokens, "tokens") && need_ptr(greedy, "greedy") &&
+                 need_ptr(n_accept, "n_accept") && need_ptr(commit, "commit"),
+             MOEV_ERR_INVALID_ARG);
+  const int T = B * (K + 1);
+  const StepLayout L = layout(*m, T);
+  MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE,
+               "workspace must be non-NULL and 16-byte aligned");
+  MOEV_REQUIRE(ws_bytes >= L.total, MOEV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+               ws_bytes, L.total);
+
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  float* h = reinterpret_cast<float*>(base + L.h);
+  void* x = base + L.x;
+  int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
+  float* w = reinterpret_cast<float*>(base + L.w);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+  float* y = reinterpret_cast<float*>(base + L.y);
+  void* ffn_ws = base + L.ffn;
+  void* head_ws = base + L.head;
+  const hipStream_t s = as_stream(stream);
+  const int H = m->hidden, E = m->n_routed, k = m->top_k, ns = m->n_shared;
+
+  launch_embed(tokens, m->emb, T, H, m->vocab, m->dtype, h, s);
+  for (int l = 0; l < m->n_layers; ++l) {
+    const moev_layer_weights& lw = m->layers[l];
+    launch_route(h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, m->dtype, x, idx, w,
+                 nullptr, s);
+    launch_permute(idx, T, k, E, ns, offsets, sorted, s);
+    launch_grouped_ffn(x, sorted, offsets, w, lw.w_gate, lw.w_up, lw.w_down, T, H, m->inter, E, k,
+                       ns, m->dtype, y, ffn_ws, s);
+    launch_combine(y, h, T, H, k + ns, h, s);
+  }
+  launch_lmhead(h, m->norm_f, m->eps, m->w_lm, T, H, m->vocab, m->dtype, greedy, nullptr, nullptr,
+                head_ws, s);
+  launch_verify(tokens, greedy, B, K, n_accept, commit, commit_len, next_last, s);
+  return launch_status("moev_verify_step");
+}

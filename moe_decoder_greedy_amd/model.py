@@ -1,0 +1,98 @@
+"""Device-resident synthetic decoder and the whole-step runner.
+
+``DeviceModel`` uploads a weight dict (as produced by ``synth.model_weights``:
+bf16 bit patterns as uint16, or float32) to HBM once, keeps it resident, and
+exposes ``verify_step`` -- one call into ``moev_verify_step`` that enqueues the
+embedding gather, every MoE layer, the greedy head and the prefix accept on
+the current stream.  Python only marshals pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from .ops import BF16, F32, check, lib, ptr, stream_handle
+
+
+def to_device(a: Optional[np.ndarray], dtype: str, device) -> Optional[torch.Tensor]:
+    """numpy -> torch on ``device``; uint16 arrays are bf16 bit patterns."""
+    if a is None:
+        return None
+    if dtype == "bf16" and a.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device)
+
+
+class DeviceModel:
+    """A synthetic MoE decoder resident on one GPU."""
+
+    def __init__(self, weights: dict, device="cuda"):
+        shape = weights["shape"]
+        self.shape = shape
+        self.dtype = weights["dtype"]
+        self.device = torch.device(device)
+        dt = self.dtype
+        self.layers = []
+        for d in weights["layers"]:
+            self.layers.append({key: to_device(d[key], dt if key != "bias" else "f32", self.device)
+                                for key in ("norm", "w_router", "w_gate", "w_up", "w_down", "bias")})
+        self.emb = to_device(weights["emb"], dt, self.device)
+        self.norm_f = to_device(weights["norm_f"], dt, self.device)
+        self.w_lm = to_device(weights["w_lm"], dt, self.device)
+        n = len(self.layers)
+        self._c_layers = (_lib.LayerWeights * max(n, 1))()
+        for i, L in enumerate(self.layers):
+            self._c_layers[i] = _lib.LayerWeights(ptr(L["norm"]), ptr(L["w_router"]), ptr(L["bias"]),
+                                                  ptr(L["w_gate"]), ptr(L["w_up"]), ptr(L["w_down"]))
+        self._c_model = _lib.Model(
+            shape.hidden, shape.n_routed, shape.inter, shape.top_k, shape.n_shared, shape.vocab, n,
+            BF16 if dt == "bf16" else F32, shape.eps, ptr(self.emb), ptr(self.norm_f),
+            ptr(self.w_lm), self._c_layers)
+        self._ws: Dict[tuple, torch.Tensor] = {}
+
+    @property
+    def c_model(self):
+        return ctypes.byref(self._c_model)
+
+    def weight_bytes(self) -> int:
+        n = self.emb.nbytes + self.norm_f.nbytes + self.w_lm.nbytes
+        for L in self.layers:
+            n += sum(t.nbytes for t in L.values() if t is not None)
+        return n
+
+    def workspace(self, B: int, K: int) -> torch.Tensor:
+        key = (B, K)
+        if key not in self._ws:
+            n = lib().moev_verify_step_workspace_size(self.c_model, B, K)
+            self._ws[key] = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        return self._ws[key]
+
+    def alloc_outputs(self, B: int, K: int) -> dict:
+        d = self.device
+        return {"greedy": torch.empty((B, K + 1), dtype=torch.int32, device=d),
+                "n_accept": torch.empty((B,), dtype=torch.int32, device=d),
+                "commit": torch.empty((B, K + 1), dtype=torch.int32, device=d),
+                "commit_len": torch.empty((B,), dtype=torch.int32, device=d),
+                "next_last": torch.empty((B,), dtype=torch.int32, device=d)}
+
+    def verify_step(self, tokens: torch.Tensor, out: Optional[dict] = None, stream=None) -> dict:
+        """One verify pass; ``tokens`` int32 [B, K+1] on the GPU."""
+        B, K1 = tokens.shape
+        K = K1 - 1
+        out = self.alloc_outputs(B, K) if out is None else out
+        ws = self.workspace(B, K)
+        check("moev_verify_step", lib().moev_verify_step(
+            self.c_model, ptr(tokens), B, K, ptr(out["greedy"]), ptr(out["n_accept"]),
+            ptr(out["commit"]), ptr(out["commit_len"]), ptr(out["next_last"]), ptr(ws), ws.numel(),
+            stream_handle(stream)))
+        return out
+
+    def greedy(self, tokens: torch.Tensor) -> torch.Tensor:
+        """Greedy successor of every token (a K = 0 step)."""
+        return self.verify_step(tokens.reshape(-1, 1).to(torch.int32).contiguous())["greedy"].reshape(-1)

@@ -1,0 +1,118 @@
+"""The C-ABI library on the host: it loads, exports every entry point that
+include/moev.h declares, and rejects bad arguments before touching the GPU.
+No kernel is launched here (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_decoder_greedy_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moev.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+BF16, F32 = 1, 0
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmoev.so not built: run python -m moe_decoder_greedy_amd.build")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "moe_route" in names and "mtp_verify" in names and "moev_verify_step" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.moev_status_string(0) == b"ok"
+    assert lib.moev_status_string(3) == b"workspace missing or too small"
+    assert lib.moev_version() == 100
+
+
+def _err(lib):
+    return lib.moev_last_error().decode()
+
+
+def test_route_validation(lib):
+    s = None
+    args = dict(h=FAKE, norm=None, eps=1e-6, wr=FAKE, bias=None, T=4, H=1280, E=64, k=6, dt=BF16,
+                x=FAKE, idx=FAKE, w=FAKE, logits=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.moe_route(a["h"], a["norm"], a["eps"], a["wr"], a["bias"], a["T"], a["H"], a["E"],
+                             a["k"], a["dt"], a["x"], a["idx"], a["w"], a["logits"], s)
+    assert call(h=None) == INVALID and "h must not be NULL" in _err(lib)
+    assert call(x=FAKE + 4) == INVALID and "aligned" in _err(lib)
+    assert call(k=7, E=6) == UNSUPPORTED
+    assert call(E=65) == UNSUPPORTED
+    assert call(H=1000) == UNSUPPORTED
+    assert call(dt=7) == UNSUPPORTED
+    assert call(T=-1) == INVALID
+    assert call(T=0, h=None, x=None) == OK          # empty batch: nothing enqueued
+
+
+def test_permute_validation(lib):
+    assert lib.moe_permute(FAKE, 8, 2, 8, 9, FAKE, FAKE, None) == UNSUPPORTED   # ns > 8
+    assert lib.moe_permute(FAKE, 8, 0, 8, 1, FAKE, FAKE, None) == UNSUPPORTED   # k = 0
+    assert lib.moe_permute(None, 8, 2, 8, 1, FAKE, FAKE, None) == INVALID
+    assert lib.moe_permute(FAKE, 8, 2, 8, 1, None, FAKE, None) == INVALID
+
+
+def test_grouped_ffn_validation_and_workspace(lib):
+    need = lib.moe_grouped_ffn_workspace_size(128, 896, 6, 2, BF16)
+    assert need >= 128 * 8 * 896 * 2
+    call = lambda ws, n, I=896: lib.moe_grouped_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128,
+                                                    1280, I, 64, 6, 2, BF16, FAKE, ws, n, None)
+    assert call(FAKE, need - 1) == WORKSPACE and "needs" in _err(lib)
+    assert call(None, need) == WORKSPACE
+    assert call(FAKE, need, I=900) == UNSUPPORTED
+
+
+def test_lmhead_validation(lib):
+    need = lib.lmhead_argmax_workspace_size(128, 1280, 129280, BF16)
+    assert need > 128 * 1280 * 2
+    f = lambda **kw: lib.lmhead_argmax(kw.get("h", FAKE), None, 1e-6, FAKE, 128, 1280, kw.get("V", 129280),
+                                       BF16, kw.get("out", FAKE), None, None, FAKE, kw.get("n", need), None)
+    assert f(n=need - 1) == WORKSPACE
+    assert f(out=None) == INVALID
+    assert f(V=0) == INVALID
+
+
+def test_verify_and_combine_validation(lib):
+    assert lib.mtp_verify(FAKE, FAKE, 4, -1, FAKE, FAKE, None, None, None) == INVALID
+    assert lib.mtp_verify(FAKE, FAKE, 4, 65, FAKE, FAKE, None, None, None) == UNSUPPORTED
+    assert lib.mtp_verify(None, None, 0, 3, None, None, None, None, None) == OK
+    assert lib.moe_combine(FAKE, None, 4, 6, 8, FAKE, None) == UNSUPPORTED   # H % 4
+    assert lib.moe_combine(None, None, 4, 8, 8, FAKE, None) == INVALID
+
+
+def test_step_validation(lib):
+    layers = (_lib.LayerWeights * 1)(_lib.LayerWeights(None, FAKE, None, FAKE, FAKE, None))
+    m = _lib.Model(1280, 64, 896, 6, 2, 129280, 1, BF16, 1e-6, FAKE, None, FAKE, layers)
+    ws = lib.moev_verify_step_workspace_size(ctypes.byref(m), 32, 3)
+    assert ws > 0
+    st = lib.moev_verify_step(ctypes.byref(m), FAKE, 32, 3, FAKE, FAKE, FAKE, None, None, FAKE, ws, None)
+    assert st == INVALID and "layer 0" in _err(lib) and "w_down" in _err(lib)
+    m.n_layers = 0
+    assert lib.moev_verify_step(ctypes.byref(m), FAKE, 32, 3, FAKE, FAKE, FAKE, None, None, FAKE,
+                                ws - 1, None) == WORKSPACE
+    m.top_k = 65
+    assert lib.moev_verify_step(ctypes.byref(m), FAKE, 32, 3, FAKE, FAKE, FAKE, None, None, FAKE,
+                                ws, None) == UNSUPPORTED

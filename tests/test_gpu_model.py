@@ -1,0 +1,160 @@
+"""Whole verify steps through moev_verify_step (the entry point bench.py
+times): parity with the oracle, losslessness against greedy rollout, batch
+invariance, and tau against the pages' Table 8 acceptances."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import dev_i32, host, need_gpu, report
+
+pytestmark = pytest.mark.gpu
+
+HEAD_GAP, ROUTE_GAP = 1e-2, 1e-3
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def model_mod():
+    need_gpu()
+    from moe_decoder_greedy_amd import model
+    return model
+
+
+@pytest.fixture(scope="module")
+def tiny_pair(model_mod):
+    w = synth.model_weights(synth.TINY)
+    return w, model_mod.DeviceModel(w)
+
+
+@pytest.fixture(scope="module")
+def decoder_pair(model_mod):
+    report("decoder", msg="generating 12-layer synthetic decoder")
+    w = synth.model_weights(synth.DECODER)
+    return w, model_mod.DeviceModel(w)
+
+
+def _flags(ref):
+    return (ref["gap"] < HEAD_GAP) | (ref["router_gap"] < ROUTE_GAP)
+
+
+def test_step_tiny_matches_oracle(tiny_pair):
+    w, dm = tiny_pair
+    B, K, V = 4, 3, synth.TINY.vocab
+    for step in range(4):
+        rng = np.random.default_rng(step)
+        tokens = rng.integers(0, V, size=(B, K + 1)).astype(np.int32)
+        if step % 2 == 0:  # make some drafts right so accepts vary
+            g = oracle.model_greedy(tokens[:, 0], w, "exact")["argmax"]
+            tokens[:, 1] = g
+        out = dm.verify_step(dev_i32(tokens))
+        ref = oracle.verify_step(tokens[:, 0], tokens[:, 1:], w, operands="exact")
+        flagged = _flags(ref)
+        gg = host(out["greedy"])
+        np.testing.assert_array_equal(gg[~flagged], ref["greedy"][~flagged])
+        n, c, l, nx = oracle.mtp_verify(tokens, gg)
+        np.testing.assert_array_equal(host(out["n_accept"]), n)
+        np.testing.assert_array_equal(host(out["commit"]), c)
+        np.testing.assert_array_equal(host(out["commit_len"]), l)
+        np.testing.assert_array_equal(host(out["next_last"]), nx)
+        report("step_tiny", step=step, flagged=int(flagged.sum()))
+
+
+def test_step_decoder_sampled(decoder_pair):
+    """B=32, K=3 on the 12-layer decoder with the 129280-token head: every
+    greedy token of 3 sequences (12 of 128 positions) recomputed by the oracle."""
+    w, dm = decoder_pair
+    B, K, V = 32, 3, synth.DECODER.vocab
+    last = synth.initial_tokens(B, V)
+    rng = np.random.default_rng(4)
+    tokens = np.concatenate([last[:, None], rng.integers(0, V, size=(B, K))], axis=1).astype(np.int32)
+    out = dm.verify_step(dev_i32(tokens))
+    gg = host(out["greedy"])
+    sample = [0, 17, 31]
+    ref = oracle.model_greedy(tokens[sample].reshape(-1), w, "bf16")
+    flagged = _flags(ref)
+    got = gg[sample].reshape(-1)
+    report("step_decoder", flagged=int(flagged.sum()),
+           mismatches=int((got != ref["argmax"]).sum()))
+    np.testing.assert_array_equal(got[~flagged], ref["argmax"][~flagged])
+    n, c, l, nx = oracle.mtp_verify(tokens, gg)
+    np.testing.assert_array_equal(host(out["commit"]), c)
+
+
+def _gpu_rollout(dm, last, n):
+    cur = torch.from_numpy(last.astype(np.int32)).cuda()
+    seq = []
+    for _ in range(n):
+        cur = dm.greedy(cur)
+        seq.append(cur)
+    return host(torch.stack(seq, dim=1))
+
+
+def test_lossless_64_steps(decoder_pair):
+    """Speculative commits are bit-identical to the GPU's own greedy rollout
+    over 64 verify steps of 32 sequences with K=3 drafts drawn at Table 8's
+    per-position acceptances; tau sits within 4 sigma of the closed form the
+    pages print as 2.73."""
+    w, dm = decoder_pair
+    wl = synth.WORKLOADS["verify_step_b32k3"]
+    B, K, V, steps = wl.batch, wl.drafts, wl.shape.vocab, wl.steps
+    last0 = synth.initial_tokens(B, V)
+    roll = _gpu_rollout(dm, last0, steps * (K + 1) + K + 1)
+    traj = np.concatenate([last0[:, None], roll], axis=1)
+    pos = np.zeros(B, np.int64)
+    last = last0.copy()
+    committed = 0
+    for s in range(steps):
+        cont = np.stack([traj[b, pos[b] + 1:pos[b] + 1 + K] for b in range(B)])
+        drafts = synth.draft_tokens(cont, pos, wl.accept, V)
+        tokens = np.concatenate([last[:, None], drafts], axis=1).astype(np.int32)
+        out = dm.verify_step(dev_i32(tokens))
+        clen = host(out["commit_len"])
+        commit = host(out["commit"])
+        for b in range(B):
+            np.testing.assert_array_equal(commit[b, :clen[b]], traj[b, pos[b] + 1:pos[b] + 1 + clen[b]])
+        pos += clen
+        last = host(out["next_last"]).astype(np.int32)
+        committed += clen.sum()
+    tau = committed / (B * steps)
+    t8 = json.load(open(os.path.join(GOLDEN, "fastmtp_table8.json")))
+    report("lossless", tau=tau, expected=oracle.expected_tau(t8["conditional_acceptance"]))
+    assert abs(tau - oracle.expected_tau(t8["conditional_acceptance"])) < 0.10
+
+
+def test_batch_invariance(decoder_pair):
+    """A token's greedy successor is the same bits whatever batch it is in."""
+    w, dm = decoder_pair
+    V = synth.DECODER.vocab
+    rng = np.random.default_rng(8)
+    pool = rng.integers(0, V, size=512).astype(np.int32)
+    full = host(dm.greedy(dev_i32(pool)))
+    for T in (1, 4, 32, 128, 300):
+        sub = rng.choice(512, T, replace=False)
+        got = host(dm.greedy(dev_i32(pool[sub])))
+        np.testing.assert_array_equal(got, full[sub])
+    # inside a verify batch (positions 1..K are drafts) the same holds
+    toks = pool[:128].reshape(32, 4)
+    out = dm.verify_step(dev_i32(toks))
+    np.testing.assert_array_equal(host(out["greedy"]).reshape(-1), full[:128])
+
+
+def test_zipf_step_sampled(model_mod):
+    """Skewed routing (per-layer Zipf(1.1) router bias) through the whole step
+    at B=8, K=3, two layers: sampled tokens against the oracle."""
+    import dataclasses
+    shape = dataclasses.replace(synth.DECODER, zipf=True, n_layers=2)
+    w = synth.model_weights(shape)
+    dm = model_mod.DeviceModel(w)
+    B, K = 8, 3
+    tokens = np.random.default_rng(2).integers(0, shape.vocab, size=(B, K + 1)).astype(np.int32)
+    out = dm.verify_step(dev_i32(tokens))
+    ref = oracle.model_greedy(tokens[:2].reshape(-1), w, "bf16")
+    flagged = _flags(ref)
+    got = host(out["greedy"])[:2].reshape(-1)
+    report("zipf_step", flagged=int(flagged.sum()))
+    np.testing.assert_array_equal(got[~flagged], ref["argmax"][~flagged])
