@@ -1,0 +1,412 @@
+#!/usr/bin/env python3
+"""Throughput of the FastMTP verify step on one MI355X.
+
+Default workload: 32 sequences x (last committed token + K=3 drafts) = 128
+tokens through the 12-layer synthetic MoE decoder (64 routed top-6 + 2 shared
+SwiGLU experts, hidden 1280, intermediate 896) and the 129280-token greedy
+head, then prefix acceptance.  Weights, tokens and drafts are synthetic and
+seeded (drafts agree with greedy at 0.830/0.663/0.636 per position).
+
+Prints ONE JSON line: verified tokens/s (value), committed tokens/s and tau,
+the roofline of the dominant kernel (the gate/up grouped GEMM) from HIP events,
+and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "verified tokens/s per MoE verify step (32 seq×K=3) + % HBM/MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="verify_step_b32k3",
+                    help="verify_step_b32k3 | zipf_verify_b{1,8,32,128}k{1,3} | decode_layer_t128 | prefill_layer_t9760")
+    ap.add_argument("--launch", choices=("auto", "eager", "graph"), default="auto")
+    ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event pass")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (PMC calibration)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+
+def gate_up_bytes(touched: int, T: int, P: int, H: int, I: int, es: int = 2) -> int:
+    """Bytes the gate/up stage must move: gate+up weights of every touched
+    group once, the T normalised rows once, the P activation rows out, and the
+    sort metadata."""
+    return touched * 2 * I * H * es + T * H * es + P * I * es + 4 * P
+
+
+def layer_bytes(touched: int, T: int, P: int, H: int, I: int, E: int, es: int = 2) -> int:
+    """One MoE layer: router weights, all three matrices of each touched group,
+    the residual in and out, expert slots in and out, activations."""
+    return (E * H * es + touched * 3 * I * H * es + 2 * T * H * 4 + T * H * es
+            + 2 * P * I * es + 2 * P * H * 4)
+
+
+def head_bytes(T: int, H: int, V: int, es: int = 2) -> int:
+    return V * H * es + T * H * 4 + T * 4
+
+
+# ---------------------------------------------------------------------------
+
+def copy_probe(torch, mib: int):
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: {mib} MiB read + {mib} MiB written per copy, 3 copies")
+
+
+def cpu_baseline(wl, weights, tokens_np, budget_s):
+    """The oracle as it stands, on this host's cores, over one verify step of
+    the same batch: layers are timed one by one until the budget is spent and
+    the per-layer mean is extrapolated to the full depth, plus the head and
+    the accept step."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    shape = wl.shape
+    dt = weights["dtype"]
+    B, K1 = tokens_np.shape
+    t0 = time.perf_counter()
+    h = oracle.embed(tokens_np.reshape(-1), weights["emb"], dt)
+    layer_times = []
+    for layer in weights["layers"]:
+        ts = time.perf_counter()
+        st = oracle.moe_layer(h, layer, dt, shape.top_k, shape.n_routed, shape.n_shared, shape.eps, "bf16")
+        h = st["h_out"]
+        layer_times.append(time.perf_counter() - ts)
+        if time.perf_counter() - t0 > budget_s * 0.7:
+            break
+    ts = time.perf_counter()
+    head = oracle.lm_head(h, weights["norm_f"], weights["w_lm"], dt, shape.eps, "bf16")
+    oracle.mtp_verify(tokens_np, head["argmax"].reshape(B, K1))
+    t_head = time.perf_counter() - ts
+    n_l = len(layer_times)
+    t_step = float(np.mean(layer_times)) * shape.n_layers + t_head
+    T = B * K1
+    return {"value": T / t_step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"one verify step of {B}x{K1} tokens (float64 numpy oracle): {n_l} of "
+                       f"{shape.n_layers} layers timed, mean extrapolated to {shape.n_layers}, "
+                       f"plus head and accept; oracle step {t_step:.2f} s"),
+            "seconds_measured": round(time.perf_counter() - t0, 2)}
+
+
+def run_verify(args, torch, np):
+    import synth
+    from moe_decoder_greedy_amd import model as mdl
+    from moe_decoder_greedy_amd import ops
+
+    wl = synth.WORKLOADS[args.workload]
+    shape = wl.shape
+    B, K, V, H, I = wl.batch, wl.drafts, shape.vocab, shape.hidden, shape.inter
+    E, k, ns = shape.n_routed, shape.top_k, shape.n_shared
+    T, S, P = B * (K + 1), k + ns, B * (K + 1) * (k + ns)
+    t0 = time.perf_counter()
+    weights = synth.model_weights(shape)
+    log(f"weights generated in {time.perf_counter() - t0:.1f} s")
+    dm = mdl.DeviceModel(weights)
+    torch.cuda.synchronize()
+    log(f"uploaded {dm.weight_bytes() / 1e9:.2f} GB")
+
+    # greedy trajectory of every sequence (the drafts are drawn against it)
+    n_steps = args.warmup + args.steps
+    n_roll = n_steps * (K + 1) + K + 1
+    last0 = synth.initial_tokens(B, V)
+    cur = torch.from_numpy(last0).cuda()
+    seq = []
+    for _ in range(n_roll):
+        cur = dm.greedy(cur)
+        seq.append(cur)
+    traj = np.concatenate([last0[:, None], torch.stack(seq, 1).cpu().numpy()], axis=1)
+    pos = np.zeros(B, np.int64)
+    inputs = np.empty((n_steps, B, K + 1), np.int32)
+    want_len = np.empty((n_steps, B), np.int64)
+    for s in range(n_steps):
+        cont = np.stack([traj[b, pos[b] + 1:pos[b] + 1 + K] for b in range(B)]) if K else np.zeros((B, 0), np.int64)
+        drafts = synth.draft_tokens(cont, pos, wl.accept, V, mode=wl.draft_mode) if K else cont
+        inputs[s, :, 0] = traj[np.arange(B), pos]
+        inputs[s, :, 1:] = drafts
+        n = np.zeros(B, np.int64)
+        for b in range(B):
+            while n[b] < K and drafts[b, n[b]] == cont[b, n[b]]:
+                n[b] += 1
+        want_len[s] = n + 1
+        pos += n + 1
+    inputs_d = torch.from_numpy(inputs).cuda()
+    log(f"trajectory of {n_roll} greedy tokens, {n_steps} step inputs staged in HBM")
+
+    # ------------------------------------------------------------------ eager
+    outs = {key: torch.empty((n_steps,) + tuple(v.shape), dtype=v.dtype, device="cuda")
+            for key, v in dm.alloc_outputs(B, K).items()}
+
+    def step_out(s):
+        return {key: v[s] for key, v in outs.items()}
+
+    def eager_run():
+        for s in range(args.warmup):
+            dm.verify_step(inputs_d[s], out=step_out(s))
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for s in range(args.warmup, n_steps):
+            dm.verify_step(inputs_d[s], out=step_out(s))
+        torch.cuda.synchronize()
+        return (time.perf_counter() - ta) / args.steps
+
+    t_eager = eager_run()
+    clen = outs["commit_len"].cpu().numpy()
+    lossless = bool(np.array_equal(clen, want_len))
+    log(f"eager: {t_eager * 1e3:.3f} ms/step, commits as expected: {lossless}")
+
+    # ------------------------------------------------------------------ graph
+    t_graph = None
+    if args.launch in ("auto", "graph"):
+        tok_static = inputs_d[0].clone()
+        out_static = dm.alloc_outputs(B, K)
+        dm.verify_step(tok_static, out=out_static)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dm.verify_step(tok_static, out=out_static)
+        clen_g = torch.empty((n_steps, B), dtype=torch.int32, device="cuda")
+        for s in range(args.warmup):
+            tok_static.copy_(inputs_d[s])
+            g.replay()
+            clen_g[s].copy_(out_static["commit_len"])
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for s in range(args.warmup, n_steps):
+            tok_static.copy_(inputs_d[s])
+            g.replay()
+            clen_g[s].copy_(out_static["commit_len"])
+        torch.cuda.synchronize()
+        t_graph = (time.perf_counter() - ta) / args.steps
+        graph_ok = bool(np.array_equal(clen_g.cpu().numpy(), want_len))
+        lossless = lossless and graph_ok
+        log(f"graph: {t_graph * 1e3:.3f} ms/step, commits as expected: {graph_ok}")
+        del g
+
+    if args.launch == "eager" or t_graph is None:
+        t_step, launch = t_eager, "eager"
+    elif args.launch == "graph":
+        t_step, launch = t_graph, "hipgraph"
+    else:
+        t_step, launch = (t_graph, "hipgraph") if t_graph < t_eager else (t_eager, "eager")
+    committed = float(want_len[args.warmup:].sum()) / args.steps   # per step
+    tau = committed / B
+
+    # ------------------------------- per-kernel durations (HIP events, roofline)
+    # Events are recorded by the step driver itself, on the stream the kernels
+    # run on, right around the launches of one stage per pass, so the GPU is
+    # never waiting on the host between the two events.
+    stages = ("route", "permute", "gate_up", "down", "combine", "head")
+    dur_us = {}
+    for st in stages:
+        n_ev = 1 if st == "head" else shape.n_layers
+        pend = []
+        for s in range(args.kernel_steps):
+            bef = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+            aft = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+            i = args.warmup + s % args.steps
+            dm.verify_step_probed(inputs_d[i], st, bef, aft, out=step_out(i))
+            pend.append((bef, aft))
+        torch.cuda.synchronize()
+        dur_us[st] = float(np.mean([b.elapsed_time(a) for bef, aft in pend for b, a in zip(bef, aft)])) * 1e3
+
+    # experts touched per layer (the routing of the first timed step, per layer)
+    dt_code = ops.BF16 if dm.dtype == "bf16" else ops.F32
+    es = 2 if dm.dtype == "bf16" else 4
+    xbuf = torch.empty((T, H), dtype=torch.bfloat16 if es == 2 else torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    offs = torch.empty((shape.n_layers, E + ns + 1), dtype=torch.int32, device="cuda")
+    src = torch.empty((P,), dtype=torch.int32, device="cuda")
+    act = torch.empty((P, I), dtype=xbuf.dtype, device="cuda")
+    y = torch.empty((T, S, H), dtype=torch.float32, device="cuda")
+    h = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    tok = inputs_d[args.warmup]
+    ops.moe_embed(tok.reshape(-1), dm.emb, out=h)
+    for l, L in enumerate(dm.layers):
+        ops.moe_route(h, L["norm"], shape.eps, L["w_router"], L["bias"], k, x_out=xbuf, topk_idx=idx, topk_w=wts)
+        ops.moe_permute(idx, E, ns, offsets=offs[l], sorted_src=src)
+        ops.moe_ffn_gate_up(xbuf, src, offs[l], L["w_gate"], L["w_up"], E, k, ns, act=act)
+        ops.moe_ffn_down(act, src, offs[l], wts, L["w_down"], T, E, k, ns, y_slots=y)
+        ops.moe_combine(y, h, out=h)
+    touched = (np.diff(offs.cpu().numpy(), axis=1) > 0).sum(axis=1)     # [layers]
+    gu_bytes = float(np.mean([gate_up_bytes(int(t), T, P, H, I, es) for t in touched]))
+    gu_flops = 4.0 * P * H * I
+    step_bytes = sum(layer_bytes(int(t), T, P, H, I, E, es) for t in touched) + head_bytes(T, H, V, es)
+    gu_gbs = gu_bytes / (dur_us["gate_up"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "stream_gemm<bf16, gate/up> (moe_ffn_gate_up)",
+                "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(dur_us["gate_up"], 2),
+                "mfma_frac": round(gu_flops / (dur_us["gate_up"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    step_gbs = step_bytes / t_step / 1e9
+    result = {
+        "metric": METRIC, "value": round(T / t_step, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dm.dtype,
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, drafts at 0.830/0.663/0.636 acceptance)",
+        "config": {"workload": wl.name, "layers": shape.n_layers, "hidden": H, "routed_experts": E,
+                   "top_k": k, "shared_experts": ns, "intermediate": I, "vocab": V, "batch": B,
+                   "drafts": K, "tokens_per_step": T, "zipf_bias": shape.zipf, "launch": launch},
+        "committed_tokens_per_s": round(committed / t_step, 1), "tau": round(tau, 4),
+        "lossless_commits": lossless,
+        "ms_per_step_eager": round(t_eager * 1e3, 4),
+        "ms_per_step_graph": None if t_graph is None else round(t_graph * 1e3, 4),
+        "step_roofline": {"bound": "hbm", "bytes_per_step": int(step_bytes), "achieved": round(step_gbs, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "kernel_avg_us": {n: round(v, 2) for n, v in dur_us.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(wl, weights, inputs[args.warmup], args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    return result
+
+
+def run_layer(args, torch, np):
+    """One MoE layer at decode (T=128) or prefill (T=9760) shape on h ~ N(0,1),
+    rotating through 4 distinct layers so no weight byte is served by a cache."""
+    import dataclasses
+    import synth
+    from moe_decoder_greedy_amd import ops
+    from moe_decoder_greedy_amd.model import to_device
+
+    wl = synth.WORKLOADS[args.workload]
+    n_copies = 4
+    shape = dataclasses.replace(wl.shape, n_layers=n_copies)
+    weights = synth.model_weights(shape, head=False)
+    layers = []
+    for d in weights["layers"]:
+        L = {key: to_device(d[key], "bf16" if key != "bias" else "f32", "cuda") for key in ("norm", "w_router", "bias")}
+        for key in ("w_gate", "w_up", "w_down"):
+            L[key] = ops.pack_weights(to_device(d[key], "bf16", "cuda"))
+        layers.append(L)
+    T, H, I, E, k, ns = wl.n_tokens, shape.hidden, shape.inter, shape.n_routed, shape.top_k, shape.n_shared
+    S, P = k + ns, wl.n_tokens * (k + ns)
+    h0 = torch.from_numpy(synth.hidden_states(shape, T)).cuda()
+    x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    offs = torch.empty((n_copies, E + ns + 1), dtype=torch.int32, device="cuda")
+    src = torch.empty((P,), dtype=torch.int32, device="cuda")
+    act = torch.empty((P, I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, S, H), dtype=torch.float32, device="cuda")
+    h = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ev = {n: [] for n in ("route", "permute", "gate_up", "down", "combine", "layer")}
+
+    def one(L, o, rec):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if rec else None
+        if rec: evs[0].record()
+        ops.moe_route(h0, L["norm"], shape.eps, L["w_router"], L["bias"], k, x_out=x, topk_idx=idx, topk_w=w)
+        if rec: evs[1].record()
+        ops.moe_permute(idx, E, ns, offsets=o, sorted_src=src)
+        if rec: evs[2].record()
+        ops.moe_ffn_gate_up(x, src, o, L["w_gate"], L["w_up"], E, k, ns, act=act)
+        if rec: evs[3].record()
+        ops.moe_ffn_down(act, src, o, w, L["w_down"], T, E, k, ns, y_slots=y)
+        if rec: evs[4].record()
+        ops.moe_combine(y, h0, out=h)
+        if rec:
+            evs[5].record()
+            for n, (a, b) in zip(("route", "permute", "gate_up", "down", "combine", "layer"),
+                                 ((0, 1), (1, 2), (2, 3), (3, 4), (4, 5), (0, 5))):
+                ev[n].append((evs[a], evs[b]))
+
+    for i in range(args.warmup):
+        one(layers[i % n_copies], offs[i % n_copies], False)
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    for i in range(args.steps):
+        one(layers[i % n_copies], offs[i % n_copies], False)
+    torch.cuda.synchronize()
+    t_layer = (time.perf_counter() - ta) / args.steps
+    for i in range(args.steps):
+        one(layers[i % n_copies], offs[i % n_copies], True)
+    torch.cuda.synchronize()
+    dur = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for n, v in ev.items()}
+    touched = (np.diff(offs.cpu().numpy(), axis=1) > 0).sum(axis=1)
+    gu_bytes = float(np.mean([gate_up_bytes(int(t), T, P, H, I) for t in touched]))
+    gu_flops = 4.0 * P * H * I
+    lb = float(np.mean([layer_bytes(int(t), T, P, H, I, E) for t in touched]))
+    lflops = 6.0 * P * H * I + 2.0 * T * E * H
+    prefill = T > 1024
+    if prefill:
+        ach = gu_flops / (dur["gate_up"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        ach = gu_bytes / (dur["gate_up"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    roof.update({"kernel": "stream_gemm<bf16, gate/up> (moe_ffn_gate_up)", "avg_launch_us": round(dur["gate_up"], 2),
+                 "bytes_per_launch": int(gu_bytes), "flops_per_launch": gu_flops})
+    return {
+        "metric": "tokens/s through one MoE layer", "value": round(T / t_layer, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_layer * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, h ~ N(0,1))",
+        "config": {"workload": wl.name, "tokens": T, "hidden": H, "routed_experts": E, "top_k": k,
+                   "shared_experts": ns, "intermediate": I, "weight_copies_rotated": n_copies},
+        "layer_hbm_frac": round(lb / t_layer / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_mfma_frac": round(lflops / t_layer / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roof, "kernel_avg_us": {n: round(v, 2) for n, v in dur.items()},
+        "cpu_baseline": None,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the verify step is data "
+              "parallel with no cross-GPU exchange, so N GPUs are N independent copies of this "
+              "measurement; see the sharding notes in DESIGN.md", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib)
+    if args.workload.endswith(("_t128", "_t9760")):
+        result = run_layer(args, torch, np)
+    else:
+        result = run_verify(args, torch, np)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

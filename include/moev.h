@@ -12,7 +12,10 @@
  *
  * Conventions for every entry point
  *   - Device pointers are caller-owned device memory (for example torch
- *     tensors), row-major and contiguous, 16-byte aligned.  The library
+ *     tensors), row-major and contiguous.  int32 arrays, router weights,
+ *     biases, arg max / max / logits outputs need 4-byte alignment; every
+ *     other buffer (hidden states, operands, weights, expert slots,
+ *     workspaces) 16-byte alignment.  The library
  *     allocates nothing and keeps no state between calls; scratch space comes
  *     from a caller-provided workspace sized by the matching *_workspace_size.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
@@ -33,7 +36,7 @@
  * ns shared experts, G = E + ns expert groups (routed 0..E-1, shared E..G-1),
  * S = k + ns slots per token, I expert intermediate width, V vocabulary.
  * Limits: 1 <= E <= 64, 1 <= k <= E, 0 <= ns <= 8, H and I multiples of 64,
- * 64 <= H <= 4032, 64 <= I <= 8192, T * S < 2^31.
+ * 64 <= H <= 3840, 64 <= I <= 8192, T * S < 2^31.
  * Weight/operand type `dt`: MOEV_BF16 (bf16 bit patterns, GEMMs on bf16 MFMA
  * with fp32 accumulation) or MOEV_F32 (fp32 MFMA).  Residual stream, router
  * weights out, expert outputs and logits are always fp32.
@@ -64,6 +67,24 @@ const char* moev_status_string(int status);
 const char* moev_last_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int moev_version(void);
+
+/*
+ * Fragment-packed weights.  Every expert and LM-head weight argument below
+ * (w_gate, w_up, w_down, w_lm, and the same fields of moev_model) is taken in
+ * this layout, made from row-major [G, N, K] by moev_pack_weights: for group
+ * g, row tile t (rows 16t..16t+15, rows past N zero) and K block b (columns
+ * 32b..32b+31), the 512 elements
+ *   packed[((g*ceil(N/16) + t)*(K/32) + b)*512 + lane*8 + e]
+ *     = W[g][16t + lane % 16][32b + 8*(lane / 16) + e],   lane < 64, e < 8
+ * are the 64 lanes' MFMA A fragments of that 16x32 block, stored
+ * contiguously, with the blocks of a tile adjacent along K.  A wavefront then
+ * streams one contiguous region of HBM per 16-row tile.
+ * moev_packed_size: bytes of the packed form (0 for invalid arguments).
+ * moev_pack_weights: src dt [G, N, K] row-major -> dst packed; K % 32 == 0.
+ */
+size_t moev_packed_size(int G, int N, int K, int dt);
+moev_status moev_pack_weights(const void* src, void* dst, int G, int N, int K, int dt,
+                              void* stream);
 
 /*
  * moe_embed -- residual stream input: h_out[t, :] = emb[tokens[t], :] as fp32.
@@ -118,7 +139,8 @@ moev_status moe_permute(const int32_t* topk_idx, int T, int k, int E, int ns,
  *   x        dt [T, H] (moe_route's x_out)
  *   sorted_src, group_offsets from moe_permute
  *   topk_w   fp32 [T, k]
- *   w_gate, w_up  dt [G, I, H];  w_down dt [G, H, I]  (shared experts last)
+ *   w_gate, w_up  dt [G, I, H];  w_down dt [G, H, I]  (shared experts last),
+ *            all fragment-packed
  *   y_slots  fp32 [T, S, H] (written, every slot)
  *   ws       workspace of moe_grouped_ffn_workspace_size() bytes
  * Each output element is a fixed-order fp32 sum, so a token's result does not
@@ -129,6 +151,21 @@ moev_status moe_grouped_ffn(const void* x, const int32_t* sorted_src, const int3
                             const float* topk_w, const void* w_gate, const void* w_up,
                             const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
                             float* y_slots, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The two stages of moe_grouped_ffn as separate calls (same kernels).
+ * moe_ffn_gate_up: act[j, :] = SiLU(w_gate[g] . x[t]) * (w_up[g] . x[t]),
+ *   rounded to dt, for every row j of the sorted pair order (pair
+ *   sorted_src[j] = t*S + slot, j in group g's segment).  act: dt [T*S, I].
+ * moe_ffn_down: y_slots[t, slot, :] = wgt * (w_down[g] . act[j, :]) for the
+ *   same rows, wgt as in moe_grouped_ffn.
+ */
+moev_status moe_ffn_gate_up(const void* x, const int32_t* sorted_src, const int32_t* group_offsets,
+                            const void* w_gate, const void* w_up, int T, int H, int I, int E,
+                            int k, int ns, int dt, void* act, void* stream);
+moev_status moe_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* group_offsets,
+                         const float* topk_w, const void* w_down, int T, int H, int I, int E,
+                         int k, int ns, int dt, float* y_slots, void* stream);
 
 /*
  * moe_combine -- residual add of every slot's expert output:
@@ -146,7 +183,7 @@ moev_status moe_combine(const float* y_slots, const float* h_in, int T, int H, i
  * measure").
  *   x = RMSNorm(h) * norm_f rounded to dt;  logits = w_lm . x  (fp32 acc)
  *   argmax_out[t] = lowest index of the largest logit
- *   h        fp32 [T, H];  norm_f dt [H] or NULL;  w_lm dt [V, H]
+ *   h        fp32 [T, H];  norm_f dt [H] or NULL;  w_lm dt [V, H] fragment-packed
  *   argmax_out int32 [T] (written);  max_out fp32 [T] or NULL
  *   logits_out fp32 [T, V] or NULL (written when non-NULL; for checking)
  *   ws       workspace of lmhead_argmax_workspace_size() bytes
@@ -179,9 +216,9 @@ typedef struct moev_layer_weights {
   const void* norm;     /* dt [H] or NULL */
   const void* w_router; /* dt [E, H] */
   const float* bias;    /* fp32 [E] or NULL */
-  const void* w_gate;   /* dt [G, I, H] */
-  const void* w_up;     /* dt [G, I, H] */
-  const void* w_down;   /* dt [G, H, I] */
+  const void* w_gate;   /* dt [G, I, H], fragment-packed */
+  const void* w_up;     /* dt [G, I, H], fragment-packed */
+  const void* w_down;   /* dt [G, H, I], fragment-packed */
 } moev_layer_weights;
 
 typedef struct moev_model {
@@ -190,7 +227,7 @@ typedef struct moev_model {
   float eps;    /* RMSNorm epsilon */
   const void* emb;    /* dt [V, H] */
   const void* norm_f; /* dt [H] or NULL */
-  const void* w_lm;   /* dt [V, H] */
+  const void* w_lm;   /* dt [V, H], fragment-packed */
   const moev_layer_weights* layers; /* host array of n_layers entries */
 } moev_model;
 
@@ -208,6 +245,29 @@ moev_status moev_verify_step(const moev_model* m, const int32_t* tokens, int B, 
                              int32_t* greedy, int32_t* n_accept, int32_t* commit,
                              int32_t* commit_len, int32_t* next_last, void* ws, size_t ws_bytes,
                              void* stream);
+
+/*
+ * moev_verify_step_probed -- moev_verify_step with timing events: for every
+ * layer l < probe->n (and for the head when stage == MOEV_STAGE_HEAD, using
+ * index 0), records probe->before[l] / probe->after[l] on `stream` right
+ * before / after the launches of stage `probe->stage`.  Events are
+ * hipEvent_t handles created by the caller; probe == NULL is
+ * moev_verify_step.  For measurement only.
+ */
+enum {
+  MOEV_STAGE_ROUTE = 0, MOEV_STAGE_PERMUTE = 1, MOEV_STAGE_GATE_UP = 2, MOEV_STAGE_DOWN = 3,
+  MOEV_STAGE_COMBINE = 4, MOEV_STAGE_HEAD = 5
+};
+typedef struct moev_step_probe {
+  int stage;
+  int n;
+  void* const* before;
+  void* const* after;
+} moev_step_probe;
+moev_status moev_verify_step_probed(const moev_model* m, const int32_t* tokens, int B, int K,
+                                    int32_t* greedy, int32_t* n_accept, int32_t* commit,
+                                    int32_t* commit_len, int32_t* next_last, void* ws,
+                                    size_t ws_bytes, const moev_step_probe* probe, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,11 +26,20 @@ class Model(ctypes.Structure):
                 ("layers", ctypes.POINTER(LayerWeights))]
 
 
+class StepProbe(ctypes.Structure):
+    _fields_ = [("stage", c_int), ("n", c_int), ("before", ctypes.POINTER(c_void_p)),
+                ("after", ctypes.POINTER(c_void_p))]
+
+
+STAGES = {"route": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4, "head": 5}
+
 # name -> (restype, argtypes); mirrors include/moev.h
 SIGNATURES = {
     "moev_status_string": (ctypes.c_char_p, [c_int]),
     "moev_last_error": (ctypes.c_char_p, []),
     "moev_version": (c_int, []),
+    "moev_packed_size": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "moev_pack_weights": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p]),
     "moe_embed": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
     "moe_route": (c_int, [c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_int, c_int, c_int,
                           c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -39,6 +48,10 @@ SIGNATURES = {
     "moe_grouped_ffn": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_ffn_gate_up": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,
+                                c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "moe_ffn_down": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                             c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
     "moe_combine": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p]),
     "lmhead_argmax_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
     "lmhead_argmax": (c_int, [c_void_p, c_void_p, c_float, c_void_p, c_int, c_int, c_int, c_int,
@@ -49,6 +62,9 @@ SIGNATURES = {
     "moev_verify_step": (c_int, [ctypes.POINTER(Model), c_void_p, c_int, c_int, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                  c_void_p]),
+    "moev_verify_step_probed": (c_int, [ctypes.POINTER(Model), c_void_p, c_int, c_int, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                        ctypes.POINTER(StepProbe), c_void_p]),
 }
 
 _lib = None

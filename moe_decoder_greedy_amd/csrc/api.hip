@@ -19,21 +19,17 @@ void set_error(const char* fmt, ...) {
 
 void clear_error() { g_last_error.clear(); }
 
-bool need_ptr(const void* p, const char* name) {
+bool need_ptr(const void* p, const char* name, unsigned align) {
   if (p == nullptr) {
     set_error("%s must not be NULL", name);
     return false;
   }
-  if (!aligned16(p)) {
-    set_error("%s must be 16-byte aligned", name);
-    return false;
-  }
-  return true;
+  return opt_ptr(p, name, align);
 }
 
-bool opt_ptr(const void* p, const char* name) {
-  if (p != nullptr && !aligned16(p)) {
-    set_error("%s must be 16-byte aligned", name);
+bool opt_ptr(const void* p, const char* name, unsigned align) {
+  if (p != nullptr && (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0) {
+    set_error("%s must be %u-byte aligned", name, align);
     return false;
   }
   return true;

@@ -92,8 +92,8 @@ moev_status validate_verify(const int32_t* tokens, const int32_t* greedy, int B,
   MOEV_REQUIRE(B >= 0 && K >= 0, MOEV_ERR_INVALID_ARG, "need B >= 0 and K >= 0 (B=%d K=%d)", B, K);
   MOEV_REQUIRE(K <= 64, MOEV_ERR_UNSUPPORTED, "K=%d drafts exceeds 64", K);
   if (B == 0) return MOEV_OK;
-  MOEV_CHECK(need_ptr(tokens, "tokens") && need_ptr(greedy, "greedy") &&
-                 need_ptr(n_accept, "n_accept") && need_ptr(commit, "commit"),
+  MOEV_CHECK(need_ptr(tokens, "tokens", 4) && need_ptr(greedy, "greedy", 4) &&
+                 need_ptr(n_accept, "n_accept", 4) && need_ptr(commit, "commit", 4),
              MOEV_ERR_INVALID_ARG);
   return MOEV_OK;
 }

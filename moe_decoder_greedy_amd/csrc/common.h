@@ -25,9 +25,11 @@ void clear_error();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Validation helpers: each returns false after recording the reason.
-bool need_ptr(const void* p, const char* name);
-bool opt_ptr(const void* p, const char* name);  // NULL allowed, else aligned
+// Validation helpers: each returns false after recording the reason.  Buffers
+// read or written with 16-byte vector accesses need align = 16; int32/fp32
+// arrays touched one element at a time need align = 4.
+bool need_ptr(const void* p, const char* name, unsigned align = 16);
+bool opt_ptr(const void* p, const char* name, unsigned align = 16);  // NULL allowed
 bool check_dtype(int dt);
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -61,6 +63,31 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
   return v;
+}
+
+// DPP lane move of a float (gfx9 data-parallel primitives): CTRL selects the
+// pattern; rows outside ROW_MASK receive 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum across the 64 lanes with DPP steps (VALU latency, no LDS round trips):
+// pairs, quads, half rows, rows, then rows 0+1 and 0+1+2+3 via row broadcasts.
+// The complete sum is in lane 63; the order of additions is fixed.
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+  v += dpp_mov<0xb1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4e>(v);        // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);       // row_half_mirror
+  v += dpp_mov<0x140>(v);       // row_mirror
+  v += dpp_mov<0x142, 0xa>(v);  // row_bcast:15 -> rows 1, 3
+  v += dpp_mov<0x143, 0xc>(v);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+__device__ __forceinline__ float lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -10,21 +10,24 @@
 //
 // Design (decode shapes are weight-bandwidth bound: every expert's weights
 // are read from HBM exactly once per call):
-//   * one workgroup = 4 wavefronts owns a slab of weight rows of one group
-//     and ALL of that group's tokens (in passes of up to 128), so no weight
-//     byte is fetched twice;
-//   * each wavefront owns RT tiles of 16 weight rows; its A fragments come
-//     straight from global memory (16 contiguous bytes per lane per 32-wide K
-//     block) through a register ring kNB chunks deep, so HBM requests for
-//     later K chunks are in flight while the current one is multiplied;
-//   * the token operand (gathered rows of x, or the group's activation rows)
-//     is staged through LDS in 64-wide K chunks, shared by the 4 wavefronts,
-//     double-buffered through registers (the next chunk is fetched while the
-//     current one is consumed); LDS rows are padded by 16 bytes so the
-//     16-byte B-fragment reads of 16 rows hit distinct banks;
+//   * weights are stored fragment-packed: for each tile of 16 rows and each
+//     32-wide K block, the 64 lanes' 16-byte A fragments lie contiguously
+//     (1 KB for bf16), and consecutive K blocks of a tile are adjacent, so a
+//     wavefront streams one contiguous region with full-line loads;
+//   * one workgroup = 4 wavefronts owns a slab of 64 (or 64*RT) weight rows of
+//     one group and ALL of that group's tokens (in passes), so no weight byte
+//     is fetched twice; each wavefront owns RT tiles of 16 rows;
+//   * A fragments go straight from HBM into a register ring several K blocks
+//     deep, so requests for later blocks are in flight while the current one
+//     is multiplied;
+//   * passes of at most 32 tokens (the routed experts at decode batch sizes)
+//     fetch their token fragments straight from global memory (L2) through
+//     the same ring -- no LDS, no barriers; larger passes stage the token rows
+//     through LDS in 64-wide K chunks shared by the 4 wavefronts (rows padded
+//     by 16 bytes so the 16-byte fragment reads of 16 rows hit distinct banks);
 //   * every output element is a single fp32 accumulation over K in the same
-//     block order whatever the token count, so a token's result does not
-//     depend on its batch companions.
+//     block order whatever path or pass size ran it, so a token's result does
+//     not depend on its batch companions.
 #include "launch.h"
 
 namespace moev {
@@ -32,22 +35,40 @@ namespace {
 
 enum Mode { kGateUp = 0, kDown = 1, kHead = 2 };
 
-constexpr int kThreads = 256;
-constexpr int kMaxTok = 128;  // tokens per pass: 8 MFMA column tiles
-constexpr int kKC = 64;       // K elements per LDS chunk: 2 MFMA K blocks
-constexpr int kNB = 4;        // weight ring depth in chunks
-constexpr int kRtDown = 1;    // 16-row tiles per wave, down projection
-constexpr int kRtHead = 2;    // 16-row tiles per wave, LM head
+#ifndef MOEV_KC
+#define MOEV_KC 64
+#endif
+#ifndef MOEV_KNB
+#define MOEV_KNB 3
+#endif
+#ifndef MOEV_KNBD
+#define MOEV_KNBD 3
+#endif
+constexpr int kKC = MOEV_KC;     // K elements per LDS chunk (multiple of 32)
+constexpr int kKB = kKC / 32;    // MFMA K blocks per chunk
+constexpr int kNB = MOEV_KNB;    // LDS path: weight ring depth in chunks
+constexpr int kNBD = MOEV_KNBD;  // direct path: ring depth in K blocks
+constexpr int kFrag = 512;       // elements of one packed 16x32 fragment
+constexpr int kRtDown = 1;       // 16-row tiles per wave, down projection
+constexpr int kRtHead = 2;       // 16-row tiles per wave, LM head
+constexpr int kWavesFfn = 4;     // wavefronts per workgroup, expert GEMMs
+constexpr int kWavesHead = 8;    // wavefronts per workgroup, LM head (256 rows)
 
-template <typename WT> struct Cfg {
+// MT = tokens per pass (32, 64 or 128 = 2, 4 or 8 MFMA column tiles).  The
+// variant only changes how many accumulators and LDS rows a workgroup holds;
+// every variant adds the same K blocks in the same order, so a token's result
+// is the same bits whichever variant ran it.
+template <typename WT, int MT> struct Cfg {
   static constexpr int kEpv = 16 / sizeof(WT);                     // elements per 16 B
   static constexpr int kRowBytes = kKC * sizeof(WT) + 16;          // padded LDS row
   static constexpr int kVecPerRow = kKC * sizeof(WT) / 16;         // 16-B vectors per row
-  static constexpr int kStage = kMaxTok * kVecPerRow / kThreads;   // vectors per thread
+  static constexpr int kTiles = MT / 16;                           // MFMA column tiles
+  static constexpr int kRedBytes = 8 * kWavesHead * MT;            // head arg max scratch
+  static constexpr int kLdsBytes = MT * kRowBytes > kRedBytes ? MT * kRowBytes : kRedBytes;
 };
 
 struct GemmArgs {
-  const void* w0;           // [G, N, K] (gate/up: gate; down: w_down; head: w_lm)
+  const void* w0;           // packed [G][N/16][K/32][512] (gate/up: gate; down; head)
   const void* w1;           // gate/up: up, else unused
   long long w_group;        // elements between consecutive groups
   int N, K;                 // weight rows per group, contraction length
@@ -55,6 +76,8 @@ struct GemmArgs {
   const int32_t* offsets;   // [G+1] (gate/up, down)
   const int32_t* sorted_src;
   int S, k, P, T;           // slots, routed slots, pairs, tokens
+  int n_first;              // the last n_first groups (the shared experts, which
+                            // hold every token) are dispatched first
   const float* topk_w;      // [T, k] (down)
   void* out;                // gate/up: act [P, N] WT; down: y [P, N] fp32; head: pmax
   int32_t* out_idx;         // head: partial arg max [blocks, T]
@@ -74,22 +97,273 @@ template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
-template <typename WT, int MODE, int RT>
-__global__ __launch_bounds__(kThreads) void stream_gemm(GemmArgs a) {
-  using C = Cfg<WT>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kMaxTok * C::kRowBytes];
+// Row of the operand matrix that token row `row` of this pass reads.
+template <int MODE>
+__device__ __forceinline__ long long operand_row(const GemmArgs& a, int off, int m0, int row) {
+  if (MODE == kGateUp) return clampi(a.sorted_src[off + m0 + row], 0, a.P - 1) / a.S;
+  if (MODE == kDown) return off + m0 + row;
+  return m0 + row;
+}
 
+// Epilogue of one pass: lane (r16, q) holds rows rowbase[rt] + 4q + v of
+// token column j*16 + r16.
+template <typename WT, int MODE, int RT, int MT, int NTX, int W>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, unsigned char* __restrict__ lds,
+                                         const f32x4 (&acc)[RT][NTX], int off, int m0, int mp,
+                                         const int (&rowbase)[RT]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int q = lane >> 4;
+  const int mt = (mp + 15) >> 4;
+  if (MODE == kGateUp) {
+    WT* act = static_cast<WT*>(a.out);
+    const int n = rowbase[0] + 4 * q;
+#pragma unroll
+    for (int j = 0; j < NTX; ++j) {
+      const int m = j * 16 + r16;
+      if (m < mp) {
+        f32x4 gv = acc[0][j], uv = acc[1][j], o;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] = gv[v] / (1.0f + expf(-gv[v])) * uv[v];
+        store4<WT>(act + static_cast<long long>(off + m0 + m) * a.N + n, o);
+      }
+    }
+  } else if (MODE == kDown) {
+    float* y = static_cast<float*>(a.out);
+#pragma unroll
+    for (int j = 0; j < NTX; ++j) {
+      const int m = j * 16 + r16;
+      if (m < mp) {
+        const int p = clampi(a.sorted_src[off + m0 + m], 0, a.P - 1);
+        const int t = p / a.S;
+        const int slot = p - t * a.S;
+        const float wgt = slot < a.k ? a.topk_w[static_cast<long long>(t) * a.k + slot] : 1.0f;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4 o = acc[rt][j];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] *= wgt;
+          store4<float>(y + static_cast<long long>(p) * a.N + rowbase[rt] + 4 * q, o);
+        }
+      }
+    }
+  } else {
+    // per token column: best (value, vocab index) over this wave's rows
+    __syncthreads();  // every wave is done with the staged chunk
+    float* red_v = reinterpret_cast<float*>(lds);         // [W][MT]
+    int* red_i = reinterpret_cast<int*>(lds) + W * MT;    // [W][MT]
+#pragma unroll
+    for (int j = 0; j < NTX; ++j) {
+      if (j < mt) {
+        const int m = j * 16 + r16;
+        float best = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int n = rowbase[rt] + 4 * q + v;
+            if (n < a.N) {
+              const float val = acc[rt][j][v];
+              if (a.logits != nullptr && m < mp) a.logits[static_cast<long long>(m0 + m) * a.N + n] = val;
+              if (better(val, n, best, bi)) { best = val; bi = n; }
+            }
+          }
+#pragma unroll
+        for (int msk = 16; msk <= 32; msk <<= 1) {
+          const float ov = __shfl_xor(best, msk, kWave);
+          const int oi = __shfl_xor(bi, msk, kWave);
+          if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+        }
+        if (q == 0) {
+          red_v[wave * MT + m] = best;
+          red_i[wave * MT + m] = bi;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < mp) {
+      float best = red_v[tid];
+      int bi = red_i[tid];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        const float ov = red_v[w * MT + tid];
+        const int oi = red_i[w * MT + tid];
+        if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+      }
+      const long long o = static_cast<long long>(blockIdx.x) * a.T + m0 + tid;
+      static_cast<float*>(a.out)[o] = best;
+      a.out_idx[o] = bi;
+    }
+  }
+}
+
+// Direct pass (mp <= 16 * NTX <= 32): both fragments come from global memory
+// through one register ring kNBD K blocks deep; no LDS, no barriers.  Token
+// rows past mp read row 0 of the pass and are dropped by the epilogue.
+template <typename WT, int MODE, int RT, int MT, int NTX, int W>
+__device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned char* __restrict__ lds,
+                                                 int off, int m0, int mp,
+                                                 const WT* const (&wp)[RT],
+                                                 const int (&rowbase)[RT]) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int q = lane >> 4;
+  const int K = a.K;
+  const int nkb = K / 32;
+  const WT* __restrict__ xsrc = static_cast<const WT*>(a.x);
+  const WT* xp[NTX];
+#pragma unroll
+  for (int j = 0; j < NTX; ++j) {
+    const int m = j * 16 + r16;
+    xp[j] = xsrc + operand_row<MODE>(a, off, m0, m < mp ? m : 0) * K + q * 8;
+  }
+  f32x4 acc[RT][NTX];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < NTX; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Frag<WT> rw[kNBD][RT], rx[kNBD][NTX];
+#pragma unroll
+  for (int u = 0; u < kNBD; ++u)
+    if (u < nkb) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) rw[u][rt].load(wp[rt] + u * kFrag);
+#pragma unroll
+      for (int j = 0; j < NTX; ++j) rx[u][j].load(xp[j] + u * 32);
+    }
+  for (int kb0 = 0; kb0 < nkb; kb0 += kNBD) {
+#pragma unroll
+    for (int u = 0; u < kNBD; ++u) {
+      const int kb = kb0 + u;
+      if (kb < nkb) {
+#pragma unroll
+        for (int j = 0; j < NTX; ++j)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt][j] = mma(rw[u][rt], rx[u][j], acc[rt][j]);
+        if (kb + kNBD < nkb) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) rw[u][rt].load(wp[rt] + (kb + kNBD) * kFrag);
+#pragma unroll
+          for (int j = 0; j < NTX; ++j) rx[u][j].load(xp[j] + (kb + kNBD) * 32);
+        }
+      }
+    }
+  }
+  epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
+}
+
+// LDS-staged pass: mt = ceil(mp / 16) <= NTX column tiles.  NTX is a
+// compile-time tile count, so the K loop carries no per-tile predicates;
+// tiles past mt multiply LDS rows that the staging loop zero-filled and are
+// dropped by the epilogue.
+template <typename WT, int MODE, int RT, int MT, int NTX, int W>
+__device__ __forceinline__ void gemm_pass_lds(const GemmArgs& a, unsigned char* __restrict__ lds,
+                                              int off, int m0, int mp,
+                                              const WT* const (&wp)[RT], const int (&rowbase)[RT]) {
+  using C = Cfg<WT, MT>;
+  constexpr int kThreads = W * kWave;
+  constexpr int kVecs = 16 * NTX * C::kVecPerRow;                // 16-B vectors per chunk
+  constexpr int kStage = (kVecs + kThreads - 1) / kThreads;      // staging vectors per thread
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int r16 = lane & 15;
+  const int q = lane >> 4;
+  const int K = a.K;
+  const int nchunks = K / kKC;
+  const WT* __restrict__ xsrc = static_cast<const WT*>(a.x);
+
+  // source rows for this thread's staging vectors (nullptr: zero-fill)
+  const WT* src[kStage];
+#pragma unroll
+  for (int s = 0; s < kStage; ++s) {
+    const int v = tid + s * kThreads;
+    const int row = v / C::kVecPerRow;
+    const int cv = v - row * C::kVecPerRow;
+    src[s] = (v < kVecs && row < mp) ? xsrc + operand_row<MODE>(a, off, m0, row) * K + cv * C::kEpv
+                                     : nullptr;
+  }
+  uint4 stage[kStage];
+#pragma unroll
+  for (int s = 0; s < kStage; ++s)
+    stage[s] = src[s] ? *reinterpret_cast<const uint4*>(src[s]) : make_uint4(0, 0, 0, 0);
+
+  f32x4 acc[RT][NTX];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < NTX; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Frag<WT> ring[kNB][RT][kKB];
+#pragma unroll
+  for (int u = 0; u < kNB; ++u)
+    if (u < nchunks)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int kk = 0; kk < kKB; ++kk) ring[u][rt][kk].load(wp[rt] + (u * kKB + kk) * kFrag);
+
+  for (int c0 = 0; c0 < nchunks; c0 += kNB) {
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {
+      const int c = c0 + u;
+      if (c < nchunks) {
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < kStage; ++s) {
+          const int v = tid + s * kThreads;
+          const int row = v / C::kVecPerRow;
+          const int cv = v - row * C::kVecPerRow;
+          if (v < kVecs) *reinterpret_cast<uint4*>(lds + row * C::kRowBytes + cv * 16) = stage[s];
+        }
+        __syncthreads();
+        if (c + 1 < nchunks) {
+#pragma unroll
+          for (int s = 0; s < kStage; ++s)
+            if (src[s]) stage[s] = *reinterpret_cast<const uint4*>(src[s] + (c + 1) * kKC);
+        }
+#pragma unroll
+        for (int kk = 0; kk < kKB; ++kk) {
+#pragma unroll
+          for (int j = 0; j < NTX; ++j) {
+            Frag<WT> b;
+            b.load(reinterpret_cast<const WT*>(lds + (j * 16 + r16) * C::kRowBytes) + kk * 32 + q * 8);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) acc[rt][j] = mma(ring[u][rt][kk], b, acc[rt][j]);
+          }
+        }
+        if (c + kNB < nchunks) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kk = 0; kk < kKB; ++kk)
+              ring[u][rt][kk].load(wp[rt] + ((c + kNB) * kKB + kk) * kFrag);
+        }
+      }
+    }
+  }
+  epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
+}
+
+template <typename WT, int MODE, int RT, int MT, int W>
+__global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
+  using C = Cfg<WT, MT>;
+  constexpr int NT = C::kTiles;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
 
   int g = 0, off = 0, M;
   if (MODE == kHead) {
     M = a.T;
   } else {
-    g = blockIdx.y;
+    const int G = gridDim.y;
+    g = static_cast<int>(blockIdx.y) < a.n_first ? G - a.n_first + blockIdx.y : blockIdx.y - a.n_first;
     off = clampi(a.offsets[g], 0, a.P);
     M = clampi(a.offsets[g + 1], off, a.P) - off;
   }
@@ -97,192 +371,66 @@ __global__ __launch_bounds__(kThreads) void stream_gemm(GemmArgs a) {
 
   const WT* __restrict__ w0 = static_cast<const WT*>(a.w0);
   const WT* __restrict__ w1 = static_cast<const WT*>(a.w1);
-  const WT* __restrict__ xsrc = static_cast<const WT*>(a.x);
-  const int K = a.K;
-  const int nchunks = K / kKC;
+  const int nkb = a.K / 32;
+  const int ntiles = (a.N + 15) / 16;
 
-  // weight rows of this wave's tiles; lane pointer = row (rowbase + r16), k = 8q
+  // this wave's weight tiles; lane pointer = its 16 bytes of the first fragment
   const WT* wp[RT];
   int rowbase[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int rb = (MODE == kGateUp) ? blockIdx.x * 64 + wave * 16
-                                     : blockIdx.x * (64 * RT) + wave * (16 * RT) + rt * 16;
+    const int rb = (MODE == kGateUp) ? blockIdx.x * (16 * W) + wave * 16
+                                     : blockIdx.x * (16 * RT * W) + wave * (16 * RT) + rt * 16;
     rowbase[rt] = rb;
-    const int row = min(rb + r16, a.N - 1);
+    const int tile = min(rb / 16, ntiles - 1);
     const WT* base = (MODE == kGateUp && rt == 1) ? w1 : w0;
-    wp[rt] = base + static_cast<long long>(g) * a.w_group + static_cast<long long>(row) * K + q * 8;
+    wp[rt] = base + static_cast<long long>(g) * a.w_group +
+             static_cast<long long>(tile) * nkb * kFrag + lane * 8;
   }
 
-  for (int m0 = 0; m0 < M; m0 += kMaxTok) {
-    const int mp = min(kMaxTok, M - m0);
-    const int mt = (mp + 15) >> 4;
-
-    // source rows for this thread's staging vectors
-    const WT* src[C::kStage];
-#pragma unroll
-    for (int s = 0; s < C::kStage; ++s) {
-      const int v = tid + s * kThreads;
-      const int row = v / C::kVecPerRow;
-      const int cv = v - row * C::kVecPerRow;
-      src[s] = nullptr;
-      if (row < mp) {
-        long long xr;
-        if (MODE == kGateUp) {
-          const int p = clampi(a.sorted_src[off + m0 + row], 0, a.P - 1);
-          xr = p / a.S;
-        } else if (MODE == kDown) {
-          xr = off + m0 + row;
-        } else {
-          xr = m0 + row;
-        }
-        src[s] = xsrc + xr * K + cv * C::kEpv;
-      }
+  for (int m0 = 0; m0 < M; m0 += MT) {
+    const int mp = min(MT, M - m0);
+    // the branches are uniform across the workgroup
+    if (mp <= 16) {
+      gemm_pass_direct<WT, MODE, RT, MT, 1, W>(a, lds, off, m0, mp, wp, rowbase);
+    } else if (mp <= 32) {
+      gemm_pass_direct<WT, MODE, RT, MT, 2, W>(a, lds, off, m0, mp, wp, rowbase);
+    } else if constexpr (NT >= 4) {
+      if (mp <= 64 || NT == 4)
+        gemm_pass_lds<WT, MODE, RT, MT, 4, W>(a, lds, off, m0, mp, wp, rowbase);
+      else
+        gemm_pass_lds<WT, MODE, RT, MT, NT, W>(a, lds, off, m0, mp, wp, rowbase);
     }
-    uint4 stage[C::kStage];
-#pragma unroll
-    for (int s = 0; s < C::kStage; ++s)
-      stage[s] = src[s] ? *reinterpret_cast<const uint4*>(src[s]) : make_uint4(0, 0, 0, 0);
+  }
+}
 
-    f32x4 acc[RT][8];
+// Fragment packing of row-major weights: thread i writes the 8 elements of
+// packed position i = ((g * ntiles + tile) * nkb + kb) * 64 + lane, taken from
+// row tile*16 + lane % 16, columns kb*32 + 8*(lane / 16) .. +7 (zero past N).
+template <typename WT>
+__global__ __launch_bounds__(256) void pack_kernel(const WT* __restrict__ src, WT* __restrict__ dst,
+                                                   int G, int N, int K) {
+  const long long ntiles = (N + 15) / 16, nkb = K / 32;
+  const long long total = static_cast<long long>(G) * ntiles * nkb * 64;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const int lane = static_cast<int>(i & 63);
+    long long r = i >> 6;
+    const long long kb = r % nkb;
+    r /= nkb;
+    const long long tile = r % ntiles;
+    const long long g = r / ntiles;
+    const long long row = tile * 16 + (lane & 15);
+    const long long col = kb * 32 + 8 * (lane >> 4);
+    uint4* d = reinterpret_cast<uint4*>(dst + i * 8);
+    constexpr int kVec = 8 * sizeof(WT) / 16;   // 16-byte vectors per 8 elements
+    if (row < N) {
+      const uint4* s = reinterpret_cast<const uint4*>(src + (g * N + row) * K + col);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    Frag<WT> ring[kNB][RT][2];
-#pragma unroll
-    for (int u = 0; u < kNB; ++u)
-      if (u < nchunks)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) ring[u][rt][kk].load(wp[rt] + u * kKC + kk * 32);
-
-    for (int c0 = 0; c0 < nchunks; c0 += kNB) {
-#pragma unroll
-      for (int u = 0; u < kNB; ++u) {
-        const int c = c0 + u;
-        if (c < nchunks) {
-          __syncthreads();
-#pragma unroll
-          for (int s = 0; s < C::kStage; ++s) {
-            const int v = tid + s * kThreads;
-            const int row = v / C::kVecPerRow;
-            const int cv = v - row * C::kVecPerRow;
-            *reinterpret_cast<uint4*>(lds + row * C::kRowBytes + cv * 16) = stage[s];
-          }
-          __syncthreads();
-          if (c + 1 < nchunks) {
-#pragma unroll
-            for (int s = 0; s < C::kStage; ++s)
-              if (src[s]) stage[s] = *reinterpret_cast<const uint4*>(src[s] + (c + 1) * kKC);
-          }
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              if (j < mt) {
-                Frag<WT> b;
-                b.load(reinterpret_cast<const WT*>(lds + (j * 16 + r16) * C::kRowBytes) + kk * 32 + q * 8);
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) acc[rt][j] = mma(ring[u][rt][kk], b, acc[rt][j]);
-              }
-            }
-          }
-          if (c + kNB < nchunks) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-              for (int kk = 0; kk < 2; ++kk)
-                ring[u][rt][kk].load(wp[rt] + (c + kNB) * kKC + kk * 32);
-          }
-        }
-      }
-    }
-
-    // ------------------------------------------------------------ epilogues
-    if (MODE == kGateUp) {
-      WT* act = static_cast<WT*>(a.out);
-      const int n = rowbase[0] + 4 * q;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int m = j * 16 + r16;
-        if (j < mt && m < mp) {
-          f32x4 gv = acc[0][j], uv = acc[1][j], o;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] = gv[v] / (1.0f + expf(-gv[v])) * uv[v];
-          store4<WT>(act + static_cast<long long>(off + m0 + m) * a.N + n, o);
-        }
-      }
-    } else if (MODE == kDown) {
-      float* y = static_cast<float*>(a.out);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int m = j * 16 + r16;
-        if (j < mt && m < mp) {
-          const int p = clampi(a.sorted_src[off + m0 + m], 0, a.P - 1);
-          const int t = p / a.S;
-          const int slot = p - t * a.S;
-          const float wgt = slot < a.k ? a.topk_w[static_cast<long long>(t) * a.k + slot] : 1.0f;
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            f32x4 o = acc[rt][j];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) o[v] *= wgt;
-            store4<float>(y + static_cast<long long>(p) * a.N + rowbase[rt] + 4 * q, o);
-          }
-        }
-      }
+      for (int v = 0; v < kVec; ++v) d[v] = s[v];
     } else {
-      // per token column: best (value, vocab index) over this wave's rows
-      __syncthreads();  // every wave is done reading the staged chunk
-      float* red_v = reinterpret_cast<float*>(lds);                 // [4][128]
-      int* red_i = reinterpret_cast<int*>(lds) + 4 * kMaxTok;       // [4][128]
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < mt) {
-          const int m = j * 16 + r16;
-          float best = -INFINITY;
-          int bi = 0x7fffffff;
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int n = rowbase[rt] + 4 * q + v;
-              if (n < a.N) {
-                const float val = acc[rt][j][v];
-                if (a.logits != nullptr && m < mp)
-                  a.logits[static_cast<long long>(m0 + m) * a.N + n] = val;
-                if (better(val, n, best, bi)) { best = val; bi = n; }
-              }
-            }
-#pragma unroll
-          for (int msk = 16; msk <= 32; msk <<= 1) {
-            const float ov = __shfl_xor(best, msk, kWave);
-            const int oi = __shfl_xor(bi, msk, kWave);
-            if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
-          }
-          if (q == 0) {
-            red_v[wave * kMaxTok + m] = best;
-            red_i[wave * kMaxTok + m] = bi;
-          }
-        }
-      }
-      __syncthreads();
-      if (tid < mp) {
-        float best = red_v[tid];
-        int bi = red_i[tid];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-          const float ov = red_v[w * kMaxTok + tid];
-          const int oi = red_i[w * kMaxTok + tid];
-          if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
-        }
-        const long long o = static_cast<long long>(blockIdx.x) * a.T + m0 + tid;
-        static_cast<float*>(a.out)[o] = best;
-        a.out_idx[o] = bi;
-      }
+      for (int v = 0; v < kVec; ++v) d[v] = make_uint4(0, 0, 0, 0);
     }
   }
 }
@@ -336,12 +484,19 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* __restri
   }
 }
 
-template <typename WT, int MODE, int RT>
+// Token-pass variant by batch size: every group holds at most T rows (the
+// shared experts hold exactly T), so T <= MT means one pass per group.
+template <typename WT, int MODE, int RT, int W>
 void launch_gemm(const GemmArgs& args, dim3 grid, hipStream_t s) {
-  stream_gemm<WT, MODE, RT><<<grid, kThreads, 0, s>>>(args);
+  if (args.T <= 32)
+    stream_gemm<WT, MODE, RT, 32, W><<<grid, W * 64, 0, s>>>(args);
+  else if (args.T <= 64)
+    stream_gemm<WT, MODE, RT, 64, W><<<grid, W * 64, 0, s>>>(args);
+  else
+    stream_gemm<WT, MODE, RT, 128, W><<<grid, W * 64, 0, s>>>(args);
 }
 
-int head_blocks(int V) { return (V + 64 * kRtHead - 1) / (64 * kRtHead); }
+int head_blocks(int V) { return (V + 16 * kRtHead * kWavesHead - 1) / (16 * kRtHead * kWavesHead); }
 
 size_t esize(int dt) { return dt == MOEV_BF16 ? 2 : 4; }
 
@@ -352,8 +507,8 @@ moev_status check_inter(int I) {
 }
 
 moev_status check_hid(int H) {
-  MOEV_REQUIRE(H >= 64 && H <= 4032 && H % 64 == 0, MOEV_ERR_UNSUPPORTED,
-               "hidden size %d must be a multiple of 64 in [64, 4032]", H);
+  MOEV_REQUIRE(H >= 64 && H <= 3840 && H % 64 == 0, MOEV_ERR_UNSUPPORTED,
+               "hidden size %d must be a multiple of 64 in [64, 3840]", H);
   return MOEV_OK;
 }
 
@@ -369,41 +524,61 @@ size_t lmhead_ws_bytes(int T, int H, int V, int dt) {
   return xf + 2 * part;
 }
 
-void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,
-                        const float* topk_w, const void* w_gate, const void* w_up,
-                        const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
-                        float* y_slots, void* ws, hipStream_t s) {
-  const int G = E + ns;
-  GemmArgs up{};
+GemmArgs ffn_args(const int32_t* sorted_src, const int32_t* offsets, int T, int H, int I,
+                  int k, int ns) {
+  GemmArgs a{};
+  a.offsets = offsets;
+  a.sorted_src = sorted_src;
+  a.S = k + ns;
+  a.k = k;
+  a.P = T * (k + ns);
+  a.T = T;
+  a.n_first = ns;
+  return a;
+}
+
+void launch_ffn_gate_up(const void* x, const int32_t* sorted_src, const int32_t* offsets,
+                        const void* w_gate, const void* w_up, int T, int H, int I, int E, int k,
+                        int ns, int dt, void* act, hipStream_t s) {
+  GemmArgs up = ffn_args(sorted_src, offsets, T, H, I, k, ns);
   up.w0 = w_gate;
   up.w1 = w_up;
   up.w_group = static_cast<long long>(I) * H;
   up.N = I;
   up.K = H;
   up.x = x;
-  up.offsets = offsets;
-  up.sorted_src = sorted_src;
-  up.S = k + ns;
-  up.k = k;
-  up.P = T * (k + ns);
-  up.T = T;
-  up.out = ws;
-  GemmArgs dn = up;
+  up.out = act;
+  const dim3 grid(I / (16 * kWavesFfn), E + ns);
+  if (dt == MOEV_BF16)
+    launch_gemm<u16, kGateUp, 2, kWavesFfn>(up, grid, s);
+  else
+    launch_gemm<float, kGateUp, 2, kWavesFfn>(up, grid, s);
+}
+
+void launch_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* offsets,
+                     const float* topk_w, const void* w_down, int T, int H, int I, int E, int k,
+                     int ns, int dt, float* y_slots, hipStream_t s) {
+  GemmArgs dn = ffn_args(sorted_src, offsets, T, H, I, k, ns);
   dn.w0 = w_down;
-  dn.w1 = nullptr;
+  dn.w_group = static_cast<long long>(H) * I;
   dn.N = H;
   dn.K = I;
-  dn.x = ws;
+  dn.x = act;
   dn.topk_w = topk_w;
   dn.out = y_slots;
-  const dim3 gu(I / 64, G), gd(H / (64 * kRtDown), G);
-  if (dt == MOEV_BF16) {
-    launch_gemm<u16, kGateUp, 2>(up, gu, s);
-    launch_gemm<u16, kDown, kRtDown>(dn, gd, s);
-  } else {
-    launch_gemm<float, kGateUp, 2>(up, gu, s);
-    launch_gemm<float, kDown, kRtDown>(dn, gd, s);
-  }
+  const dim3 grid(H / (16 * kRtDown * kWavesFfn), E + ns);
+  if (dt == MOEV_BF16)
+    launch_gemm<u16, kDown, kRtDown, kWavesFfn>(dn, grid, s);
+  else
+    launch_gemm<float, kDown, kRtDown, kWavesFfn>(dn, grid, s);
+}
+
+void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,
+                        const float* topk_w, const void* w_gate, const void* w_up,
+                        const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
+                        float* y_slots, void* ws, hipStream_t s) {
+  launch_ffn_gate_up(x, sorted_src, offsets, w_gate, w_up, T, H, I, E, k, ns, dt, ws, s);
+  launch_ffn_down(ws, sorted_src, offsets, topk_w, w_down, T, H, I, E, k, ns, dt, y_slots, s);
 }
 
 void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,
@@ -430,11 +605,11 @@ void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_
   if (dt == MOEV_BF16) {
     norm_cast_kernel<u16><<<nb, 256, 0, s>>>(h, static_cast<const u16*>(norm_f), eps, T, H,
                                               static_cast<u16*>(xf));
-    launch_gemm<u16, kHead, kRtHead>(hd, dim3(nblk), s);
+    launch_gemm<u16, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   } else {
     norm_cast_kernel<float><<<nb, 256, 0, s>>>(h, static_cast<const float*>(norm_f), eps, T, H,
                                                 static_cast<float*>(xf));
-    launch_gemm<float, kHead, kRtHead>(hd, dim3(nblk), s);
+    launch_gemm<float, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   }
   argmax_reduce_kernel<<<T, 64, 0, s>>>(pmax, pidx, nblk, T, argmax_out, max_out);
 }
@@ -453,8 +628,8 @@ moev_status validate_grouped_ffn(const void* x, const int32_t* sorted_src, const
   MOEV_REQUIRE(static_cast<long long>(T) * (k + ns) < (1ll << 31), MOEV_ERR_UNSUPPORTED,
                "T*(k+ns) must be < 2^31");
   if (T == 0) return MOEV_OK;
-  MOEV_CHECK(need_ptr(x, "x") && need_ptr(sorted_src, "sorted_src") &&
-                 need_ptr(offsets, "group_offsets") && need_ptr(topk_w, "topk_w") &&
+  MOEV_CHECK(need_ptr(x, "x") && need_ptr(sorted_src, "sorted_src", 4) &&
+                 need_ptr(offsets, "group_offsets", 4) && need_ptr(topk_w, "topk_w", 4) &&
                  need_ptr(w_gate, "w_gate") && need_ptr(w_up, "w_up") &&
                  need_ptr(w_down, "w_down") && need_ptr(y_slots, "y_slots"),
              MOEV_ERR_INVALID_ARG);
@@ -463,6 +638,26 @@ moev_status validate_grouped_ffn(const void* x, const int32_t* sorted_src, const
   const size_t need = grouped_ffn_ws_bytes(T, I, k, ns, dt);
   MOEV_REQUIRE(ws_bytes >= need, MOEV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
                ws_bytes, need);
+  return MOEV_OK;
+}
+
+moev_status validate_ffn_stage(const void* in, const int32_t* sorted_src, const int32_t* offsets,
+                               const void* w_a, const void* w_b, int T, int H, int I, int E, int k,
+                               int ns, int dt, const void* out) {
+  MOEV_CHECK(check_dtype(dt), MOEV_ERR_UNSUPPORTED);
+  if (moev_status st = check_hid(H)) return st;
+  if (moev_status st = check_inter(I)) return st;
+  MOEV_REQUIRE(T >= 0, MOEV_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+  MOEV_REQUIRE(E >= 1 && E <= 64, MOEV_ERR_UNSUPPORTED, "routed experts E=%d must be in [1, 64]", E);
+  MOEV_REQUIRE(k >= 1 && k <= E, MOEV_ERR_UNSUPPORTED, "top-k k=%d must be in [1, E=%d]", k, E);
+  MOEV_REQUIRE(ns >= 0 && ns <= 8, MOEV_ERR_UNSUPPORTED, "shared experts ns=%d must be in [0, 8]", ns);
+  MOEV_REQUIRE(static_cast<long long>(T) * (k + ns) < (1ll << 31), MOEV_ERR_UNSUPPORTED,
+               "T*(k+ns) must be < 2^31");
+  if (T == 0) return MOEV_OK;
+  MOEV_CHECK(need_ptr(in, "input") && need_ptr(sorted_src, "sorted_src", 4) &&
+                 need_ptr(offsets, "group_offsets", 4) && need_ptr(w_a, "weights") &&
+                 need_ptr(w_b, "weights/topk_w", 4) && need_ptr(out, "output"),
+             MOEV_ERR_INVALID_ARG);
   return MOEV_OK;
 }
 
@@ -475,8 +670,8 @@ moev_status validate_lmhead(const float* h, const void* norm_f, const void* w_lm
   MOEV_REQUIRE(V >= 1, MOEV_ERR_INVALID_ARG, "vocabulary V must be >= 1 (got %d)", V);
   if (T == 0) return MOEV_OK;
   MOEV_CHECK(need_ptr(h, "h") && opt_ptr(norm_f, "norm_f") && need_ptr(w_lm, "w_lm") &&
-                 need_ptr(argmax_out, "argmax_out") && opt_ptr(max_out, "max_out") &&
-                 opt_ptr(logits_out, "logits_out"),
+                 need_ptr(argmax_out, "argmax_out", 4) && opt_ptr(max_out, "max_out", 4) &&
+                 opt_ptr(logits_out, "logits_out", 4),
              MOEV_ERR_INVALID_ARG);
   MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE,
                "workspace must be non-NULL and 16-byte aligned");
@@ -508,6 +703,32 @@ extern "C" moev_status moe_grouped_ffn(const void* x, const int32_t* sorted_src,
   return moev::launch_status("moe_grouped_ffn");
 }
 
+extern "C" moev_status moe_ffn_gate_up(const void* x, const int32_t* sorted_src,
+                                       const int32_t* group_offsets, const void* w_gate,
+                                       const void* w_up, int T, int H, int I, int E, int k, int ns,
+                                       int dt, void* act, void* stream) {
+  if (moev_status st = moev::validate_ffn_stage(x, sorted_src, group_offsets, w_gate, w_up, T, H, I,
+                                                E, k, ns, dt, act))
+    return st;
+  if (T == 0) return MOEV_OK;
+  moev::launch_ffn_gate_up(x, sorted_src, group_offsets, w_gate, w_up, T, H, I, E, k, ns, dt, act,
+                           moev::as_stream(stream));
+  return moev::launch_status("moe_ffn_gate_up");
+}
+
+extern "C" moev_status moe_ffn_down(const void* act, const int32_t* sorted_src,
+                                    const int32_t* group_offsets, const float* topk_w,
+                                    const void* w_down, int T, int H, int I, int E, int k, int ns,
+                                    int dt, float* y_slots, void* stream) {
+  if (moev_status st = moev::validate_ffn_stage(act, sorted_src, group_offsets, w_down, topk_w, T,
+                                                H, I, E, k, ns, dt, y_slots))
+    return st;
+  if (T == 0) return MOEV_OK;
+  moev::launch_ffn_down(act, sorted_src, group_offsets, topk_w, w_down, T, H, I, E, k, ns, dt,
+                        y_slots, moev::as_stream(stream));
+  return moev::launch_status("moe_ffn_down");
+}
+
 extern "C" size_t lmhead_argmax_workspace_size(int T, int H, int V, int dt) {
   if (T < 0 || H < 0 || V < 1) return 0;
   return moev::lmhead_ws_bytes(T, H, V, dt);
@@ -524,4 +745,32 @@ extern "C" moev_status lmhead_argmax(const float* h, const void* norm_f, float e
   moev::launch_lmhead(h, norm_f, eps, w_lm, T, H, V, dt, argmax_out, max_out, logits_out, ws,
                       moev::as_stream(stream));
   return moev::launch_status("lmhead_argmax");
+}
+
+namespace moev {
+size_t packed_elems(int G, int N, int K) {
+  return static_cast<size_t>(G) * ((static_cast<size_t>(N) + 15) / 16 * 16) * K;
+}
+}  // namespace moev
+
+extern "C" size_t moev_packed_size(int G, int N, int K, int dt) {
+  if (G < 1 || N < 1 || K < 32 || K % 32 != 0 || (dt != MOEV_BF16 && dt != MOEV_F32)) return 0;
+  return moev::packed_elems(G, N, K) * (dt == MOEV_BF16 ? 2 : 4);
+}
+
+extern "C" moev_status moev_pack_weights(const void* src, void* dst, int G, int N, int K, int dt,
+                                         void* stream) {
+  using namespace moev;
+  MOEV_CHECK(check_dtype(dt), MOEV_ERR_UNSUPPORTED);
+  MOEV_REQUIRE(G >= 1 && N >= 1, MOEV_ERR_INVALID_ARG, "need G >= 1 and N >= 1 (G=%d N=%d)", G, N);
+  MOEV_REQUIRE(K >= 32 && K % 32 == 0, MOEV_ERR_UNSUPPORTED, "K=%d must be a positive multiple of 32", K);
+  MOEV_CHECK(need_ptr(src, "src") && need_ptr(dst, "dst"), MOEV_ERR_INVALID_ARG);
+  const long long total = static_cast<long long>(G) * ((N + 15) / 16) * (K / 32) * 64;
+  const int blocks = static_cast<int>(min(8192ll, (total + 255) / 256));
+  const hipStream_t s = as_stream(stream);
+  if (dt == MOEV_BF16)
+    pack_kernel<u16><<<blocks, 256, 0, s>>>(static_cast<const u16*>(src), static_cast<u16*>(dst), G, N, K);
+  else
+    pack_kernel<float><<<blocks, 256, 0, s>>>(static_cast<const float*>(src), static_cast<float*>(dst), G, N, K);
+  return launch_status("moev_pack_weights");
 }

@@ -17,6 +17,12 @@ void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t*
                         const float* topk_w, const void* w_gate, const void* w_up,
                         const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
                         float* y_slots, void* ws, hipStream_t s);
+void launch_ffn_gate_up(const void* x, const int32_t* sorted_src, const int32_t* offsets,
+                        const void* w_gate, const void* w_up, int T, int H, int I, int E, int k,
+                        int ns, int dt, void* act, hipStream_t s);
+void launch_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* offsets,
+                     const float* topk_w, const void* w_down, int T, int H, int I, int E, int k,
+                     int ns, int dt, float* y_slots, hipStream_t s);
 void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
                     hipStream_t s);
 void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,

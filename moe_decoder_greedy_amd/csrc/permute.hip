@@ -116,9 +116,9 @@ moev_status validate_permute(const int32_t* topk_idx, int T, int k, int E, int n
   MOEV_REQUIRE(ns >= 0 && ns <= 8, MOEV_ERR_UNSUPPORTED, "shared experts ns=%d must be in [0, 8]", ns);
   MOEV_REQUIRE(static_cast<long long>(T) * (k + ns) < (1ll << 31), MOEV_ERR_UNSUPPORTED,
                "T*(k+ns) must be < 2^31");
-  MOEV_CHECK(need_ptr(offsets, "group_offsets"), MOEV_ERR_INVALID_ARG);
+  MOEV_CHECK(need_ptr(offsets, "group_offsets", 4), MOEV_ERR_INVALID_ARG);
   if (T == 0) return MOEV_OK;
-  MOEV_CHECK(need_ptr(topk_idx, "topk_idx") && need_ptr(sorted_src, "sorted_src"),
+  MOEV_CHECK(need_ptr(topk_idx, "topk_idx", 4) && need_ptr(sorted_src, "sorted_src", 4),
              MOEV_ERR_INVALID_ARG);
   return MOEV_OK;
 }

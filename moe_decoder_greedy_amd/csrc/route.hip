@@ -7,15 +7,20 @@
 // softmax renormalised over the selected experts, i.e. exp(l_r - l_max) over
 // the sum of the k chosen exp(l_j - l_max).
 //
-// Layout of one block (256 threads = 4 wavefronts, TPB tokens):
-//   phase 1  one wave per token: sum of squares (per-lane strided partials,
-//            then a butterfly), x = h * rsqrt-scale * gamma into LDS (fp32)
-//            and to x_out (rounded to the operand type);
-//   phase 2  wave w computes the logits of experts w, w+4, ... for all TPB
-//            tokens, streaming each router row once per block (coalesced
-//            8-byte bf16 loads) against the LDS copy of x;
-//   phase 3  one wave per token, one lane per expert: k rounds of a wavefront
-//            (value, index) arg max, then the renormalised softmax weights.
+// Layout of one block (1024 threads = 16 wavefronts, TPB = 4 tokens):
+//   start    wave w fetches the router rows of experts 4w..4w+3 into
+//            registers (coalesced 8-byte bf16 loads, all in flight), so the
+//            weight fetch overlaps phase 1;
+//   phase 1  waves 0..3, one per token: sum of squares (per-lane strided
+//            partials, then a DPP reduction), x = h * rsqrt-scale * gamma into
+//            LDS (fp32) and to x_out (rounded to the operand type);
+//   phase 2  every wave multiplies its 4 router rows against the LDS copy of
+//            the block's tokens;
+//   phase 3  one wave per token, one lane per expert: each lane's rank is
+//            the number of experts that beat it (read back from LDS), the
+//            k best file themselves by rank, then the renormalised softmax
+//            weights are formed in rank order.
+// Lane sums use DPP row/broadcast steps rather than LDS shuffles.
 // Every reduction has a fixed order, so a token's outputs do not depend on
 // which block or batch it lands in.
 #include "launch.h"
@@ -23,7 +28,9 @@
 namespace moev {
 namespace {
 
-constexpr int kRouteTPB = 4;
+constexpr int kRouteTPB = 4;         // tokens per block
+constexpr int kRouteThreads = 1024;   // 16 wavefronts
+constexpr int kExpertsPerWave = 4;    // 16 waves x 4 = 64 experts
 
 template <typename WT> struct Vec4;
 template <> struct Vec4<u16> {
@@ -57,95 +64,158 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     *reinterpret_cast<float4*>(dst + i) = Vec4<WT>::load(src + i);
 }
 
-template <typename WT>
-__global__ __launch_bounds__(256) void route_kernel(
+// NCH = ceil(H / 256): 4-element chunks per lane per row, a compile-time count
+// so that every router-row load of a wave is in flight at once.
+template <typename WT, int NCH>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const float* __restrict__ h, const WT* __restrict__ norm_w, float eps,
     const WT* __restrict__ wr, const float* __restrict__ bias, int T, int H, int E, int k,
     WT* __restrict__ x_out, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ logits_out) {
   extern __shared__ float smem[];
-  float* xs = smem;                   // [TPB][H]
-  float* lg = smem + kRouteTPB * H;   // [TPB][64]
+  float* xs = smem;                                             // [TPB][H]
+  float* lg = smem + kRouteTPB * H;                             // [TPB][64]
+  float* sel_v = lg + kRouteTPB * 64;                           // [TPB][64]
+  int* sel_i = reinterpret_cast<int*>(sel_v + kRouteTPB * 64);  // [TPB][64]
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * kRouteTPB;
 
-  // phase 1: RMSNorm, wave `wave` takes token t0 + wave
-  {
+  // router rows of this wave's experts, fetched before anything else so the
+  // fetch overlaps the RMSNorm phase
+  const int e0 = wave * kExpertsPerWave;
+  float4 wv[kExpertsPerWave][NCH];
+#pragma unroll
+  for (int u = 0; u < kExpertsPerWave; ++u) {
+    const int e = min(e0 + u, E - 1);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int i = min(lane * 4 + c * 256, H - 4);
+      wv[u][c] = Vec4<WT>::load(wr + static_cast<size_t>(e) * H + i);
+    }
+  }
+
+  // phase 1: RMSNorm, wave w < TPB takes token t0 + w
+  if (wave < kRouteTPB) {
     const int t = t0 + wave;
     if (t < T) {
       const float* hr = h + static_cast<size_t>(t) * H;
+      float4 hv[NCH], gv[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int i = lane * 4 + c * 256;
+        const bool in = i < H;
+        hv[c] = in ? *reinterpret_cast<const float4*>(hr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        gv[c] = (in && norm_w) ? Vec4<WT>::load(norm_w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
+      }
       float ss = 0.f;
-      for (int i = lane * 4; i < H; i += 256) {
-        float4 v = *reinterpret_cast<const float4*>(hr + i);
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-      }
-      ss = wave_sum(ss);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        ss += hv[c].x * hv[c].x + hv[c].y * hv[c].y + hv[c].z * hv[c].z + hv[c].w * hv[c].w;
+      ss = lane63(wave_sum_lane63(ss));
       const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
-      for (int i = lane * 4; i < H; i += 256) {
-        float4 v = *reinterpret_cast<const float4*>(hr + i);
-        float4 g = norm_w ? Vec4<WT>::load(norm_w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
-        float4 x = make_float4(v.x * r * g.x, v.y * r * g.y, v.z * r * g.z, v.w * r * g.w);
-        *reinterpret_cast<float4*>(xs + wave * H + i) = x;
-        Vec4<WT>::store(x_out + static_cast<size_t>(t) * H + i, x);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int i = lane * 4 + c * 256;
+        if (i < H) {
+          const float4 v = hv[c], g = gv[c];
+          const float4 x = make_float4(v.x * r * g.x, v.y * r * g.y, v.z * r * g.z, v.w * r * g.w);
+          *reinterpret_cast<float4*>(xs + wave * H + i) = x;
+          Vec4<WT>::store(x_out + static_cast<size_t>(t) * H + i, x);
+        }
       }
     }
   }
   __syncthreads();
 
-  // phase 2: router logits
+  // phase 2: router logits of this wave's experts for the block's tokens
   const int nt = min(kRouteTPB, T - t0);
-  for (int e = wave; e < E; e += 4) {
-    const WT* w = wr + static_cast<size_t>(e) * H;
-    float acc[kRouteTPB];
+  if (e0 < E) {
+    float acc[kExpertsPerWave][kRouteTPB];
 #pragma unroll
-    for (int tt = 0; tt < kRouteTPB; ++tt) acc[tt] = 0.f;
-    for (int i = lane * 4; i < H; i += 256) {
-      float4 wv = Vec4<WT>::load(w + i);
+    for (int u = 0; u < kExpertsPerWave; ++u)
 #pragma unroll
-      for (int tt = 0; tt < kRouteTPB; ++tt) {
-        float4 x = *reinterpret_cast<const float4*>(xs + tt * H + i);
-        acc[tt] += x.x * wv.x + x.y * wv.y + x.z * wv.z + x.w * wv.w;
+      for (int tt = 0; tt < kRouteTPB; ++tt) acc[u][tt] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int i = lane * 4 + c * 256;
+      if (i < H) {
+#pragma unroll
+        for (int tt = 0; tt < kRouteTPB; ++tt) {
+          const float4 x = *reinterpret_cast<const float4*>(xs + tt * H + i);
+#pragma unroll
+          for (int u = 0; u < kExpertsPerWave; ++u)
+            acc[u][tt] += x.x * wv[u][c].x + x.y * wv[u][c].y + x.z * wv[u][c].z + x.w * wv[u][c].w;
+        }
       }
     }
-    const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-    for (int tt = 0; tt < kRouteTPB; ++tt) {
-      float s = wave_sum(acc[tt]);
-      if (lane == 0 && tt < nt) lg[tt * 64 + e] = s + b;
+    for (int u = 0; u < kExpertsPerWave; ++u) {
+      const int e = e0 + u;
+      if (e < E) {
+        const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+        for (int tt = 0; tt < kRouteTPB; ++tt) {
+          const float s = wave_sum_lane63(acc[u][tt]);
+          if (lane == 63 && tt < nt) lg[tt * 64 + e] = s + b;
+        }
+      }
     }
   }
   __syncthreads();
 
-  // phase 3: top-k + renormalised softmax, one wave per token
-  {
+  // phase 3: top-k + renormalised softmax, one wave per token, one lane per
+  // expert.  Each lane counts the experts that beat it (larger logit, or equal
+  // logit and lower index): that count is its rank, and the k lanes of rank
+  // < k file themselves into sel_* by rank.
+  if (wave < kRouteTPB) {
     const int t = t0 + wave;
     if (t < T) {
-      float v = lane < E ? lg[wave * 64 + lane] : -INFINITY;
+      const float* row = lg + wave * 64;
+      const float v = lane < E ? row[lane] : -INFINITY;
       if (logits_out != nullptr && lane < E) logits_out[static_cast<size_t>(t) * E + lane] = v;
-      float top0 = 0.f, mine = 0.f;
-      int mine_idx = 0;
-      for (int r = 0; r < k; ++r) {
-        float bv = v;
-        int bi = lane;
-        wave_argmax(bv, bi);
-        if (r == 0) top0 = bv;
-        if (lane == r) { mine = bv; mine_idx = bi; }
-        if (lane == bi) v = -INFINITY;
+      int rank = 0;
+      for (int j = 0; j < E; ++j) rank += better(row[j], j, v, lane) ? 1 : 0;
+      if (lane < E && rank < k) {
+        sel_v[wave * 64 + rank] = v;
+        sel_i[wave * 64 + rank] = lane;
       }
-      const float ex = lane < k ? expf(mine - top0) : 0.f;
-      const float sum = wave_sum(ex);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       if (lane < k) {
-        topk_idx[static_cast<size_t>(t) * k + lane] = mine_idx;
-        topk_w[static_cast<size_t>(t) * k + lane] = ex / sum;
+        const float top0 = sel_v[wave * 64];
+        float sum = 0.f;
+        for (int j = 0; j < k; ++j) sum += expf(sel_v[wave * 64 + j] - top0);
+        topk_idx[static_cast<size_t>(t) * k + lane] = sel_i[wave * 64 + lane];
+        topk_w[static_cast<size_t>(t) * k + lane] = expf(sel_v[wave * 64 + lane] - top0) / sum;
       }
     }
   }
 }
 
+template <typename WT>
+void launch_route_t(int nch, dim3 grid, size_t lds, hipStream_t s, const float* h, const WT* norm_w,
+                    float eps, const WT* wr, const float* bias, int T, int H, int E, int k,
+                    WT* x_out, int32_t* idx, float* w, float* logits) {
+#define MOEV_ROUTE_CASE(N)                                                                 \
+  case N:                                                                                  \
+    route_kernel<WT, N><<<grid, kRouteThreads, lds, s>>>(h, norm_w, eps, wr, bias, T, H, E, k, x_out, \
+                                               idx, w, logits);                            \
+    break;
+  switch (nch) {
+    MOEV_ROUTE_CASE(1) MOEV_ROUTE_CASE(2) MOEV_ROUTE_CASE(3) MOEV_ROUTE_CASE(4)
+    MOEV_ROUTE_CASE(5) MOEV_ROUTE_CASE(6) MOEV_ROUTE_CASE(7) MOEV_ROUTE_CASE(8)
+    MOEV_ROUTE_CASE(9) MOEV_ROUTE_CASE(10) MOEV_ROUTE_CASE(11) MOEV_ROUTE_CASE(12)
+    MOEV_ROUTE_CASE(13) MOEV_ROUTE_CASE(14) MOEV_ROUTE_CASE(15) MOEV_ROUTE_CASE(16)
+    default: break;  // H <= 3840 is validated, so nch <= 16
+  }
+#undef MOEV_ROUTE_CASE
+}
+
 moev_status check_hidden(int H) {
-  if (H < 64 || H > 4032 || H % 64 != 0) {
-    set_error("hidden size %d must be a multiple of 64 in [64, 4032]", H);
+  if (H < 64 || H > 3840 || H % 64 != 0) {
+    set_error("hidden size %d must be a multiple of 64 in [64, 3840]", H);
     return MOEV_ERR_UNSUPPORTED;
   }
   return MOEV_OK;
@@ -165,18 +235,17 @@ void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, i
 void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,
                   const float* bias, int T, int H, int E, int k, int dt, void* x_out,
                   int32_t* topk_idx, float* topk_w, float* logits_out, hipStream_t s) {
-  const int blocks = (T + kRouteTPB - 1) / kRouteTPB;
-  const size_t lds = (static_cast<size_t>(kRouteTPB) * H + kRouteTPB * 64) * sizeof(float);
+  const dim3 grid((T + kRouteTPB - 1) / kRouteTPB);
+  const size_t lds = (static_cast<size_t>(kRouteTPB) * H + 3 * kRouteTPB * 64) * sizeof(float);
+  const int nch = (H + 255) / 256;
   if (dt == MOEV_BF16)
-    route_kernel<u16><<<blocks, 256, lds, s>>>(h, static_cast<const u16*>(norm_w), eps,
-                                                static_cast<const u16*>(w_router), bias, T, H, E, k,
-                                                static_cast<u16*>(x_out), topk_idx, topk_w,
-                                                logits_out);
+    launch_route_t<u16>(nch, grid, lds, s, h, static_cast<const u16*>(norm_w), eps,
+                        static_cast<const u16*>(w_router), bias, T, H, E, k,
+                        static_cast<u16*>(x_out), topk_idx, topk_w, logits_out);
   else
-    route_kernel<float><<<blocks, 256, lds, s>>>(h, static_cast<const float*>(norm_w), eps,
-                                                  static_cast<const float*>(w_router), bias, T, H, E,
-                                                  k, static_cast<float*>(x_out), topk_idx, topk_w,
-                                                  logits_out);
+    launch_route_t<float>(nch, grid, lds, s, h, static_cast<const float*>(norm_w), eps,
+                          static_cast<const float*>(w_router), bias, T, H, E, k,
+                          static_cast<float*>(x_out), topk_idx, topk_w, logits_out);
 }
 
 moev_status validate_route(const float* h, const void* norm_w, const void* w_router,
@@ -190,9 +259,9 @@ moev_status validate_route(const float* h, const void* norm_w, const void* w_rou
   MOEV_REQUIRE(k >= 1 && k <= E, MOEV_ERR_UNSUPPORTED, "top-k k=%d must be in [1, E=%d]", k, E);
   if (T == 0) return MOEV_OK;
   MOEV_CHECK(need_ptr(h, "h") && opt_ptr(norm_w, "norm_w") && need_ptr(w_router, "w_router") &&
-                 opt_ptr(bias, "bias") && need_ptr(x_out, "x_out") &&
-                 need_ptr(topk_idx, "topk_idx") && need_ptr(topk_w, "topk_w") &&
-                 opt_ptr(logits_out, "logits_out"),
+                 opt_ptr(bias, "bias", 4) && need_ptr(x_out, "x_out") &&
+                 need_ptr(topk_idx, "topk_idx", 4) && need_ptr(topk_w, "topk_w", 4) &&
+                 opt_ptr(logits_out, "logits_out", 4),
              MOEV_ERR_INVALID_ARG);
   return MOEV_OK;
 }
@@ -203,7 +272,7 @@ moev_status validate_embed(const int32_t* tokens, const void* emb, int T, int H,
   if (moev_status st = check_hidden(H)) return st;
   MOEV_REQUIRE(T >= 0 && V >= 1, MOEV_ERR_INVALID_ARG, "need T >= 0 and V >= 1 (T=%d V=%d)", T, V);
   if (T == 0) return MOEV_OK;
-  MOEV_CHECK(need_ptr(tokens, "tokens") && need_ptr(emb, "emb") && need_ptr(h_out, "h_out"),
+  MOEV_CHECK(need_ptr(tokens, "tokens", 4) && need_ptr(emb, "emb") && need_ptr(h_out, "h_out"),
              MOEV_ERR_INVALID_ARG);
   return MOEV_OK;
 }

@@ -48,8 +48,8 @@ moev_status validate_model(const moev_model* m, int B, int K) {
   MOEV_CHECK(check_dtype(m->dtype), MOEV_ERR_UNSUPPORTED);
   MOEV_REQUIRE(B >= 0 && K >= 0, MOEV_ERR_INVALID_ARG, "need B >= 0 and K >= 0 (B=%d K=%d)", B, K);
   MOEV_REQUIRE(K <= 64, MOEV_ERR_UNSUPPORTED, "K=%d drafts exceeds 64", K);
-  MOEV_REQUIRE(m->hidden >= 64 && m->hidden <= 4032 && m->hidden % 64 == 0, MOEV_ERR_UNSUPPORTED,
-               "hidden size %d must be a multiple of 64 in [64, 4032]", m->hidden);
+  MOEV_REQUIRE(m->hidden >= 64 && m->hidden <= 3840 && m->hidden % 64 == 0, MOEV_ERR_UNSUPPORTED,
+               "hidden size %d must be a multiple of 64 in [64, 3840]", m->hidden);
   MOEV_REQUIRE(m->inter >= 64 && m->inter <= 8192 && m->inter % 64 == 0, MOEV_ERR_UNSUPPORTED,
                "intermediate size %d must be a multiple of 64 in [64, 8192]", m->inter);
   MOEV_REQUIRE(m->n_routed >= 1 && m->n_routed <= 64, MOEV_ERR_UNSUPPORTED,
@@ -71,7 +71,7 @@ moev_status validate_model(const moev_model* m, int B, int K) {
   for (int l = 0; l < m->n_layers; ++l) {
     const moev_layer_weights& lw = m->layers[l];
     if (!(opt_ptr(lw.norm, "layer.norm") && need_ptr(lw.w_router, "layer.w_router") &&
-          opt_ptr(lw.bias, "layer.bias") && need_ptr(lw.w_gate, "layer.w_gate") &&
+          opt_ptr(lw.bias, "layer.bias", 4) && need_ptr(lw.w_gate, "layer.w_gate") &&
           need_ptr(lw.w_up, "layer.w_up") && need_ptr(lw.w_down, "layer.w_down"))) {
       set_error("layer %d: %s", l, moev_last_error());
       return MOEV_ERR_INVALID_ARG;
@@ -88,16 +88,22 @@ extern "C" size_t moev_verify_step_workspace_size(const moev_model* m, int B, in
   return moev::layout(*m, B * (K + 1)).total;
 }
 
-extern "C" moev_status moev_verify_step(const moev_model* m, const int32_t* tokens, int B, int K,
-                                        int32_t* greedy, int32_t* n_accept, int32_t* commit,
-                                        int32_t* commit_len, int32_t* next_last, void* ws,
-                                        size_t ws_bytes, void* stream) {
-  using namespace moev;
+namespace moev {
+namespace {
+
+moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, int32_t* greedy,
+                     int32_t* n_accept, int32_t* commit, int32_t* commit_len, int32_t* next_last,
+                     void* ws, size_t ws_bytes, const moev_step_probe* probe, void* stream) {
   if (moev_status st = validate_model(m, B, K)) return st;
   if (B == 0) return MOEV_OK;
-  MOEV_CHECK(need_ptr(tokens, "tokens") && need_ptr(greedy, "greedy") &&
-                 need_ptr(n_accept, "n_accept") && need_ptr(commit, "commit"),
+  MOEV_CHECK(need_ptr(tokens, "tokens", 4) && need_ptr(greedy, "greedy", 4) &&
+                 need_ptr(n_accept, "n_accept", 4) && need_ptr(commit, "commit", 4),
              MOEV_ERR_INVALID_ARG);
+  if (probe != nullptr) {
+    MOEV_REQUIRE(probe->stage >= MOEV_STAGE_ROUTE && probe->stage <= MOEV_STAGE_HEAD &&
+                     probe->n >= 0 && (probe->n == 0 || (probe->before && probe->after)),
+                 MOEV_ERR_INVALID_ARG, "bad probe");
+  }
   const int T = B * (K + 1);
   const StepLayout L = layout(*m, T);
   MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE,
@@ -116,20 +122,58 @@ extern "C" moev_status moev_verify_step(const moev_model* m, const int32_t* toke
   void* ffn_ws = base + L.ffn;
   void* head_ws = base + L.head;
   const hipStream_t s = as_stream(stream);
-  const int H = m->hidden, E = m->n_routed, k = m->top_k, ns = m->n_shared;
+  const int H = m->hidden, E = m->n_routed, k = m->top_k, ns = m->n_shared, I = m->inter;
+  const int dt = m->dtype;
 
-  launch_embed(tokens, m->emb, T, H, m->vocab, m->dtype, h, s);
+  // probe events around one stage (index = layer, or 0 for the head)
+  auto mark = [&](int stage, int index, bool after) {
+    if (probe == nullptr || probe->stage != stage || index >= probe->n) return;
+    hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
+  };
+
+  launch_embed(tokens, m->emb, T, H, m->vocab, dt, h, s);
   for (int l = 0; l < m->n_layers; ++l) {
     const moev_layer_weights& lw = m->layers[l];
-    launch_route(h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, m->dtype, x, idx, w,
-                 nullptr, s);
+    mark(MOEV_STAGE_ROUTE, l, false);
+    launch_route(h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, dt, x, idx, w, nullptr, s);
+    mark(MOEV_STAGE_ROUTE, l, true);
+    mark(MOEV_STAGE_PERMUTE, l, false);
     launch_permute(idx, T, k, E, ns, offsets, sorted, s);
-    launch_grouped_ffn(x, sorted, offsets, w, lw.w_gate, lw.w_up, lw.w_down, T, H, m->inter, E, k,
-                       ns, m->dtype, y, ffn_ws, s);
+    mark(MOEV_STAGE_PERMUTE, l, true);
+    mark(MOEV_STAGE_GATE_UP, l, false);
+    launch_ffn_gate_up(x, sorted, offsets, lw.w_gate, lw.w_up, T, H, I, E, k, ns, dt, ffn_ws, s);
+    mark(MOEV_STAGE_GATE_UP, l, true);
+    mark(MOEV_STAGE_DOWN, l, false);
+    launch_ffn_down(ffn_ws, sorted, offsets, w, lw.w_down, T, H, I, E, k, ns, dt, y, s);
+    mark(MOEV_STAGE_DOWN, l, true);
+    mark(MOEV_STAGE_COMBINE, l, false);
     launch_combine(y, h, T, H, k + ns, h, s);
+    mark(MOEV_STAGE_COMBINE, l, true);
   }
-  launch_lmhead(h, m->norm_f, m->eps, m->w_lm, T, H, m->vocab, m->dtype, greedy, nullptr, nullptr,
+  mark(MOEV_STAGE_HEAD, 0, false);
+  launch_lmhead(h, m->norm_f, m->eps, m->w_lm, T, H, m->vocab, dt, greedy, nullptr, nullptr,
                 head_ws, s);
+  mark(MOEV_STAGE_HEAD, 0, true);
   launch_verify(tokens, greedy, B, K, n_accept, commit, commit_len, next_last, s);
   return launch_status("moev_verify_step");
+}
+
+}  // namespace
+}  // namespace moev
+
+extern "C" moev_status moev_verify_step(const moev_model* m, const int32_t* tokens, int B, int K,
+                                        int32_t* greedy, int32_t* n_accept, int32_t* commit,
+                                        int32_t* commit_len, int32_t* next_last, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  return moev::run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last, ws,
+                        ws_bytes, nullptr, stream);
+}
+
+extern "C" moev_status moev_verify_step_probed(const moev_model* m, const int32_t* tokens, int B,
+                                               int K, int32_t* greedy, int32_t* n_accept,
+                                               int32_t* commit, int32_t* commit_len,
+                                               int32_t* next_last, void* ws, size_t ws_bytes,
+                                               const moev_step_probe* probe, void* stream) {
+  return moev::run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last, ws,
+                        ws_bytes, probe, stream);
 }

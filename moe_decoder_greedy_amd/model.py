@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from .ops import BF16, F32, check, lib, ptr, stream_handle
+from .ops import BF16, F32, check, lib, pack_weights, ptr, stream_handle
 
 
 def to_device(a: Optional[np.ndarray], dtype: str, device) -> Optional[torch.Tensor]:
@@ -40,11 +40,14 @@ class DeviceModel:
         dt = self.dtype
         self.layers = []
         for d in weights["layers"]:
-            self.layers.append({key: to_device(d[key], dt if key != "bias" else "f32", self.device)
-                                for key in ("norm", "w_router", "w_gate", "w_up", "w_down", "bias")})
+            L = {key: to_device(d[key], dt if key != "bias" else "f32", self.device)
+                 for key in ("norm", "w_router", "bias")}
+            for key in ("w_gate", "w_up", "w_down"):   # packed on the GPU, row-major copy freed
+                L[key] = pack_weights(to_device(d[key], dt, self.device))
+            self.layers.append(L)
         self.emb = to_device(weights["emb"], dt, self.device)
         self.norm_f = to_device(weights["norm_f"], dt, self.device)
-        self.w_lm = to_device(weights["w_lm"], dt, self.device)
+        self.w_lm = pack_weights(to_device(weights["w_lm"], dt, self.device))
         n = len(self.layers)
         self._c_layers = (_lib.LayerWeights * max(n, 1))()
         for i, L in enumerate(self.layers):
@@ -91,6 +94,26 @@ class DeviceModel:
             self.c_model, ptr(tokens), B, K, ptr(out["greedy"]), ptr(out["n_accept"]),
             ptr(out["commit"]), ptr(out["commit_len"]), ptr(out["next_last"]), ptr(ws), ws.numel(),
             stream_handle(stream)))
+        return out
+
+    def verify_step_probed(self, tokens: torch.Tensor, stage: str, before, after,
+                           out: Optional[dict] = None, stream=None) -> dict:
+        """``verify_step`` that also records the torch.cuda.Events ``before[i]``
+        / ``after[i]`` around stage ``stage`` of layer i (or of the head)."""
+        B, K1 = tokens.shape
+        K = K1 - 1
+        out = self.alloc_outputs(B, K) if out is None else out
+        ws = self.workspace(B, K)
+        for e in list(before) + list(after):
+            e.record()   # the runtime creates the event on first record
+        n = len(before)
+        arr_b = (ctypes.c_void_p * n)(*[e.cuda_event for e in before])
+        arr_a = (ctypes.c_void_p * n)(*[e.cuda_event for e in after])
+        probe = _lib.StepProbe(_lib.STAGES[stage], n, arr_b, arr_a)
+        check("moev_verify_step_probed", lib().moev_verify_step_probed(
+            self.c_model, ptr(tokens), B, K, ptr(out["greedy"]), ptr(out["n_accept"]),
+            ptr(out["commit"]), ptr(out["commit_len"]), ptr(out["next_last"]), ptr(ws), ws.numel(),
+            ctypes.byref(probe), stream_handle(stream)))
         return out
 
     def greedy(self, tokens: torch.Tensor) -> torch.Tensor:

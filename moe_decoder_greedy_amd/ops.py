@@ -52,6 +52,21 @@ def _empty(shape, dtype, like: torch.Tensor):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+def pack_weights(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """Row-major [G, N, K] (or [N, K]) weights -> the fragment-packed layout
+    the GEMM entry points take, returned with shape [G, ceil(N/16)*16, K] (or
+    [ceil(N/16)*16, K]); the row count keeps the padded tiles."""
+    two_d = w.dim() == 2
+    G, N, K = (1, *w.shape) if two_d else w.shape
+    n = lib().moev_packed_size(G, N, K, dtype_code(w))
+    npad = (N + 15) // 16 * 16
+    out = torch.empty((G, npad, K), dtype=w.dtype, device=w.device)
+    assert out.numel() * out.element_size() == n
+    check("moev_pack_weights", lib().moev_pack_weights(ptr(w), ptr(out), G, N, K, dtype_code(w),
+                                                       stream_handle(stream)))
+    return out[0] if two_d else out
+
+
 def moe_embed(tokens: torch.Tensor, emb: torch.Tensor, out: Optional[torch.Tensor] = None,
               stream=None) -> torch.Tensor:
     T = tokens.numel()
@@ -110,6 +125,32 @@ def moe_grouped_ffn(x: torch.Tensor, sorted_src: torch.Tensor, offsets: torch.Te
     return y_slots
 
 
+def moe_ffn_gate_up(x: torch.Tensor, sorted_src: torch.Tensor, offsets: torch.Tensor,
+                    w_gate: torch.Tensor, w_up: torch.Tensor, n_routed: int, k: int, n_shared: int,
+                    act=None, stream=None) -> torch.Tensor:
+    T, H = x.shape
+    G, I, _ = w_gate.shape
+    dt = dtype_code(w_gate)
+    act = _empty((T * (k + n_shared), I), torch_dtype(dt), x) if act is None else act
+    check("moe_ffn_gate_up", lib().moe_ffn_gate_up(
+        ptr(x), ptr(sorted_src), ptr(offsets), ptr(w_gate), ptr(w_up), T, H, I, n_routed, k,
+        n_shared, dt, ptr(act), stream_handle(stream)))
+    return act
+
+
+def moe_ffn_down(act: torch.Tensor, sorted_src: torch.Tensor, offsets: torch.Tensor,
+                 topk_w: torch.Tensor, w_down: torch.Tensor, T: int, n_routed: int, k: int,
+                 n_shared: int, y_slots=None, stream=None) -> torch.Tensor:
+    G, H, I = w_down.shape
+    dt = dtype_code(w_down)
+    S = k + n_shared
+    y_slots = _empty((T, S, H), torch.float32, act) if y_slots is None else y_slots
+    check("moe_ffn_down", lib().moe_ffn_down(
+        ptr(act), ptr(sorted_src), ptr(offsets), ptr(topk_w), ptr(w_down), T, H, I, n_routed, k,
+        n_shared, dt, ptr(y_slots), stream_handle(stream)))
+    return y_slots
+
+
 def moe_combine(y_slots: torch.Tensor, h_in: Optional[torch.Tensor], out=None, stream=None) -> torch.Tensor:
     T, S, H = y_slots.shape
     out = _empty((T, H), torch.float32, y_slots) if out is None else out
@@ -125,9 +166,11 @@ def lmhead_workspace(T: int, H: int, V: int, dt: int, device) -> torch.Tensor:
 
 def lmhead_argmax(h: torch.Tensor, norm_f: Optional[torch.Tensor], eps: float, w_lm: torch.Tensor,
                   want_max: bool = False, want_logits: bool = False, ws=None, argmax_out=None,
-                  stream=None):
+                  vocab: Optional[int] = None, stream=None):
+    """``w_lm`` is fragment-packed (``pack_weights``); ``vocab`` is the real
+    row count when it is not a multiple of 16."""
     T, H = h.shape
-    V = w_lm.shape[0]
+    V = w_lm.shape[0] if vocab is None else vocab
     dt = dtype_code(w_lm)
     argmax_out = _empty((T,), torch.int32, h) if argmax_out is None else argmax_out
     mx = _empty((T,), torch.float32, h) if want_max else None

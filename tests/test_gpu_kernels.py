@@ -134,8 +134,8 @@ def test_grouped_ffn(ops, tiny, dec_layer, zipf_layer, which, T):
     report("grouped_ffn", which=which, T=T)
     x_op, idx, w32, off, src = _ffn_case(shape, L, dt, T, seed=21)
     y_d = ops.moe_grouped_ffn(dev_operand(x_op, dt), dev_i32(src), dev_i32(off), dev_f32(w32),
-                              dev_bits(L["w_gate"], dt), dev_bits(L["w_up"], dt),
-                              dev_bits(L["w_down"], dt), shape.n_routed, shape.top_k, shape.n_shared)
+                              ops.pack_weights(dev_bits(L["w_gate"], dt)), ops.pack_weights(dev_bits(L["w_up"], dt)),
+                              ops.pack_weights(dev_bits(L["w_down"], dt)), shape.n_routed, shape.top_k, shape.n_shared)
     torch.cuda.synchronize()
     y = host(y_d)
     args = (x_op, src, off, w32, L["w_gate"], L["w_up"], L["w_down"], dt, shape.top_k, shape.n_shared)
@@ -166,8 +166,8 @@ def test_grouped_ffn_prefill_sampled(ops, dec_layer):
     w32 = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
     off, src = oracle.permute(idx, shape.n_routed, shape.n_shared)
     y_d = ops.moe_grouped_ffn(dev_operand(x_op, dt), dev_i32(src), dev_i32(off), dev_f32(w32),
-                              dev_bits(L["w_gate"], dt), dev_bits(L["w_up"], dt),
-                              dev_bits(L["w_down"], dt), shape.n_routed, shape.top_k, shape.n_shared)
+                              ops.pack_weights(dev_bits(L["w_gate"], dt)), ops.pack_weights(dev_bits(L["w_up"], dt)),
+                              ops.pack_weights(dev_bits(L["w_down"], dt)), shape.n_routed, shape.top_k, shape.n_shared)
     torch.cuda.synchronize()
     sample = np.sort(rng.choice(T, 192, replace=False))
     y_s = host(y_d[torch.from_numpy(sample).cuda()])
@@ -215,8 +215,9 @@ def test_lmhead(ops, V, H, T, dt):
     w_lm = _head_case(V, H, dt, seed=V + T)
     h = np.random.default_rng(T).standard_normal((T, H)).astype(np.float32)
     gamma = np.ones(H, np.float32) if dt == "f32" else np.full(H, 0x3F80, np.uint16)
-    am_d, mx_d, lg_d = ops.lmhead_argmax(dev_f32(h), dev_bits(gamma, dt), 1e-6, dev_bits(w_lm, dt),
-                                         want_max=True, want_logits=True)
+    am_d, mx_d, lg_d = ops.lmhead_argmax(dev_f32(h), dev_bits(gamma, dt), 1e-6,
+                                         ops.pack_weights(dev_bits(w_lm, dt)), want_max=True,
+                                         want_logits=True, vocab=V)
     torch.cuda.synchronize()
     tight = oracle.lm_head(h, gamma, w_lm, dt, 1e-6, "bf16", keep_logits=True)
     exact = oracle.lm_head(h, gamma, w_lm, dt, 1e-6, "exact", keep_logits=True)
@@ -241,7 +242,7 @@ def test_lmhead_planted_tie(ops):
     w[hi] = w[lo]
     h = np.random.default_rng(9).standard_normal((T, H)).astype(np.float32)
     h[0] = (w[lo].astype(np.uint32) << 16).view(np.float32) * 50   # aligned with row lo
-    am_d, _, _ = ops.lmhead_argmax(dev_f32(h), None, 1e-6, dev_bits(w, "bf16"))
+    am_d, _, _ = ops.lmhead_argmax(dev_f32(h), None, 1e-6, ops.pack_weights(dev_bits(w, "bf16")))
     am = host(am_d)
     assert am[0] == lo
 
@@ -280,8 +281,8 @@ def test_layer_chain(ops, tiny, dec_layer, zipf_layer, which, T):
     x_d, idx_d, w_d, _ = ops.moe_route(hd, dev_bits(L["norm"], dt), shape.eps, dev_bits(L["w_router"], dt),
                                        None if L["bias"] is None else dev_f32(L["bias"]), shape.top_k)
     off_d, src_d = ops.moe_permute(idx_d, shape.n_routed, shape.n_shared)
-    y_d = ops.moe_grouped_ffn(x_d, src_d, off_d, w_d, dev_bits(L["w_gate"], dt), dev_bits(L["w_up"], dt),
-                              dev_bits(L["w_down"], dt), shape.n_routed, shape.top_k, shape.n_shared)
+    y_d = ops.moe_grouped_ffn(x_d, src_d, off_d, w_d, ops.pack_weights(dev_bits(L["w_gate"], dt)), ops.pack_weights(dev_bits(L["w_up"], dt)),
+                              ops.pack_weights(dev_bits(L["w_down"], dt)), shape.n_routed, shape.top_k, shape.n_shared)
     h_d = ops.moe_combine(y_d, hd)
     torch.cuda.synchronize()
     ref = oracle.moe_layer(h, L, dt, shape.top_k, shape.n_routed, shape.n_shared, shape.eps, "bf16")
@@ -292,3 +293,23 @@ def test_layer_chain(ops, tiny, dec_layer, zipf_layer, which, T):
     report("layer_chain", which=which, T=T, flagged=int((~ok).sum()), err_tight=e_t, err_exact=e_x)
     assert e_x < BAR[dt]
     assert e_t < (2e-3 if dt == "bf16" else 1e-5)
+
+
+# ---------------------------------------------------------------- packing
+
+@pytest.mark.parametrize("G,N,K,dt", [(3, 64, 128, "bf16"), (2, 1280, 896, "bf16"), (1, 77, 64, "f32"),
+                                      (1, 1000, 256, "bf16")])
+def test_pack_weights_layout(ops, G, N, K, dt):
+    """The packed buffer against the layout's definition, index by index."""
+    rng = np.random.default_rng(G * N)
+    w = rng.standard_normal((G, N, K)).astype(np.float32)
+    if dt == "bf16":
+        w = synth.f32_to_bf16_bits(w)
+    got = host(ops.pack_weights(dev_bits(w, dt))).reshape(-1)
+    ref_w = oracle.to_f64(w, dt)
+    nt, nkb = (N + 15) // 16, K // 32
+    g, t, b, lane, e = np.meshgrid(np.arange(G), np.arange(nt), np.arange(nkb), np.arange(64),
+                                   np.arange(8), indexing="ij")
+    row, col = 16 * t + lane % 16, 32 * b + 8 * (lane // 16) + e
+    ref = np.where(row < N, ref_w[g, np.minimum(row, N - 1), col], 0.0).reshape(-1)
+    np.testing.assert_array_equal(got, ref)
