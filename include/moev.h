@@ -36,7 +36,7 @@
  * ns shared experts, G = E + ns expert groups (routed 0..E-1, shared E..G-1),
  * S = k + ns slots per token, I expert intermediate width, V vocabulary.
  * Limits: 1 <= E <= 64, 1 <= k <= E, 0 <= ns <= 8, H and I multiples of 64,
- * 64 <= H <= 3840, 64 <= I <= 8192, T * S < 2^31.
+ * 64 <= H <= 3072, 64 <= I <= 8192, T * S < 2^31.
  * Weight/operand type `dt`: MOEV_BF16 (bf16 bit patterns, GEMMs on bf16 MFMA
  * with fp32 accumulation) or MOEV_F32 (fp32 MFMA).  Residual stream, router
  * weights out, expert outputs and logits are always fp32.
@@ -238,7 +238,8 @@ typedef struct moev_model {
  *   greedy   int32 [B, K+1] (written): greedy token after every input token
  *   n_accept, commit, commit_len, next_last: as mtp_verify
  *   ws       workspace of moev_verify_step_workspace_size() bytes
- * K = 0 is plain greedy decoding of one token per sequence.
+ * K = 0 is plain greedy decoding of one token per sequence.  Needs k + ns <= 16
+ * (each layer's residual add is folded into the next router launch).
  */
 size_t moev_verify_step_workspace_size(const moev_model* m, int B, int K);
 moev_status moev_verify_step(const moev_model* m, const int32_t* tokens, int B, int K,

@@ -49,10 +49,23 @@ constexpr int kKB = kKC / 32;    // MFMA K blocks per chunk
 constexpr int kNB = MOEV_KNB;    // LDS path: weight ring depth in chunks
 constexpr int kNBD = MOEV_KNBD;  // direct path: ring depth in K blocks
 constexpr int kFrag = 512;       // elements of one packed 16x32 fragment
-constexpr int kRtDown = 1;       // 16-row tiles per wave, down projection
-constexpr int kRtHead = 2;       // 16-row tiles per wave, LM head
-constexpr int kWavesFfn = 4;     // wavefronts per workgroup, expert GEMMs
-constexpr int kWavesHead = 8;    // wavefronts per workgroup, LM head (256 rows)
+#ifndef MOEV_RT_DOWN
+#define MOEV_RT_DOWN 1
+#endif
+#ifndef MOEV_RT_HEAD
+#define MOEV_RT_HEAD 2
+#endif
+#ifndef MOEV_WAVES_HEAD
+#define MOEV_WAVES_HEAD 8
+#endif
+constexpr int kRtDown = MOEV_RT_DOWN;        // 16-row tiles per wave, down projection
+constexpr int kRtHead = MOEV_RT_HEAD;        // 16-row tiles per wave, LM head
+constexpr int kWavesFfn = 4;                 // wavefronts per workgroup, expert GEMMs
+#ifndef MOEV_TILE_MIN_TOKENS
+#define MOEV_TILE_MIN_TOKENS 512
+#endif
+constexpr int kTileMinTokens = MOEV_TILE_MIN_TOKENS;  // larger batches use the tile schedule
+constexpr int kWavesHead = MOEV_WAVES_HEAD;  // wavefronts per workgroup, LM head
 
 // MT = tokens per pass (32, 64 or 128 = 2, 4 or 8 MFMA column tiles).  The
 // variant only changes how many accumulators and LDS rows a workgroup holds;
@@ -404,6 +417,242 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tile schedule for large groups (prefill-sized batches).
+//
+// One workgroup computes one (group, column tile, 128-token tile): 4
+// wavefronts x 4 weight tiles of 16 rows (gate/up: 2 gate + the same 2 up
+// tiles, i.e. 32 intermediate columns per wave, 128 per workgroup; down: 64
+// hidden rows per wave, 256 per workgroup) against 8 token tiles.  Weight
+// fragments come straight from the packed layout into a register ring; the
+// token rows go through a double-buffered LDS chunk (one barrier per 64-wide
+// K chunk), and the next chunk's rows are fetched into registers while the
+// current one is multiplied.  Tiles of one (group, column tile) are
+// consecutive in the tile order and the order is laid out so that consecutive
+// tiles land on the same XCD: the workgroups sharing a weight slab run side
+// by side and read it through one L2.
+// Accumulation is the same single fp32 chain over K blocks in order with the
+// same MFMA as the streaming schedule, so results are bitwise identical.
+constexpr int kTileTok = 128;                 // tokens per tile
+constexpr int kTileRt = 4;                    // 16-row weight tiles per wave
+constexpr int kTileNT = kTileTok / 16;        // token tiles per wave
+constexpr int kTileThreads = 256;
+constexpr int kTileNB = 4;                    // weight ring depth, in chunks (even)
+constexpr int kXcds = 8;
+
+template <int MODE> constexpr int tile_cols() { return MODE == kGateUp ? 128 : 256; }
+
+template <typename WT, int MODE>
+__global__ __launch_bounds__(kTileThreads) void tile_gemm(GemmArgs a, int n_ctiles, int G) {
+  using C = Cfg<WT, kTileTok>;
+  constexpr int kVecs = kTileTok * C::kVecPerRow;             // 16-B vectors per chunk
+  constexpr int kStage = kVecs / kTileThreads;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileTok * C::kRowBytes];
+  __shared__ int tile_info[3];  // group, column tile, token tile (-1: no work)
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r16 = lane & 15;
+  const int q = lane >> 4;
+
+  // XCD-aware tile index: hardware deals consecutive block ids round-robin
+  // over the XCDs, so tile = xcd * (grid / 8) + (bid / 8) keeps a run of
+  // consecutive tiles on one XCD.
+  const int nb = gridDim.x;
+  const int bid = blockIdx.x;
+  const int tile = (bid % kXcds) * (nb / kXcds) + bid / kXcds;
+  if (tid == 0) {
+    int run = 0, g = -1, ct = 0, mt = 0;
+    for (int gg = 0; gg < G && g < 0; ++gg) {
+      const int M = max(0, min(a.offsets[gg + 1], a.P) - max(min(a.offsets[gg], a.P), 0));
+      const int mtiles = (M + kTileTok - 1) / kTileTok;
+      const int n = mtiles * n_ctiles;
+      if (tile < run + n) {
+        g = gg;
+        ct = (tile - run) / mtiles;
+        mt = (tile - run) - ct * mtiles;
+      }
+      run += n;
+    }
+    tile_info[0] = g;
+    tile_info[1] = ct;
+    tile_info[2] = mt;
+  }
+  __syncthreads();
+  const int g = tile_info[0];
+  if (g < 0) return;
+  const int ct = tile_info[1];
+  const int off = clampi(a.offsets[g], 0, a.P);
+  const int M = clampi(a.offsets[g + 1], off, a.P) - off;
+  const int m0 = tile_info[2] * kTileTok;
+  const int mp = min(kTileTok, M - m0);
+
+  const WT* __restrict__ w0 = static_cast<const WT*>(a.w0);
+  const WT* __restrict__ w1 = static_cast<const WT*>(a.w1);
+  const WT* __restrict__ xsrc = static_cast<const WT*>(a.x);
+  const int K = a.K;
+  const int nkb = K / 32;
+  const int nchunks = K / kKC;
+
+  // this wave's weight tiles and their first output row
+  const WT* wp[kTileRt];
+  int rowbase[kTileRt];
+#pragma unroll
+  for (int rt = 0; rt < kTileRt; ++rt) {
+    int rb;
+    const WT* base;
+    if (MODE == kGateUp) {  // tiles 0,1: gate columns c0, c0+16; tiles 2,3: up, same columns
+      rb = ct * tile_cols<MODE>() + wave * 32 + (rt & 1) * 16;
+      base = rt < 2 ? w0 : w1;
+    } else {
+      rb = ct * tile_cols<MODE>() + wave * 64 + rt * 16;
+      base = w0;
+    }
+    rowbase[rt] = rb;
+    wp[rt] = base + static_cast<long long>(g) * a.w_group + static_cast<long long>(rb / 16) * nkb * kFrag +
+             lane * 8;
+  }
+
+  // token rows of this thread's staging vectors (nullptr: zero-fill)
+  const WT* src[kStage];
+#pragma unroll
+  for (int s = 0; s < kStage; ++s) {
+    const int v = tid + s * kTileThreads;
+    const int row = v / C::kVecPerRow;
+    const int cv = v - row * C::kVecPerRow;
+    src[s] = row < mp ? xsrc + operand_row<MODE>(a, off, m0, row) * K + cv * C::kEpv : nullptr;
+  }
+  auto fetch = [&](uint4 (&st)[kStage], int c) {
+#pragma unroll
+    for (int s = 0; s < kStage; ++s)
+      st[s] = src[s] ? *reinterpret_cast<const uint4*>(src[s] + c * kKC) : make_uint4(0, 0, 0, 0);
+  };
+  auto put = [&](const uint4 (&st)[kStage], unsigned char* buf) {
+#pragma unroll
+    for (int s = 0; s < kStage; ++s) {
+      const int v = tid + s * kTileThreads;
+      const int row = v / C::kVecPerRow;
+      const int cv = v - row * C::kVecPerRow;
+      *reinterpret_cast<uint4*>(buf + row * C::kRowBytes + cv * 16) = st[s];
+    }
+  };
+
+  f32x4 acc[kTileRt][kTileNT];
+#pragma unroll
+  for (int rt = 0; rt < kTileRt; ++rt)
+#pragma unroll
+    for (int j = 0; j < kTileNT; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Pipeline (loads complete in issue order, so every wait also covers the
+  // loads issued before it): in iteration c the token rows of chunk c+2 and
+  // the weights of chunk c+kTileNB are requested, and the rows of chunk c+1
+  // (requested an iteration earlier, ahead of the weights of chunk c+kTileNB-1)
+  // are written to the other LDS buffer; one barrier per chunk.
+  uint4 st0[kStage], st1[kStage];
+  fetch(st0, 0);
+  Frag<WT> ring[kTileNB][kTileRt][kKB];
+#pragma unroll
+  for (int u = 0; u < kTileNB; ++u)
+    if (u < nchunks)
+#pragma unroll
+      for (int rt = 0; rt < kTileRt; ++rt)
+#pragma unroll
+        for (int kk = 0; kk < kKB; ++kk) ring[u][rt][kk].load(wp[rt] + (u * kKB + kk) * kFrag);
+  if (nchunks > 1) fetch(st1, 1);
+  put(st0, lds[0]);
+  __syncthreads();
+
+  // kTileNB is a multiple of 2, so u and c share parity and the stage sets
+  // can be named statically
+  for (int c0 = 0; c0 < nchunks; c0 += kTileNB) {
+#pragma unroll
+    for (int u = 0; u < kTileNB; ++u) {
+      const int c = c0 + u;
+      if (c < nchunks) {
+        uint4 (&st_next)[kStage] = (u & 1) ? st0 : st1;   // holds chunk c+1
+        uint4 (&st_free)[kStage] = (u & 1) ? st1 : st0;   // held chunk c, now in LDS
+        if (c + 2 < nchunks) fetch(st_free, c + 2);
+        const unsigned char* buf = lds[c & 1];
+#pragma unroll
+        for (int kk = 0; kk < kKB; ++kk) {
+          Frag<WT> b[kTileNT];
+#pragma unroll
+          for (int j = 0; j < kTileNT; ++j)
+            b[j].load(reinterpret_cast<const WT*>(buf + (j * 16 + r16) * C::kRowBytes) + kk * 32 + q * 8);
+#pragma unroll
+          for (int j = 0; j < kTileNT; ++j)
+#pragma unroll
+            for (int rt = 0; rt < kTileRt; ++rt) acc[rt][j] = mma(ring[u][rt][kk], b[j], acc[rt][j]);
+        }
+        if (c + kTileNB < nchunks) {
+#pragma unroll
+          for (int rt = 0; rt < kTileRt; ++rt)
+#pragma unroll
+            for (int kk = 0; kk < kKB; ++kk)
+              ring[u][rt][kk].load(wp[rt] + ((c + kTileNB) * kKB + kk) * kFrag);
+        }
+        if (c + 1 < nchunks) put(st_next, lds[(c + 1) & 1]);
+        __syncthreads();
+      }
+    }
+  }
+
+  // epilogue: lane (r16, q) holds rows rowbase[rt] + 4q + v of token column j*16 + r16
+  if (MODE == kGateUp) {
+    WT* act = static_cast<WT*>(a.out);
+#pragma unroll
+    for (int j = 0; j < kTileNT; ++j) {
+      const int m = j * 16 + r16;
+      if (m < mp) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 gv = acc[h][j], uv = acc[2 + h][j];
+          f32x4 o;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] = gv[v] / (1.0f + expf(-gv[v])) * uv[v];
+          store4<WT>(act + static_cast<long long>(off + m0 + m) * a.N + rowbase[h] + 4 * q, o);
+        }
+      }
+    }
+  } else {
+    float* y = static_cast<float*>(a.out);
+#pragma unroll
+    for (int j = 0; j < kTileNT; ++j) {
+      const int m = j * 16 + r16;
+      if (m < mp) {
+        const int p = clampi(a.sorted_src[off + m0 + m], 0, a.P - 1);
+        const int t = p / a.S;
+        const int slot = p - t * a.S;
+        const float wgt = slot < a.k ? a.topk_w[static_cast<long long>(t) * a.k + slot] : 1.0f;
+#pragma unroll
+        for (int rt = 0; rt < kTileRt; ++rt) {
+          f32x4 o = acc[rt][j];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] *= wgt;
+          store4<float>(y + static_cast<long long>(p) * a.N + rowbase[rt] + 4 * q, o);
+        }
+      }
+    }
+  }
+}
+
+// Upper bound of the tile count (groups are only known on the device): every
+// group contributes at most ceil(M_g / 128) <= M_g / 128 + 1 token tiles.
+int tile_grid(int T, int k, int ns, int E, int n_ctiles) {
+  const long long routed = (static_cast<long long>(T) * k + kTileTok - 1) / kTileTok + E;
+  const long long shared = static_cast<long long>(ns) * ((T + kTileTok - 1) / kTileTok);
+  long long n = (routed + shared) * n_ctiles;
+  n = (n + kXcds - 1) / kXcds * kXcds;
+  return static_cast<int>(n);
+}
+
+template <typename WT, int MODE>
+void launch_tile(const GemmArgs& args, int n_ctiles, int G, int E, int k, int ns, hipStream_t s) {
+  const int grid = tile_grid(args.T, k, ns, E, n_ctiles);
+  tile_gemm<WT, MODE><<<grid, kTileThreads, 0, s>>>(args, n_ctiles, G);
+}
+
 // Fragment packing of row-major weights: thread i writes the 8 elements of
 // packed position i = ((g * ntiles + tile) * nkb + kb) * 64 + lane, taken from
 // row tile*16 + lane % 16, columns kb*32 + 8*(lane / 16) .. +7 (zero past N).
@@ -435,30 +684,66 @@ __global__ __launch_bounds__(256) void pack_kernel(const WT* __restrict__ src, W
   }
 }
 
-// Final RMSNorm of the head input, rounded to the operand type.
+// Final RMSNorm of the head input, rounded to the operand type: one block of
+// 256 threads per 4 tokens.  With y (the last layer's expert slots) the
+// residual add happens first, in the same slot order as the combine kernel,
+// every slot load of a thread issued before the sum.
+constexpr int kNormTPB = 4;
+constexpr int kNormMaxSlots = 16;
+
 template <typename WT>
 __global__ __launch_bounds__(256) void norm_cast_kernel(const float* __restrict__ h,
+                                                        const float* __restrict__ y, int S,
                                                         const WT* __restrict__ gamma, float eps,
                                                         int T, int H, WT* __restrict__ xo) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  extern __shared__ float hs[];   // [kNormTPB][H]
+  const int t0 = blockIdx.x * kNormTPB;
+  const int nt = min(kNormTPB, T - t0);
+  const int h4 = H / 4;
+  for (int f = threadIdx.x; f < nt * h4; f += 256) {
+    const int tt = f / h4;
+    const int i = (f - tt * h4) * 4;
+    const long long t = t0 + tt;
+    float4 v = *reinterpret_cast<const float4*>(h + t * H + i);
+    if (y != nullptr) {
+      const float4* ys = reinterpret_cast<const float4*>(y + t * S * H + i);
+      float4 sv[kNormMaxSlots];
+#pragma unroll
+      for (int sl = 0; sl < kNormMaxSlots; ++sl)
+        if (sl < S) sv[sl] = ys[static_cast<long long>(sl) * h4];
+      float4 acc = sv[0];
+#pragma unroll
+      for (int sl = 1; sl < kNormMaxSlots; ++sl)
+        if (sl < S) {
+          acc.x += sv[sl].x;
+          acc.y += sv[sl].y;
+          acc.z += sv[sl].z;
+          acc.w += sv[sl].w;
+        }
+      v = make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
+    }
+    *reinterpret_cast<float4*>(hs + tt * H + i) = v;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  const float* hr = h + static_cast<long long>(t) * H;
+  if (wave >= nt) return;
+  const float* hr = hs + wave * H;
   float ss = 0.f;
   for (int i = lane * 4; i < H; i += 256) {
-    float4 v = *reinterpret_cast<const float4*>(hr + i);
+    const float4 v = *reinterpret_cast<const float4*>(hr + i);
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
-  ss = wave_sum(ss);
+  ss = lane63(wave_sum_lane63(ss));
   const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
   for (int i = lane * 4; i < H; i += 256) {
-    float4 v = *reinterpret_cast<const float4*>(hr + i);
+    const float4 v = *reinterpret_cast<const float4*>(hr + i);
     f32x4 o;
     o[0] = v.x * r * (gamma ? to_f32<WT>(gamma[i + 0]) : 1.f);
     o[1] = v.y * r * (gamma ? to_f32<WT>(gamma[i + 1]) : 1.f);
     o[2] = v.z * r * (gamma ? to_f32<WT>(gamma[i + 2]) : 1.f);
     o[3] = v.w * r * (gamma ? to_f32<WT>(gamma[i + 3]) : 1.f);
-    store4<WT>(xo + static_cast<long long>(t) * H + i, o);
+    store4<WT>(xo + static_cast<long long>(t0 + wave) * H + i, o);
   }
 }
 
@@ -507,8 +792,8 @@ moev_status check_inter(int I) {
 }
 
 moev_status check_hid(int H) {
-  MOEV_REQUIRE(H >= 64 && H <= 3840 && H % 64 == 0, MOEV_ERR_UNSUPPORTED,
-               "hidden size %d must be a multiple of 64 in [64, 3840]", H);
+  MOEV_REQUIRE(H >= 64 && H <= 3072 && H % 64 == 0, MOEV_ERR_UNSUPPORTED,
+               "hidden size %d must be a multiple of 64 in [64, 3072]", H);
   return MOEV_OK;
 }
 
@@ -548,6 +833,12 @@ void launch_ffn_gate_up(const void* x, const int32_t* sorted_src, const int32_t*
   up.K = H;
   up.x = x;
   up.out = act;
+  if (T > kTileMinTokens && I % tile_cols<kGateUp>() == 0) {
+    const int nct = I / tile_cols<kGateUp>();
+    if (dt == MOEV_BF16) launch_tile<u16, kGateUp>(up, nct, E + ns, E, k, ns, s);
+    else launch_tile<float, kGateUp>(up, nct, E + ns, E, k, ns, s);
+    return;
+  }
   const dim3 grid(I / (16 * kWavesFfn), E + ns);
   if (dt == MOEV_BF16)
     launch_gemm<u16, kGateUp, 2, kWavesFfn>(up, grid, s);
@@ -566,6 +857,12 @@ void launch_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* 
   dn.x = act;
   dn.topk_w = topk_w;
   dn.out = y_slots;
+  if (T > kTileMinTokens && H % tile_cols<kDown>() == 0) {
+    const int nct = H / tile_cols<kDown>();
+    if (dt == MOEV_BF16) launch_tile<u16, kDown>(dn, nct, E + ns, E, k, ns, s);
+    else launch_tile<float, kDown>(dn, nct, E + ns, E, k, ns, s);
+    return;
+  }
   const dim3 grid(H / (16 * kRtDown * kWavesFfn), E + ns);
   if (dt == MOEV_BF16)
     launch_gemm<u16, kDown, kRtDown, kWavesFfn>(dn, grid, s);
@@ -583,7 +880,7 @@ void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t*
 
 void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,
                    int V, int dt, int32_t* argmax_out, float* max_out, float* logits_out,
-                   void* ws, hipStream_t s) {
+                   void* ws, hipStream_t s, const float* y_prev, int S_prev) {
   const size_t xf_bytes = align_up(static_cast<size_t>(T) * H * esize(dt), 256);
   const int nblk = head_blocks(V);
   const size_t part = align_up(static_cast<size_t>(nblk) * T * 4, 256);
@@ -601,14 +898,15 @@ void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_
   hd.out = pmax;
   hd.out_idx = pidx;
   hd.logits = logits_out;
-  const int nb = (T + 3) / 4;
+  const int nb = (T + kNormTPB - 1) / kNormTPB;
+  const size_t nlds = static_cast<size_t>(kNormTPB) * H * sizeof(float);
   if (dt == MOEV_BF16) {
-    norm_cast_kernel<u16><<<nb, 256, 0, s>>>(h, static_cast<const u16*>(norm_f), eps, T, H,
-                                              static_cast<u16*>(xf));
+    norm_cast_kernel<u16><<<nb, 256, nlds, s>>>(h, y_prev, S_prev, static_cast<const u16*>(norm_f), eps,
+                                              T, H, static_cast<u16*>(xf));
     launch_gemm<u16, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   } else {
-    norm_cast_kernel<float><<<nb, 256, 0, s>>>(h, static_cast<const float*>(norm_f), eps, T, H,
-                                                static_cast<float*>(xf));
+    norm_cast_kernel<float><<<nb, 256, nlds, s>>>(h, y_prev, S_prev, static_cast<const float*>(norm_f),
+                                                eps, T, H, static_cast<float*>(xf));
     launch_gemm<float, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   }
   argmax_reduce_kernel<<<T, 64, 0, s>>>(pmax, pidx, nblk, T, argmax_out, max_out);

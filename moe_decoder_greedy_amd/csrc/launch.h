@@ -11,6 +11,12 @@ void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, i
 void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,
                   const float* bias, int T, int H, int E, int k, int dt, void* x_out,
                   int32_t* topk_idx, float* topk_w, float* logits_out, hipStream_t s);
+// Router with the previous layer's combine folded in (y_prev != NULL: h_out =
+// h + the sum of y_prev's S_prev slots, in slot order); h_out may equal h.
+void launch_route_fused(const float* h, const float* y_prev, int S_prev, float* h_out,
+                        const void* norm_w, float eps, const void* w_router, const float* bias,
+                        int T, int H, int E, int k, int dt, void* x_out, int32_t* topk_idx,
+                        float* topk_w, hipStream_t s);
 void launch_permute(const int32_t* topk_idx, int T, int k, int E, int ns, int32_t* offsets,
                     int32_t* sorted_src, hipStream_t s);
 void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,
@@ -25,9 +31,10 @@ void launch_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* 
                      int ns, int dt, float* y_slots, hipStream_t s);
 void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
                     hipStream_t s);
+// y_prev (optional): the last layer's expert slots, added to h before the norm.
 void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,
                    int V, int dt, int32_t* argmax_out, float* max_out, float* logits_out,
-                   void* ws, hipStream_t s);
+                   void* ws, hipStream_t s, const float* y_prev = nullptr, int S_prev = 0);
 void launch_verify(const int32_t* tokens, const int32_t* greedy, int B, int K, int32_t* n_accept,
                    int32_t* commit, int32_t* commit_len, int32_t* next_last, hipStream_t s);
 

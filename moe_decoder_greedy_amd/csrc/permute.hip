@@ -1,104 +1,16 @@
-// Expert sort of the (token, slot) pairs: histogram -> exclusive prefix sum
-// -> stable scatter, in one workgroup of 1024 threads with the bookkeeping in
-// LDS.  Only the T*k routed pairs need sorting; each shared expert holds every
-// token in order, so its segment is written directly.
-//
-// Stable scatter of one 1024-pair chunk (pairs in increasing id order):
-//   * within a wavefront, lanes with the same expert find each other with
-//     ballots over the expert-id bits; a lane's rank is the number of
-//     matching lower lanes;
-//   * the per-wave counts go to an LDS table [16 waves][64 experts]; one
-//     thread per expert turns its column into running bases (in wave order)
-//     and advances the expert's cursor;
-//   * position = cursor base for (wave, expert) + rank.
-// Integer work only, so the result is exact and identical on every run.
+// Expert sort of the (token, slot) pairs as its own kernel (one workgroup);
+// the algorithm is in permute_body.h.
 #include "launch.h"
+#include "permute_body.h"
 
 namespace moev {
 namespace {
-
-constexpr int kPermThreads = 1024;
-constexpr int kPermWaves = kPermThreads / kWave;
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ idx,
                                                                int T, int k, int E, int ns,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_src) {
-  __shared__ int cnt[64];
-  __shared__ int base[64];
-  __shared__ int wcnt[kPermWaves][64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int S = k + ns;
-  const int n_routed_pairs = T * k;
-
-  if (tid < 64) cnt[tid] = 0;
-  __syncthreads();
-  for (int q = tid; q < n_routed_pairs; q += kPermThreads) {
-    int g = idx[q];
-    g = g < 0 ? 0 : (g >= E ? E - 1 : g);
-    atomicAdd(&cnt[g], 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int g = 0; g < E; ++g) {
-      base[g] = run;
-      offsets[g] = run;
-      run += cnt[g];
-    }
-    for (int s = 0; s <= ns; ++s) offsets[E + s] = run + s * T;
-  }
-  __syncthreads();
-
-  const unsigned long long lower = (1ull << lane) - 1ull;
-  for (int c0 = 0; c0 < n_routed_pairs; c0 += kPermThreads) {
-    const int q = c0 + tid;
-    const bool valid = q < n_routed_pairs;
-    int g = 127;  // sentinel: never equal to a real expert id
-    if (valid) {
-      g = idx[q];
-      g = g < 0 ? 0 : (g >= E ? E - 1 : g);
-    }
-    unsigned long long match = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 7; ++b) {
-      const bool bit = (g >> b) & 1;
-      const unsigned long long bal = __ballot(bit);
-      match &= bit ? bal : ~bal;
-    }
-    const int rank = __popcll(match & lower);
-    const int wave_count = __popcll(match);
-
-    wcnt[wave][lane] = 0;
-    __syncthreads();
-    if (valid && rank == 0) wcnt[wave][g] = wave_count;
-    __syncthreads();
-    if (tid < E) {
-      int run = base[tid];
-      for (int w = 0; w < kPermWaves; ++w) {
-        const int c = wcnt[w][tid];
-        wcnt[w][tid] = run;
-        run += c;
-      }
-      base[tid] = run;
-    }
-    __syncthreads();
-    if (valid) {
-      const int t = q / k;
-      const int r = q - t * k;
-      sorted_src[wcnt[wave][g] + rank] = t * S + r;
-    }
-    __syncthreads();
-  }
-
-  const int shared_base = n_routed_pairs;
-  for (int i = tid; i < T * ns; i += kPermThreads) {
-    const int s = i / T;
-    const int t = i - s * T;
-    sorted_src[shared_base + i] = t * S + k + s;
-  }
+  permute_block([idx](int q) { return idx[q]; }, T, k, E, ns, offsets, sorted_src);
 }
 
 }  // namespace

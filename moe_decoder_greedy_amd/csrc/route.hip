@@ -31,6 +31,7 @@ namespace {
 constexpr int kRouteTPB = 4;         // tokens per block
 constexpr int kRouteThreads = 1024;   // 16 wavefronts
 constexpr int kExpertsPerWave = 4;    // 16 waves x 4 = 64 experts
+constexpr int kMaxSlots = 16;         // k + ns limit of the fused combine
 
 template <typename WT> struct Vec4;
 template <> struct Vec4<u16> {
@@ -64,15 +65,34 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     *reinterpret_cast<float4*>(dst + i) = Vec4<WT>::load(src + i);
 }
 
+struct RouteArgs {
+  const float* h;        // residual stream in [T, H]
+  const float* y;        // previous layer's expert slots [T, S, H] or NULL
+  int S;                 // slots per token of y
+  float* h_out;          // h + sum_s y[:, s] (written when y != NULL; may equal h)
+  const void* norm_w;
+  float eps;
+  const void* wr;
+  const float* bias;
+  int T, H, E, k;
+  void* x_out;
+  int32_t* topk_idx;
+  float* topk_w;
+  float* logits_out;
+};
+
 // NCH = ceil(H / 256): 4-element chunks per lane per row, a compile-time count
 // so that every router-row load of a wave is in flight at once.
-template <typename WT, int NCH>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const float* __restrict__ h, const WT* __restrict__ norm_w, float eps,
-    const WT* __restrict__ wr, const float* __restrict__ bias, int T, int H, int E, int k,
-    WT* __restrict__ x_out, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ logits_out) {
+// COMBINE: phase 0 first adds the previous layer's expert slots to the
+// residual (the same left-to-right slot order as the combine kernel, so the
+// bits are identical) and writes the new residual.
+template <typename WT, int NCH, bool COMBINE>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   extern __shared__ float smem[];
+  const int H = a.H, E = a.E, k = a.k, T = a.T;
+  const WT* __restrict__ wr = static_cast<const WT*>(a.wr);
+  const WT* __restrict__ norm_w = static_cast<const WT*>(a.norm_w);
+  WT* __restrict__ x_out = static_cast<WT*>(a.x_out);
   float* xs = smem;                                             // [TPB][H]
   float* lg = smem + kRouteTPB * H;                             // [TPB][64]
   float* sel_v = lg + kRouteTPB * 64;                           // [TPB][64]
@@ -95,17 +115,51 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
   }
 
-  // phase 1: RMSNorm, wave w < TPB takes token t0 + w
+  // phase 0: all threads stage the block's residual rows into LDS (xs),
+  // adding the previous layer's expert slots first when COMBINE; every slot
+  // load of a thread is issued before the sum, which runs left to right in
+  // slot order exactly as the combine kernel does
+  {
+    const int nt0 = min(kRouteTPB, T - t0);
+    const int h4 = H / 4;
+    for (int f = threadIdx.x; f < nt0 * h4; f += kRouteThreads) {
+      const int tt = f / h4;
+      const int i = (f - tt * h4) * 4;
+      const size_t t = static_cast<size_t>(t0 + tt);
+      float4 v = *reinterpret_cast<const float4*>(a.h + t * H + i);
+      if (COMBINE) {
+        const float4* ys = reinterpret_cast<const float4*>(a.y + t * a.S * H + i);
+        float4 sv[kMaxSlots];
+#pragma unroll
+        for (int sl = 0; sl < kMaxSlots; ++sl)
+          if (sl < a.S) sv[sl] = ys[static_cast<size_t>(sl) * h4];
+        float4 acc = sv[0];
+#pragma unroll
+        for (int sl = 1; sl < kMaxSlots; ++sl)
+          if (sl < a.S) {
+            acc.x += sv[sl].x;
+            acc.y += sv[sl].y;
+            acc.z += sv[sl].z;
+            acc.w += sv[sl].w;
+          }
+        v = make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
+        *reinterpret_cast<float4*>(a.h_out + t * H + i) = v;
+      }
+      *reinterpret_cast<float4*>(xs + tt * H + i) = v;
+    }
+  }
+  __syncthreads();
+
+  // phase 1: RMSNorm in place in LDS, wave w < TPB takes token t0 + w
   if (wave < kRouteTPB) {
     const int t = t0 + wave;
     if (t < T) {
-      const float* hr = h + static_cast<size_t>(t) * H;
       float4 hv[NCH], gv[NCH];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int i = lane * 4 + c * 256;
         const bool in = i < H;
-        hv[c] = in ? *reinterpret_cast<const float4*>(hr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        hv[c] = in ? *reinterpret_cast<const float4*>(xs + wave * H + i) : make_float4(0.f, 0.f, 0.f, 0.f);
         gv[c] = (in && norm_w) ? Vec4<WT>::load(norm_w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
       }
       float ss = 0.f;
@@ -113,7 +167,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       for (int c = 0; c < NCH; ++c)
         ss += hv[c].x * hv[c].x + hv[c].y * hv[c].y + hv[c].z * hv[c].z + hv[c].w * hv[c].w;
       ss = lane63(wave_sum_lane63(ss));
-      const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
+      const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + a.eps);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int i = lane * 4 + c * 256;
@@ -153,7 +207,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     for (int u = 0; u < kExpertsPerWave; ++u) {
       const int e = e0 + u;
       if (e < E) {
-        const float b = bias ? bias[e] : 0.f;
+        const float b = a.bias ? a.bias[e] : 0.f;
 #pragma unroll
         for (int tt = 0; tt < kRouteTPB; ++tt) {
           const float s = wave_sum_lane63(acc[u][tt]);
@@ -173,7 +227,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     if (t < T) {
       const float* row = lg + wave * 64;
       const float v = lane < E ? row[lane] : -INFINITY;
-      if (logits_out != nullptr && lane < E) logits_out[static_cast<size_t>(t) * E + lane] = v;
+      if (a.logits_out != nullptr && lane < E) a.logits_out[static_cast<size_t>(t) * E + lane] = v;
       int rank = 0;
       for (int j = 0; j < E; ++j) rank += better(row[j], j, v, lane) ? 1 : 0;
       if (lane < E && rank < k) {
@@ -187,35 +241,42 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         const float top0 = sel_v[wave * 64];
         float sum = 0.f;
         for (int j = 0; j < k; ++j) sum += expf(sel_v[wave * 64 + j] - top0);
-        topk_idx[static_cast<size_t>(t) * k + lane] = sel_i[wave * 64 + lane];
-        topk_w[static_cast<size_t>(t) * k + lane] = expf(sel_v[wave * 64 + lane] - top0) / sum;
+        a.topk_idx[static_cast<size_t>(t) * k + lane] = sel_i[wave * 64 + lane];
+        a.topk_w[static_cast<size_t>(t) * k + lane] = expf(sel_v[wave * 64 + lane] - top0) / sum;
       }
     }
   }
+
 }
 
-template <typename WT>
-void launch_route_t(int nch, dim3 grid, size_t lds, hipStream_t s, const float* h, const WT* norm_w,
-                    float eps, const WT* wr, const float* bias, int T, int H, int E, int k,
-                    WT* x_out, int32_t* idx, float* w, float* logits) {
-#define MOEV_ROUTE_CASE(N)                                                                 \
-  case N:                                                                                  \
-    route_kernel<WT, N><<<grid, kRouteThreads, lds, s>>>(h, norm_w, eps, wr, bias, T, H, E, k, x_out, \
-                                               idx, w, logits);                            \
+template <typename WT, bool COMBINE>
+void launch_route_t(int nch, dim3 grid, size_t lds, hipStream_t s, const RouteArgs& a) {
+#define MOEV_ROUTE_CASE(N)                                                               \
+  case N:                                                                                \
+    route_kernel<WT, N, COMBINE><<<grid, kRouteThreads, lds, s>>>(a);                     \
     break;
   switch (nch) {
     MOEV_ROUTE_CASE(1) MOEV_ROUTE_CASE(2) MOEV_ROUTE_CASE(3) MOEV_ROUTE_CASE(4)
     MOEV_ROUTE_CASE(5) MOEV_ROUTE_CASE(6) MOEV_ROUTE_CASE(7) MOEV_ROUTE_CASE(8)
     MOEV_ROUTE_CASE(9) MOEV_ROUTE_CASE(10) MOEV_ROUTE_CASE(11) MOEV_ROUTE_CASE(12)
-    MOEV_ROUTE_CASE(13) MOEV_ROUTE_CASE(14) MOEV_ROUTE_CASE(15) MOEV_ROUTE_CASE(16)
-    default: break;  // H <= 3840 is validated, so nch <= 16
+    MOEV_ROUTE_CASE(13) MOEV_ROUTE_CASE(14) MOEV_ROUTE_CASE(15)
+    default: break;  // H <= 3072 is validated, so nch <= 15
   }
 #undef MOEV_ROUTE_CASE
 }
 
+template <typename WT>
+void launch_route_dispatch(const RouteArgs& a, hipStream_t s) {
+  const dim3 grid((a.T + kRouteTPB - 1) / kRouteTPB);
+  const size_t lds = (static_cast<size_t>(kRouteTPB) * a.H + 3 * kRouteTPB * 64) * sizeof(float);
+  const int nch = (a.H + 255) / 256;
+  if (a.y != nullptr) launch_route_t<WT, true>(nch, grid, lds, s, a);
+  else launch_route_t<WT, false>(nch, grid, lds, s, a);
+}
+
 moev_status check_hidden(int H) {
-  if (H < 64 || H > 3840 || H % 64 != 0) {
-    set_error("hidden size %d must be a multiple of 64 in [64, 3840]", H);
+  if (H < 64 || H > 3072 || H % 64 != 0) {
+    set_error("hidden size %d must be a multiple of 64 in [64, 3072]", H);
     return MOEV_ERR_UNSUPPORTED;
   }
   return MOEV_OK;
@@ -235,17 +296,46 @@ void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, i
 void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,
                   const float* bias, int T, int H, int E, int k, int dt, void* x_out,
                   int32_t* topk_idx, float* topk_w, float* logits_out, hipStream_t s) {
-  const dim3 grid((T + kRouteTPB - 1) / kRouteTPB);
-  const size_t lds = (static_cast<size_t>(kRouteTPB) * H + 3 * kRouteTPB * 64) * sizeof(float);
-  const int nch = (H + 255) / 256;
-  if (dt == MOEV_BF16)
-    launch_route_t<u16>(nch, grid, lds, s, h, static_cast<const u16*>(norm_w), eps,
-                        static_cast<const u16*>(w_router), bias, T, H, E, k,
-                        static_cast<u16*>(x_out), topk_idx, topk_w, logits_out);
-  else
-    launch_route_t<float>(nch, grid, lds, s, h, static_cast<const float*>(norm_w), eps,
-                          static_cast<const float*>(w_router), bias, T, H, E, k,
-                          static_cast<float*>(x_out), topk_idx, topk_w, logits_out);
+  RouteArgs a{};
+  a.h = h;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.wr = w_router;
+  a.bias = bias;
+  a.T = T;
+  a.H = H;
+  a.E = E;
+  a.k = k;
+  a.x_out = x_out;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.logits_out = logits_out;
+  if (dt == MOEV_BF16) launch_route_dispatch<u16>(a, s);
+  else launch_route_dispatch<float>(a, s);
+}
+
+void launch_route_fused(const float* h, const float* y_prev, int S_prev, float* h_out,
+                        const void* norm_w, float eps, const void* w_router, const float* bias,
+                        int T, int H, int E, int k, int dt, void* x_out, int32_t* topk_idx,
+                        float* topk_w, hipStream_t s) {
+  RouteArgs a{};
+  a.h = h;
+  a.y = y_prev;
+  a.S = S_prev;
+  a.h_out = h_out;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.wr = w_router;
+  a.bias = bias;
+  a.T = T;
+  a.H = H;
+  a.E = E;
+  a.k = k;
+  a.x_out = x_out;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  if (dt == MOEV_BF16) launch_route_dispatch<u16>(a, s);
+  else launch_route_dispatch<float>(a, s);
 }
 
 moev_status validate_route(const float* h, const void* norm_w, const void* w_router,

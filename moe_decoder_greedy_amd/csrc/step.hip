@@ -48,8 +48,8 @@ moev_status validate_model(const moev_model* m, int B, int K) {
   MOEV_CHECK(check_dtype(m->dtype), MOEV_ERR_UNSUPPORTED);
   MOEV_REQUIRE(B >= 0 && K >= 0, MOEV_ERR_INVALID_ARG, "need B >= 0 and K >= 0 (B=%d K=%d)", B, K);
   MOEV_REQUIRE(K <= 64, MOEV_ERR_UNSUPPORTED, "K=%d drafts exceeds 64", K);
-  MOEV_REQUIRE(m->hidden >= 64 && m->hidden <= 3840 && m->hidden % 64 == 0, MOEV_ERR_UNSUPPORTED,
-               "hidden size %d must be a multiple of 64 in [64, 3840]", m->hidden);
+  MOEV_REQUIRE(m->hidden >= 64 && m->hidden <= 3072 && m->hidden % 64 == 0, MOEV_ERR_UNSUPPORTED,
+               "hidden size %d must be a multiple of 64 in [64, 3072]", m->hidden);
   MOEV_REQUIRE(m->inter >= 64 && m->inter <= 8192 && m->inter % 64 == 0, MOEV_ERR_UNSUPPORTED,
                "intermediate size %d must be a multiple of 64 in [64, 8192]", m->inter);
   MOEV_REQUIRE(m->n_routed >= 1 && m->n_routed <= 64, MOEV_ERR_UNSUPPORTED,
@@ -58,6 +58,8 @@ moev_status validate_model(const moev_model* m, int B, int K) {
                "top-k k=%d must be in [1, E=%d]", m->top_k, m->n_routed);
   MOEV_REQUIRE(m->n_shared >= 0 && m->n_shared <= 8, MOEV_ERR_UNSUPPORTED,
                "shared experts ns=%d must be in [0, 8]", m->n_shared);
+  MOEV_REQUIRE(m->top_k + m->n_shared <= 16, MOEV_ERR_UNSUPPORTED,
+               "the whole-step driver needs k + ns <= 16 (got %d)", m->top_k + m->n_shared);
   MOEV_REQUIRE(m->vocab >= 1, MOEV_ERR_INVALID_ARG, "vocabulary must be >= 1");
   MOEV_REQUIRE(m->n_layers >= 0, MOEV_ERR_INVALID_ARG, "n_layers must be >= 0");
   const long long T = static_cast<long long>(B) * (K + 1);
@@ -131,11 +133,17 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
     hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
   };
 
+  // Launches per layer: router (with the previous layer's combine folded in),
+  // permute, gate/up, down.  The last layer's combine happens inside the
+  // head's norm kernel.
+  const int S = k + ns;
   launch_embed(tokens, m->emb, T, H, m->vocab, dt, h, s);
   for (int l = 0; l < m->n_layers; ++l) {
     const moev_layer_weights& lw = m->layers[l];
+    const float* y_prev = l > 0 ? y : nullptr;
     mark(MOEV_STAGE_ROUTE, l, false);
-    launch_route(h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, dt, x, idx, w, nullptr, s);
+    launch_route_fused(h, y_prev, S, h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, dt, x,
+                       idx, w, s);
     mark(MOEV_STAGE_ROUTE, l, true);
     mark(MOEV_STAGE_PERMUTE, l, false);
     launch_permute(idx, T, k, E, ns, offsets, sorted, s);
@@ -146,13 +154,10 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
     mark(MOEV_STAGE_DOWN, l, false);
     launch_ffn_down(ffn_ws, sorted, offsets, w, lw.w_down, T, H, I, E, k, ns, dt, y, s);
     mark(MOEV_STAGE_DOWN, l, true);
-    mark(MOEV_STAGE_COMBINE, l, false);
-    launch_combine(y, h, T, H, k + ns, h, s);
-    mark(MOEV_STAGE_COMBINE, l, true);
   }
   mark(MOEV_STAGE_HEAD, 0, false);
   launch_lmhead(h, m->norm_f, m->eps, m->w_lm, T, H, m->vocab, dt, greedy, nullptr, nullptr,
-                head_ws, s);
+                head_ws, s, m->n_layers > 0 ? y : nullptr, S);
   mark(MOEV_STAGE_HEAD, 0, true);
   launch_verify(tokens, greedy, B, K, n_accept, commit, commit_len, next_last, s);
   return launch_status("moev_verify_step");

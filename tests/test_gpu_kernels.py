@@ -128,7 +128,7 @@ def _ffn_case(shape, L, dt, T, seed):
 
 
 @pytest.mark.parametrize("which,T", [("tiny", 16), ("tiny", 53), ("dec", 128), ("dec", 77), ("dec", 1),
-                                     ("dec", 300)])
+                                     ("dec", 300), ("dec", 600), ("tiny", 700)])
 def test_grouped_ffn(ops, tiny, dec_layer, zipf_layer, which, T):
     shape, L, dt = _layer(which, tiny, dec_layer, zipf_layer)
     report("grouped_ffn", which=which, T=T)

@@ -131,10 +131,10 @@ def test_batch_invariance(decoder_pair):
     w, dm = decoder_pair
     V = synth.DECODER.vocab
     rng = np.random.default_rng(8)
-    pool = rng.integers(0, V, size=512).astype(np.int32)
-    full = host(dm.greedy(dev_i32(pool)))
-    for T in (1, 4, 32, 128, 300):
-        sub = rng.choice(512, T, replace=False)
+    pool = rng.integers(0, V, size=1100).astype(np.int32)
+    full = host(dm.greedy(dev_i32(pool)))          # 1100 rows: the tiled GEMM schedule
+    for T in (1, 4, 32, 128, 300, 600):
+        sub = rng.choice(1100, T, replace=False)
         got = host(dm.greedy(dev_i32(pool[sub])))
         np.testing.assert_array_equal(got, full[sub])
     # inside a verify batch (positions 1..K are drafts) the same holds
@@ -158,3 +158,25 @@ def test_zipf_step_sampled(model_mod):
     got = host(out["greedy"])[:2].reshape(-1)
     report("zipf_step", flagged=int(flagged.sum()))
     np.testing.assert_array_equal(got[~flagged], ref["argmax"][~flagged])
+
+
+def test_step_matches_stage_chain(decoder_pair):
+    """The whole-step driver (router fused with the previous combine and the
+    permute, head norm fused with the last combine) gives the same greedy
+    tokens, bit for bit, as chaining the per-stage entry points."""
+    from moe_decoder_greedy_amd import ops
+    w, dm = decoder_pair
+    shape = dm.shape
+    B, K = 32, 3
+    toks = np.random.default_rng(13).integers(0, shape.vocab, size=(B, K + 1)).astype(np.int32)
+    td = dev_i32(toks)
+    fused = host(dm.verify_step(td)["greedy"]).reshape(-1)
+    h = ops.moe_embed(td.reshape(-1), dm.emb)
+    for L in dm.layers:
+        x, idx, wts, _ = ops.moe_route(h, L["norm"], shape.eps, L["w_router"], L["bias"], shape.top_k)
+        off, src = ops.moe_permute(idx, shape.n_routed, shape.n_shared)
+        y = ops.moe_grouped_ffn(x, src, off, wts, L["w_gate"], L["w_up"], L["w_down"], shape.n_routed,
+                                shape.top_k, shape.n_shared)
+        h = ops.moe_combine(y, h)
+    am, _, _ = ops.lmhead_argmax(h, dm.norm_f, shape.eps, dm.w_lm, vocab=shape.vocab)
+    np.testing.assert_array_equal(host(am), fused)
