@@ -97,6 +97,17 @@ struct GemmArgs {
   float* logits;            // head: optional logits [T, N]
 };
 
+// SwiGLU combination silu(g) * u = g / (1 + e^-g) * u from the hardware
+// base-2 exponential (v_exp_f32) and reciprocal (v_rcp_f32), each within
+// about one ulp; every GEMM schedule uses this one expression, so the
+// schedules agree bit for bit.  Large negative g: e^-g overflows to inf and
+// the product is -0; large positive g: e^-g underflows to 0 and the result
+// is g * u.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 template <typename WT> __device__ __forceinline__ void store4(WT* p, f32x4 v);
@@ -139,7 +150,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, unsigned char* __res
       if (m < mp) {
         f32x4 gv = acc[0][j], uv = acc[1][j], o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[v] = gv[v] / (1.0f + expf(-gv[v])) * uv[v];
+        for (int v = 0; v < 4; ++v) o[v] = silu_mul(gv[v], uv[v]);
         store4<WT>(act + static_cast<long long>(off + m0 + m) * a.N + n, o);
       }
     }
@@ -418,37 +429,102 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order:
+// register arrays indexed by the constant stay in registers.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Tile schedule for large groups (prefill-sized batches).
 //
-// One workgroup computes one (group, column tile, 128-token tile): 4
-// wavefronts x 4 weight tiles of 16 rows (gate/up: 2 gate + the same 2 up
-// tiles, i.e. 32 intermediate columns per wave, 128 per workgroup; down: 64
-// hidden rows per wave, 256 per workgroup) against 8 token tiles.  Weight
-// fragments come straight from the packed layout into a register ring; the
-// token rows go through a double-buffered LDS chunk (one barrier per 64-wide
-// K chunk), and the next chunk's rows are fetched into registers while the
-// current one is multiplied.  Tiles of one (group, column tile) are
-// consecutive in the tile order and the order is laid out so that consecutive
-// tiles land on the same XCD: the workgroups sharing a weight slab run side
-// by side and read it through one L2.
-// Accumulation is the same single fp32 chain over K blocks in order with the
-// same MFMA as the streaming schedule, so results are bitwise identical.
-constexpr int kTileTok = 128;                 // tokens per tile
-constexpr int kTileRt = 4;                    // 16-row weight tiles per wave
-constexpr int kTileNT = kTileTok / 16;        // token tiles per wave
-constexpr int kTileThreads = 256;
-constexpr int kTileNB = 4;                    // weight ring depth, in chunks (even)
+// One workgroup computes one (group, column tile, BT-token tile).  Its 256
+// weight rows (gate/up: 128 intermediate columns of gate and the same 128 of
+// up; down: 256 hidden rows) and its BT token rows are staged in LDS one
+// 32-wide K block at a time, both laid out as MFMA operand fragments (1 KB
+// per 16 rows x 32 K for bf16): lane l of a fragment read takes the 16 bytes
+// at l * 16, so operand reads are free of bank conflicts.  Weights are
+// already fragment-packed in HBM; token rows are gathered into that layout by
+// the load itself (lane (r, q) of a load fetches row r, elements 8q..8q+7 of
+// the block).  Loads go straight from global memory to LDS
+// (global_load_lds_dwordx4), kStages blocks deep, one barrier per block.
+// Each wave multiplies 128 weight rows (8 fragments) against 64 tokens (4
+// fragments): 32 MFMAs per block, 128 accumulator registers, so a SIMD holds
+// two waves and one wave's MFMAs cover the other's waits.  BT = 256: 8 waves
+// and one workgroup per CU; BT = 128: 4 waves, and two workgroups per CU
+// whose epilogues (the output stores) overlap each other's MFMAs.
+// Tiles of one (group, column tile) are consecutive in the tile order and
+// consecutive tiles land on the same XCD, so the workgroups sharing a weight
+// slab run side by side and read it through one L2.  Accumulation is the
+// same single fp32 chain over K blocks in order with the same MFMA as the
+// streaming schedule: results are bitwise identical.
+constexpr int kMaxGroups = 64 + 8;       // routed + shared experts
 constexpr int kXcds = 8;
 
 template <int MODE> constexpr int tile_cols() { return MODE == kGateUp ? 128 : 256; }
 
-template <typename WT, int MODE>
-__global__ __launch_bounds__(kTileThreads) void tile_gemm(GemmArgs a, int n_ctiles, int G) {
-  using C = Cfg<WT, kTileTok>;
-  constexpr int kVecs = kTileTok * C::kVecPerRow;             // 16-B vectors per chunk
-  constexpr int kStage = kVecs / kTileThreads;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileTok * C::kRowBytes];
-  __shared__ int tile_info[3];  // group, column tile, token tile (-1: no work)
+template <typename WT, int BT> struct TileCfg {
+  static_assert(BT == 128 || BT == 256, "token tile");
+  static constexpr int kWaves = 2 * BT / 64;                             // 2 x (BT / 64) grid
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kXFrags = BT / 16;                                // token fragments
+  static constexpr int kFrags = 16 + kXFrags;                            // per K block
+  static constexpr int kFragBytes = 512 * static_cast<int>(sizeof(WT));  // 16 x 32 operand block
+  static constexpr int kDma = kFragBytes / 1024;                         // 16-B loads per lane
+  static constexpr int kStageBytes = kFrags * kFragBytes;
+  static constexpr int kWPerWave = 16 / kWaves;                          // fragments each wave loads
+  static constexpr int kXPerWave = kXFrags / kWaves;
+  // LDS: 160 KB per CU.  bf16 with BT = 128 keeps two workgroups per CU.
+  static constexpr int kStages = sizeof(WT) == 4 ? 2 : (BT == 256 ? 4 : 3);
+  static constexpr int kPerCu = (BT == 128 && sizeof(WT) == 2) ? 2 : 1;
+  static_assert(kStages * kStageBytes * kPerCu <= 160 * 1024, "LDS budget");
+};
+
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+
+// Workgroup barrier for the LDS pipeline: wait until at most N of this
+// wave's vector-memory loads are outstanding (so its direct-to-LDS writes
+// older than those have landed) and all its LDS reads are done, then
+// s_barrier.  __syncthreads would also wait for the N newest loads, which
+// are the prefetches the pipeline wants in flight across the barrier.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+template <int N> __device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);  // lgkmcnt(0), expcnt off
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One LDS stage array per pipeline stage: separate objects let the compiler
+// see that reading one stage does not wait for loads into another.
+template <typename WT, int BT, int U> __device__ __forceinline__ unsigned char* tile_stage() {
+  constexpr int B = TileCfg<WT, BT>::kStageBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char s0[B];
+  __shared__ __attribute__((aligned(1024))) unsigned char s1[B];
+  __shared__ __attribute__((aligned(1024))) unsigned char s2[B];
+  __shared__ __attribute__((aligned(1024))) unsigned char s3[B];
+  static_assert(U >= 0 && U < 4, "at most four stages");
+  if constexpr (U == 0) return s0;
+  else if constexpr (U == 1) return s1;
+  else if constexpr (U == 2) return s2;
+  else return s3;
+}
+
+template <typename WT, int MODE, int BT>
+__global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPerCu)) void tile_gemm(
+    GemmArgs a, int n_ctiles, int G) {
+  using TC = TileCfg<WT, BT>;
+  constexpr int kNS = TC::kStages;
+  constexpr int kFB = TC::kFragBytes;
+  constexpr int kNWT = BT / 64;          // waves along tokens
+  __shared__ int tile_info[3];           // group, column tile, token tile (-1: no work)
+  __shared__ int group_tiles[kMaxGroups];
+  __shared__ int tile_total;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -456,28 +532,33 @@ __global__ __launch_bounds__(kTileThreads) void tile_gemm(GemmArgs a, int n_ctil
   const int r16 = lane & 15;
   const int q = lane >> 4;
 
+  // Tile counts per group (known on the device only): thread t counts group
+  // t's tiles, then the start of its range from the counts before it.
+  int mtiles = 0, run = 0;
+  if (tid < G) {
+    const int M = max(0, min(a.offsets[tid + 1], a.P) - max(min(a.offsets[tid], a.P), 0));
+    mtiles = (M + BT - 1) / BT;
+    group_tiles[tid] = mtiles * n_ctiles;
+  }
+  if (tid == 0) tile_info[0] = -1;
+  __syncthreads();
+  if (tid < G) {
+    for (int u = 0; u < tid; ++u) run += group_tiles[u];
+    if (tid == G - 1) tile_total = run + mtiles * n_ctiles;
+  }
+  __syncthreads();
   // XCD-aware tile index: hardware deals consecutive block ids round-robin
-  // over the XCDs, so tile = xcd * (grid / 8) + (bid / 8) keeps a run of
-  // consecutive tiles on one XCD.
-  const int nb = gridDim.x;
-  const int bid = blockIdx.x;
-  const int tile = (bid % kXcds) * (nb / kXcds) + bid / kXcds;
-  if (tid == 0) {
-    int run = 0, g = -1, ct = 0, mt = 0;
-    for (int gg = 0; gg < G && g < 0; ++gg) {
-      const int M = max(0, min(a.offsets[gg + 1], a.P) - max(min(a.offsets[gg], a.P), 0));
-      const int mtiles = (M + kTileTok - 1) / kTileTok;
-      const int n = mtiles * n_ctiles;
-      if (tile < run + n) {
-        g = gg;
-        ct = (tile - run) / mtiles;
-        mt = (tile - run) - ct * mtiles;
-      }
-      run += n;
-    }
-    tile_info[0] = g;
+  // over the XCDs, so with R = ceil(tiles / 8), tile = xcd * R + bid / 8
+  // gives each XCD an equal run of consecutive tiles (blocks past 8R idle).
+  const int total = tile_total;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int tile = slot < per_xcd ? (blockIdx.x % kXcds) * per_xcd + slot : total;
+  if (tid < G && tile >= run && tile < run + mtiles * n_ctiles) {
+    const int ct = (tile - run) / mtiles;
+    tile_info[0] = tid;
     tile_info[1] = ct;
-    tile_info[2] = mt;
+    tile_info[2] = (tile - run) - ct * mtiles;
   }
   __syncthreads();
   const int g = tile_info[0];
@@ -485,152 +566,143 @@ __global__ __launch_bounds__(kTileThreads) void tile_gemm(GemmArgs a, int n_ctil
   const int ct = tile_info[1];
   const int off = clampi(a.offsets[g], 0, a.P);
   const int M = clampi(a.offsets[g + 1], off, a.P) - off;
-  const int m0 = tile_info[2] * kTileTok;
-  const int mp = min(kTileTok, M - m0);
-
-  const WT* __restrict__ w0 = static_cast<const WT*>(a.w0);
-  const WT* __restrict__ w1 = static_cast<const WT*>(a.w1);
-  const WT* __restrict__ xsrc = static_cast<const WT*>(a.x);
+  const int m0 = tile_info[2] * BT;
+  const int mp = min(BT, M - m0);
   const int K = a.K;
   const int nkb = K / 32;
-  const int nchunks = K / kKC;
+  const int last = nkb - 1;
 
-  // this wave's weight tiles and their first output row
-  const WT* wp[kTileRt];
-  int rowbase[kTileRt];
-#pragma unroll
-  for (int rt = 0; rt < kTileRt; ++rt) {
-    int rb;
+  // 16-row weight tile of fragment f (0..15) of this workgroup
+  auto weight_tile = [&](int f) -> const WT* {
+    int t;
     const WT* base;
-    if (MODE == kGateUp) {  // tiles 0,1: gate columns c0, c0+16; tiles 2,3: up, same columns
-      rb = ct * tile_cols<MODE>() + wave * 32 + (rt & 1) * 16;
-      base = rt < 2 ? w0 : w1;
+    if (MODE == kGateUp) {  // f = 8 * half + 4 * (up ? 1 : 0) + i
+      t = ct * (tile_cols<MODE>() / 16) + (f >> 3) * 4 + (f & 3);
+      base = static_cast<const WT*>((f & 4) ? a.w1 : a.w0);
     } else {
-      rb = ct * tile_cols<MODE>() + wave * 64 + rt * 16;
-      base = w0;
+      t = ct * (tile_cols<MODE>() / 16) + f;
+      base = static_cast<const WT*>(a.w0);
     }
-    rowbase[rt] = rb;
-    wp[rt] = base + static_cast<long long>(g) * a.w_group + static_cast<long long>(rb / 16) * nkb * kFrag +
-             lane * 8;
-  }
-
-  // token rows of this thread's staging vectors (nullptr: zero-fill)
-  const WT* src[kStage];
-#pragma unroll
-  for (int s = 0; s < kStage; ++s) {
-    const int v = tid + s * kTileThreads;
-    const int row = v / C::kVecPerRow;
-    const int cv = v - row * C::kVecPerRow;
-    src[s] = row < mp ? xsrc + operand_row<MODE>(a, off, m0, row) * K + cv * C::kEpv : nullptr;
-  }
-  auto fetch = [&](uint4 (&st)[kStage], int c) {
-#pragma unroll
-    for (int s = 0; s < kStage; ++s)
-      st[s] = src[s] ? *reinterpret_cast<const uint4*>(src[s] + c * kKC) : make_uint4(0, 0, 0, 0);
-  };
-  auto put = [&](const uint4 (&st)[kStage], unsigned char* buf) {
-#pragma unroll
-    for (int s = 0; s < kStage; ++s) {
-      const int v = tid + s * kTileThreads;
-      const int row = v / C::kVecPerRow;
-      const int cv = v - row * C::kVecPerRow;
-      *reinterpret_cast<uint4*>(buf + row * C::kRowBytes + cv * 16) = st[s];
-    }
+    return base + static_cast<long long>(g) * a.w_group + static_cast<long long>(t) * nkb * 512;
   };
 
-  f32x4 acc[kTileRt][kTileNT];
+  // This wave loads weight fragments wave*kWPerWave .. and token fragments
+  // wave*kXPerWave .. of every block.  Token rows past the group's end
+  // repeat its last row: MFMA output columns depend on their own token row
+  // only, the epilogue drops those columns, and unconditional loads keep the
+  // wait counts exact.
+  const WT* wsrc[TC::kWPerWave];
+  const WT* xsrc[TC::kXPerWave];
 #pragma unroll
-  for (int rt = 0; rt < kTileRt; ++rt)
+  for (int i = 0; i < TC::kWPerWave; ++i) wsrc[i] = weight_tile(wave * TC::kWPerWave + i) + lane * 8;
 #pragma unroll
-    for (int j = 0; j < kTileNT; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Pipeline (loads complete in issue order, so every wait also covers the
-  // loads issued before it): in iteration c the token rows of chunk c+2 and
-  // the weights of chunk c+kTileNB are requested, and the rows of chunk c+1
-  // (requested an iteration earlier, ahead of the weights of chunk c+kTileNB-1)
-  // are written to the other LDS buffer; one barrier per chunk.
-  uint4 st0[kStage], st1[kStage];
-  fetch(st0, 0);
-  Frag<WT> ring[kTileNB][kTileRt][kKB];
-#pragma unroll
-  for (int u = 0; u < kTileNB; ++u)
-    if (u < nchunks)
-#pragma unroll
-      for (int rt = 0; rt < kTileRt; ++rt)
-#pragma unroll
-        for (int kk = 0; kk < kKB; ++kk) ring[u][rt][kk].load(wp[rt] + (u * kKB + kk) * kFrag);
-  if (nchunks > 1) fetch(st1, 1);
-  put(st0, lds[0]);
-  __syncthreads();
-
-  // kTileNB is a multiple of 2, so u and c share parity and the stage sets
-  // can be named statically
-  for (int c0 = 0; c0 < nchunks; c0 += kTileNB) {
-#pragma unroll
-    for (int u = 0; u < kTileNB; ++u) {
-      const int c = c0 + u;
-      if (c < nchunks) {
-        uint4 (&st_next)[kStage] = (u & 1) ? st0 : st1;   // holds chunk c+1
-        uint4 (&st_free)[kStage] = (u & 1) ? st1 : st0;   // held chunk c, now in LDS
-        if (c + 2 < nchunks) fetch(st_free, c + 2);
-        const unsigned char* buf = lds[c & 1];
-#pragma unroll
-        for (int kk = 0; kk < kKB; ++kk) {
-          Frag<WT> b[kTileNT];
-#pragma unroll
-          for (int j = 0; j < kTileNT; ++j)
-            b[j].load(reinterpret_cast<const WT*>(buf + (j * 16 + r16) * C::kRowBytes) + kk * 32 + q * 8);
-#pragma unroll
-          for (int j = 0; j < kTileNT; ++j)
-#pragma unroll
-            for (int rt = 0; rt < kTileRt; ++rt) acc[rt][j] = mma(ring[u][rt][kk], b[j], acc[rt][j]);
-        }
-        if (c + kTileNB < nchunks) {
-#pragma unroll
-          for (int rt = 0; rt < kTileRt; ++rt)
-#pragma unroll
-            for (int kk = 0; kk < kKB; ++kk)
-              ring[u][rt][kk].load(wp[rt] + ((c + kTileNB) * kKB + kk) * kFrag);
-        }
-        if (c + 1 < nchunks) put(st_next, lds[(c + 1) & 1]);
-        __syncthreads();
-      }
-    }
+  for (int i = 0; i < TC::kXPerWave; ++i) {
+    const int row = min((wave * TC::kXPerWave + i) * 16 + r16, mp - 1);
+    xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, off, m0, row) * K + q * 8;
   }
+  // K block kb into stage U: for each fragment, kDma loads of 16 B per lane
+  auto issue = [&](auto U, int kb) __attribute__((always_inline)) {
+    unsigned char* st = tile_stage<WT, BT, decltype(U)::value>();
+#pragma unroll
+    for (int h = 0; h < TC::kDma; ++h) {
+#pragma unroll
+      for (int i = 0; i < TC::kWPerWave; ++i)
+        __builtin_amdgcn_global_load_lds((gptr_t)(wsrc[i] + kb * 512 + h * (16 / sizeof(WT))),
+                                         (lptr_t)(st + (wave * TC::kWPerWave + i) * kFB + h * 1024), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < TC::kXPerWave; ++i)
+        __builtin_amdgcn_global_load_lds((gptr_t)(xsrc[i] + kb * 32 + h * (16 / sizeof(WT))),
+                                         (lptr_t)(st + (16 + wave * TC::kXPerWave + i) * kFB + h * 1024), 16,
+                                         0, 0);
+    }
+  };
+  constexpr int kLoads = (TC::kWPerWave + TC::kXPerWave) * TC::kDma;  // loads per lane per block
 
-  // epilogue: lane (r16, q) holds rows rowbase[rt] + 4q + v of token column j*16 + r16
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int wr = wave / kNWT;  // weight half
+  const int wt = wave % kNWT;  // token quarter (BT = 256) or half (BT = 128)
+  // fragment reads: lane l takes 16 B at l * 16 of each kDma half
+  auto frag = [&](const unsigned char* st, int f, Frag<WT>& out) __attribute__((always_inline)) {
+    if constexpr (sizeof(WT) == 2) {
+      out.v = *reinterpret_cast<const bf16x8*>(st + f * kFB + lane * 16);
+    } else {
+      out.lo = *reinterpret_cast<const f32x4*>(st + f * kFB + lane * 16);
+      out.hi = *reinterpret_cast<const f32x4*>(st + f * kFB + 1024 + lane * 16);
+    }
+  };
+
+  // prologue: blocks 0 .. kNS-2 (clamped: K may hold fewer blocks)
+  static_for<kNS - 1>([&](auto U) __attribute__((always_inline)) { issue(U, min(decltype(U)::value, last)); });
+  stage_barrier<(kNS - 2) * kLoads>();
+
+  // Block kb sits in stage kb % kNS.  Iteration kb requests block
+  // kb + kNS - 1 into the stage read in the previous iteration, multiplies
+  // block kb, then waits until block kb + 1 has landed (its loads and those
+  // of every other wave: the barrier).
+  auto iteration = [&](auto U, int kb) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    issue(std::integral_constant<int, (u + kNS - 1) % kNS>{}, min(kb + kNS - 1, last));
+    const unsigned char* st = tile_stage<WT, BT, u>();
+    Frag<WT> A[8], B[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) frag(st, 16 + wt * 4 + j, B[j]);
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) frag(st, wr * 8 + rt, A[rt]);
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[rt][j] = mma(A[rt], B[j], acc[rt][j]);
+    stage_barrier<(kNS - 2) * kLoads>();
+  };
+  int kb0 = 0;
+  for (; kb0 + kNS <= nkb; kb0 += kNS)
+    static_for<kNS>([&](auto U) __attribute__((always_inline)) { iteration(U, kb0 + decltype(U)::value); });
+  static_for<kNS>([&](auto U) __attribute__((always_inline)) {
+    if (kb0 + decltype(U)::value < nkb) iteration(U, kb0 + decltype(U)::value);
+  });
+  stage_barrier<0>();  // clamped tail loads
+
+  // epilogue: lane (r16, q) holds weight rows 4q + v of fragment wr*8 + rt
+  // for token column wt*64 + j*16 + r16
   if (MODE == kGateUp) {
     WT* act = static_cast<WT*>(a.out);
 #pragma unroll
-    for (int j = 0; j < kTileNT; ++j) {
-      const int m = j * 16 + r16;
+    for (int j = 0; j < 4; ++j) {
+      const int m = wt * 64 + j * 16 + r16;
       if (m < mp) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4 gv = acc[h][j], uv = acc[2 + h][j];
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 gv = acc[i][j], uv = acc[4 + i][j];
           f32x4 o;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] = gv[v] / (1.0f + expf(-gv[v])) * uv[v];
-          store4<WT>(act + static_cast<long long>(off + m0 + m) * a.N + rowbase[h] + 4 * q, o);
+          for (int v = 0; v < 4; ++v) o[v] = silu_mul(gv[v], uv[v]);
+          const int col = ct * tile_cols<MODE>() + wr * 64 + i * 16 + 4 * q;
+          store4<WT>(act + static_cast<long long>(off + m0 + m) * a.N + col, o);
         }
       }
     }
   } else {
     float* y = static_cast<float*>(a.out);
 #pragma unroll
-    for (int j = 0; j < kTileNT; ++j) {
-      const int m = j * 16 + r16;
+    for (int j = 0; j < 4; ++j) {
+      const int m = wt * 64 + j * 16 + r16;
       if (m < mp) {
         const int p = clampi(a.sorted_src[off + m0 + m], 0, a.P - 1);
         const int t = p / a.S;
         const int slot = p - t * a.S;
         const float wgt = slot < a.k ? a.topk_w[static_cast<long long>(t) * a.k + slot] : 1.0f;
 #pragma unroll
-        for (int rt = 0; rt < kTileRt; ++rt) {
+        for (int rt = 0; rt < 8; ++rt) {
           f32x4 o = acc[rt][j];
 #pragma unroll
           for (int v = 0; v < 4; ++v) o[v] *= wgt;
-          store4<float>(y + static_cast<long long>(p) * a.N + rowbase[rt] + 4 * q, o);
+          const int row = ct * tile_cols<MODE>() + (wr * 8 + rt) * 16 + 4 * q;
+          store4<float>(y + static_cast<long long>(p) * a.N + row, o);
         }
       }
     }
@@ -638,19 +710,26 @@ __global__ __launch_bounds__(kTileThreads) void tile_gemm(GemmArgs a, int n_ctil
 }
 
 // Upper bound of the tile count (groups are only known on the device): every
-// group contributes at most ceil(M_g / 128) <= M_g / 128 + 1 token tiles.
-int tile_grid(int T, int k, int ns, int E, int n_ctiles) {
-  const long long routed = (static_cast<long long>(T) * k + kTileTok - 1) / kTileTok + E;
-  const long long shared = static_cast<long long>(ns) * ((T + kTileTok - 1) / kTileTok);
+// group contributes at most ceil(M_g / BT) <= M_g / BT + 1 token tiles.
+int tile_grid(int T, int k, int ns, int E, int n_ctiles, int BT) {
+  const long long routed = (static_cast<long long>(T) * k + BT - 1) / BT + E;
+  const long long shared = static_cast<long long>(ns) * ((T + BT - 1) / BT);
   long long n = (routed + shared) * n_ctiles;
   n = (n + kXcds - 1) / kXcds * kXcds;
   return static_cast<int>(n);
 }
 
+// 256-token tiles once routed groups average 384 tokens or more (less
+// padding in ragged last tiles below that).
 template <typename WT, int MODE>
 void launch_tile(const GemmArgs& args, int n_ctiles, int G, int E, int k, int ns, hipStream_t s) {
-  const int grid = tile_grid(args.T, k, ns, E, n_ctiles);
-  tile_gemm<WT, MODE><<<grid, kTileThreads, 0, s>>>(args, n_ctiles, G);
+  if (static_cast<long long>(args.T) * k >= 384LL * E) {
+    const int grid = tile_grid(args.T, k, ns, E, n_ctiles, 256);
+    tile_gemm<WT, MODE, 256><<<grid, TileCfg<WT, 256>::kThreads, 0, s>>>(args, n_ctiles, G);
+  } else {
+    const int grid = tile_grid(args.T, k, ns, E, n_ctiles, 128);
+    tile_gemm<WT, MODE, 128><<<grid, TileCfg<WT, 128>::kThreads, 0, s>>>(args, n_ctiles, G);
+  }
 }
 
 // Fragment packing of row-major weights: thread i writes the 8 elements of
