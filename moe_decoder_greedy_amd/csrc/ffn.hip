@@ -88,6 +88,9 @@ struct GemmArgs {
   const void* x;            // operand rows
   const int32_t* offsets;   // [G+1] (gate/up, down)
   const int32_t* sorted_src;
+  const int32_t* counts;    // expert-list mode (streaming schedule only): group g
+                            // is sorted_src[g*T ..] with counts[g] pairs, act row g*T
+
   int S, k, P, T;           // slots, routed slots, pairs, tokens
   int n_first;              // the last n_first groups (the shared experts, which
                             // hold every token) are dispatched first
@@ -388,8 +391,13 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
   } else {
     const int G = gridDim.y;
     g = static_cast<int>(blockIdx.y) < a.n_first ? G - a.n_first + blockIdx.y : blockIdx.y - a.n_first;
-    off = clampi(a.offsets[g], 0, a.P);
-    M = clampi(a.offsets[g + 1], off, a.P) - off;
+    if (a.counts != nullptr) {
+      off = g * a.T;
+      M = clampi(a.counts[g], 0, a.T);
+    } else {
+      off = clampi(a.offsets[g], 0, a.P);
+      M = clampi(a.offsets[g + 1], off, a.P) - off;
+    }
   }
   if (M <= 0) return;
 
@@ -942,6 +950,44 @@ void launch_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* 
     else launch_tile<float, kDown>(dn, nct, E + ns, E, k, ns, s);
     return;
   }
+  const dim3 grid(H / (16 * kRtDown * kWavesFfn), E + ns);
+  if (dt == MOEV_BF16)
+    launch_gemm<u16, kDown, kRtDown, kWavesFfn>(dn, grid, s);
+  else
+    launch_gemm<float, kDown, kRtDown, kWavesFfn>(dn, grid, s);
+}
+
+void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t* counts,
+                              const void* w_gate, const void* w_up, int T, int H, int I, int E,
+                              int k, int ns, int dt, void* act, hipStream_t s) {
+  GemmArgs up = ffn_args(list, nullptr, T, H, I, k, ns);
+  up.counts = counts;
+  up.w0 = w_gate;
+  up.w1 = w_up;
+  up.w_group = static_cast<long long>(I) * H;
+  up.N = I;
+  up.K = H;
+  up.x = x;
+  up.out = act;
+  const dim3 grid(I / (16 * kWavesFfn), E + ns);
+  if (dt == MOEV_BF16)
+    launch_gemm<u16, kGateUp, 2, kWavesFfn>(up, grid, s);
+  else
+    launch_gemm<float, kGateUp, 2, kWavesFfn>(up, grid, s);
+}
+
+void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* counts,
+                           const float* topk_w, const void* w_down, int T, int H, int I, int E,
+                           int k, int ns, int dt, float* y_slots, hipStream_t s) {
+  GemmArgs dn = ffn_args(list, nullptr, T, H, I, k, ns);
+  dn.counts = counts;
+  dn.w0 = w_down;
+  dn.w_group = static_cast<long long>(H) * I;
+  dn.N = H;
+  dn.K = I;
+  dn.x = act;
+  dn.topk_w = topk_w;
+  dn.out = y_slots;
   const dim3 grid(H / (16 * kRtDown * kWavesFfn), E + ns);
   if (dt == MOEV_BF16)
     launch_gemm<u16, kDown, kRtDown, kWavesFfn>(dn, grid, s);

@@ -6,17 +6,34 @@
 
 namespace moev {
 
+// Expert lists (the whole-step driver's replacement for the sorted pair
+// order at decode sizes): group g's pairs are list[g*T .. g*T + counts[g]),
+// in any order (each token's expert output depends on its own row only).
+// Routed groups are filled by the router with one atomic per pair; shared
+// groups always hold every token in order.
+struct ExpertLists {
+  int32_t* counts;  // [n_sets][G]: one set per layer
+  int32_t* list;    // [G][T]
+  int n_sets, E, G, k, S;
+};
+constexpr int kListMaxTokens = 512;  // list mode only on the streaming GEMM schedule
+
+// lists != NULL: also resets every count set (routed 0, shared T) and writes
+// the shared groups' lists.
 void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, int dt, float* h,
-                  hipStream_t s);
+                  hipStream_t s, const ExpertLists* lists = nullptr);
 void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,
                   const float* bias, int T, int H, int E, int k, int dt, void* x_out,
                   int32_t* topk_idx, float* topk_w, float* logits_out, hipStream_t s);
 // Router with the previous layer's combine folded in (y_prev != NULL: h_out =
 // h + the sum of y_prev's S_prev slots, in slot order); h_out may equal h.
+// counts/list != NULL: each token's k pairs are also appended to the expert
+// lists (pair = t * S_pairs + slot).
 void launch_route_fused(const float* h, const float* y_prev, int S_prev, float* h_out,
                         const void* norm_w, float eps, const void* w_router, const float* bias,
                         int T, int H, int E, int k, int dt, void* x_out, int32_t* topk_idx,
-                        float* topk_w, hipStream_t s);
+                        float* topk_w, hipStream_t s, int32_t* counts = nullptr,
+                        int32_t* list = nullptr, int S_pairs = 0);
 void launch_permute(const int32_t* topk_idx, int T, int k, int E, int ns, int32_t* offsets,
                     int32_t* sorted_src, hipStream_t s);
 void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,
@@ -29,6 +46,13 @@ void launch_ffn_gate_up(const void* x, const int32_t* sorted_src, const int32_t*
 void launch_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* offsets,
                      const float* topk_w, const void* w_down, int T, int H, int I, int E, int k,
                      int ns, int dt, float* y_slots, hipStream_t s);
+// Expert GEMMs reading expert lists (T <= kListMaxTokens): act holds G*T rows.
+void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t* counts,
+                              const void* w_gate, const void* w_up, int T, int H, int I, int E,
+                              int k, int ns, int dt, void* act, hipStream_t s);
+void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* counts,
+                           const float* topk_w, const void* w_down, int T, int H, int I, int E,
+                           int k, int ns, int dt, float* y_slots, hipStream_t s);
 void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
                     hipStream_t s);
 // y_prev (optional): the last layer's expert slots, added to h before the norm.

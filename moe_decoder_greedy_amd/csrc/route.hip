@@ -7,15 +7,17 @@
 // softmax renormalised over the selected experts, i.e. exp(l_r - l_max) over
 // the sum of the k chosen exp(l_j - l_max).
 //
-// Layout of one block (1024 threads = 16 wavefronts, TPB = 4 tokens):
+// Layout of one block (1024 threads = 16 wavefronts, TPB = 1, 4 or 16
+// tokens: more blocks in flight for small batches, more tokens per fetch of
+// the router matrix for large ones):
 //   start    wave w fetches the router rows of experts 4w..4w+3 into
 //            registers (coalesced 8-byte bf16 loads, all in flight), so the
 //            weight fetch overlaps phase 1;
-//   phase 1  waves 0..3, one per token: sum of squares (per-lane strided
+//   phase 1  waves 0..TPB-1, one per token: sum of squares (per-lane strided
 //            partials, then a DPP reduction), x = h * rsqrt-scale * gamma into
 //            LDS (fp32) and to x_out (rounded to the operand type);
 //   phase 2  every wave multiplies its 4 router rows against the LDS copy of
-//            the block's tokens;
+//            the block's tokens, 4 tokens at a time;
 //   phase 3  one wave per token, one lane per expert: each lane's rank is
 //            the number of experts that beat it (read back from LDS), the
 //            k best file themselves by rank, then the renormalised softmax
@@ -28,7 +30,7 @@
 namespace moev {
 namespace {
 
-constexpr int kRouteTPB = 4;         // tokens per block
+constexpr int kRouteGroupMax = 4;    // tokens per logit pass
 constexpr int kRouteThreads = 1024;   // 16 wavefronts
 constexpr int kExpertsPerWave = 4;    // 16 waves x 4 = 64 experts
 constexpr int kMaxSlots = 16;         // k + ns limit of the fused combine
@@ -55,8 +57,18 @@ template <> struct Vec4<float> {
 template <typename WT>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
                                                     const WT* __restrict__ emb, int T, int H, int V,
-                                                    float* __restrict__ h) {
+                                                    float* __restrict__ h, ExpertLists lists) {
   const int t = blockIdx.x;
+  if (lists.list != nullptr) {
+    // block t writes token t's entry of every shared list; block 0 resets the
+    // count sets (routed 0, shared T)
+    const int ns = lists.G - lists.E;
+    if (threadIdx.x < ns)
+      lists.list[static_cast<size_t>(lists.E + threadIdx.x) * T + t] = t * lists.S + lists.k + threadIdx.x;
+    if (t == 0)
+      for (int i = threadIdx.x; i < lists.n_sets * lists.G; i += blockDim.x)
+        lists.counts[i] = (i % lists.G) < lists.E ? 0 : T;
+  }
   int tok = tokens[t];
   tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
   const WT* src = emb + static_cast<size_t>(tok) * H;
@@ -79,6 +91,9 @@ struct RouteArgs {
   int32_t* topk_idx;
   float* topk_w;
   float* logits_out;
+  int32_t* counts;       // expert lists (optional): per-group counts
+  int32_t* list;         //   and [G][T] pair lists
+  int S_pairs;           //   pair = t * S_pairs + slot
 };
 
 // NCH = ceil(H / 256): 4-element chunks per lane per row, a compile-time count
@@ -86,7 +101,7 @@ struct RouteArgs {
 // COMBINE: phase 0 first adds the previous layer's expert slots to the
 // residual (the same left-to-right slot order as the combine kernel, so the
 // bits are identical) and writes the new residual.
-template <typename WT, int NCH, bool COMBINE>
+template <typename WT, int NCH, bool COMBINE, int kRouteTPB>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   extern __shared__ float smem[];
   const int H = a.H, E = a.E, k = a.k, T = a.T;
@@ -122,7 +137,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   {
     const int nt0 = min(kRouteTPB, T - t0);
     const int h4 = H / 4;
-    for (int f = threadIdx.x; f < nt0 * h4; f += kRouteThreads) {
+    // H <= 256 * NCH, so kStageIt passes cover the block's rows; a fixed
+    // count lets every pass's loads be issued before the first is used
+    constexpr int kStageIt = (kRouteTPB * NCH * 64 + kRouteThreads - 1) / kRouteThreads;
+#pragma unroll
+    for (int it = 0; it < kStageIt; ++it) {
+      const int f = threadIdx.x + it * kRouteThreads;
+      if (f >= nt0 * h4) break;
       const int tt = f / h4;
       const int i = (f - tt * h4) * 4;
       const size_t t = static_cast<size_t>(t0 + tt);
@@ -182,36 +203,41 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  // phase 2: router logits of this wave's experts for the block's tokens
+  // phase 2: router logits of this wave's experts for the block's tokens,
+  // kRouteGroup tokens per pass (the same per-token arithmetic whatever TPB)
   const int nt = min(kRouteTPB, T - t0);
+  constexpr int kRouteGroup = kRouteTPB < kRouteGroupMax ? kRouteTPB : kRouteGroupMax;
   if (e0 < E) {
-    float acc[kExpertsPerWave][kRouteTPB];
 #pragma unroll
-    for (int u = 0; u < kExpertsPerWave; ++u)
+    for (int t1 = 0; t1 < kRouteTPB; t1 += kRouteGroup) {
+      float acc[kExpertsPerWave][kRouteGroup];
 #pragma unroll
-      for (int tt = 0; tt < kRouteTPB; ++tt) acc[u][tt] = 0.f;
+      for (int u = 0; u < kExpertsPerWave; ++u)
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int i = lane * 4 + c * 256;
-      if (i < H) {
+        for (int tt = 0; tt < kRouteGroup; ++tt) acc[u][tt] = 0.f;
 #pragma unroll
-        for (int tt = 0; tt < kRouteTPB; ++tt) {
-          const float4 x = *reinterpret_cast<const float4*>(xs + tt * H + i);
+      for (int c = 0; c < NCH; ++c) {
+        const int i = lane * 4 + c * 256;
+        if (i < H) {
 #pragma unroll
-          for (int u = 0; u < kExpertsPerWave; ++u)
-            acc[u][tt] += x.x * wv[u][c].x + x.y * wv[u][c].y + x.z * wv[u][c].z + x.w * wv[u][c].w;
+          for (int tt = 0; tt < kRouteGroup; ++tt) {
+            const float4 x = *reinterpret_cast<const float4*>(xs + (t1 + tt) * H + i);
+#pragma unroll
+            for (int u = 0; u < kExpertsPerWave; ++u)
+              acc[u][tt] += x.x * wv[u][c].x + x.y * wv[u][c].y + x.z * wv[u][c].z + x.w * wv[u][c].w;
+          }
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kExpertsPerWave; ++u) {
-      const int e = e0 + u;
-      if (e < E) {
-        const float b = a.bias ? a.bias[e] : 0.f;
+      for (int u = 0; u < kExpertsPerWave; ++u) {
+        const int e = e0 + u;
+        if (e < E) {
+          const float b = a.bias ? a.bias[e] : 0.f;
 #pragma unroll
-        for (int tt = 0; tt < kRouteTPB; ++tt) {
-          const float s = wave_sum_lane63(acc[u][tt]);
-          if (lane == 63 && tt < nt) lg[tt * 64 + e] = s + b;
+          for (int tt = 0; tt < kRouteGroup; ++tt) {
+            const float s = wave_sum_lane63(acc[u][tt]);
+            if (lane == 63 && t1 + tt < nt) lg[(t1 + tt) * 64 + e] = s + b;
+          }
         }
       }
     }
@@ -241,19 +267,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         const float top0 = sel_v[wave * 64];
         float sum = 0.f;
         for (int j = 0; j < k; ++j) sum += expf(sel_v[wave * 64 + j] - top0);
-        a.topk_idx[static_cast<size_t>(t) * k + lane] = sel_i[wave * 64 + lane];
+        const int e = sel_i[wave * 64 + lane];
+        a.topk_idx[static_cast<size_t>(t) * k + lane] = e;
         a.topk_w[static_cast<size_t>(t) * k + lane] = expf(sel_v[wave * 64 + lane] - top0) / sum;
+        if (a.list != nullptr) {
+          const int at = atomicAdd(a.counts + e, 1);
+          a.list[static_cast<size_t>(e) * T + at] = t * a.S_pairs + lane;
+        }
       }
     }
   }
 
 }
 
-template <typename WT, bool COMBINE>
+template <typename WT, bool COMBINE, int TPB>
 void launch_route_t(int nch, dim3 grid, size_t lds, hipStream_t s, const RouteArgs& a) {
 #define MOEV_ROUTE_CASE(N)                                                               \
   case N:                                                                                \
-    route_kernel<WT, N, COMBINE><<<grid, kRouteThreads, lds, s>>>(a);                     \
+    route_kernel<WT, N, COMBINE, TPB><<<grid, kRouteThreads, lds, s>>>(a);                \
     break;
   switch (nch) {
     MOEV_ROUTE_CASE(1) MOEV_ROUTE_CASE(2) MOEV_ROUTE_CASE(3) MOEV_ROUTE_CASE(4)
@@ -265,13 +296,23 @@ void launch_route_t(int nch, dim3 grid, size_t lds, hipStream_t s, const RouteAr
 #undef MOEV_ROUTE_CASE
 }
 
+template <typename WT, int TPB>
+void launch_route_tpb(const RouteArgs& a, hipStream_t s) {
+  const dim3 grid((a.T + TPB - 1) / TPB);
+  const size_t lds = (static_cast<size_t>(TPB) * a.H + 3 * TPB * 64) * sizeof(float);
+  const int nch = (a.H + 255) / 256;
+  if (a.y != nullptr) launch_route_t<WT, true, TPB>(nch, grid, lds, s, a);
+  else launch_route_t<WT, false, TPB>(nch, grid, lds, s, a);
+}
+
+// Tokens per block: 1 for decode-sized batches (more blocks in flight), 16
+// once there are enough tokens to fill the GPU that way (and their LDS copy
+// fits), else 4.
 template <typename WT>
 void launch_route_dispatch(const RouteArgs& a, hipStream_t s) {
-  const dim3 grid((a.T + kRouteTPB - 1) / kRouteTPB);
-  const size_t lds = (static_cast<size_t>(kRouteTPB) * a.H + 3 * kRouteTPB * 64) * sizeof(float);
-  const int nch = (a.H + 255) / 256;
-  if (a.y != nullptr) launch_route_t<WT, true>(nch, grid, lds, s, a);
-  else launch_route_t<WT, false>(nch, grid, lds, s, a);
+  if (a.T >= 2048 && a.H <= 2048) launch_route_tpb<WT, 16>(a, s);
+  else if (a.T > 256) launch_route_tpb<WT, 4>(a, s);
+  else launch_route_tpb<WT, 1>(a, s);
 }
 
 moev_status check_hidden(int H) {
@@ -286,11 +327,13 @@ moev_status check_hidden(int H) {
 
 // Launchers shared with the whole-step driver (no validation).
 void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, int dt, float* h,
-                  hipStream_t s) {
+                  hipStream_t s, const ExpertLists* lists) {
+  ExpertLists el{};
+  if (lists != nullptr) el = *lists;
   if (dt == MOEV_BF16)
-    embed_kernel<u16><<<T, 256, 0, s>>>(tokens, static_cast<const u16*>(emb), T, H, V, h);
+    embed_kernel<u16><<<T, 256, 0, s>>>(tokens, static_cast<const u16*>(emb), T, H, V, h, el);
   else
-    embed_kernel<float><<<T, 256, 0, s>>>(tokens, static_cast<const float*>(emb), T, H, V, h);
+    embed_kernel<float><<<T, 256, 0, s>>>(tokens, static_cast<const float*>(emb), T, H, V, h, el);
 }
 
 void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,
@@ -317,8 +360,12 @@ void launch_route(const float* h, const void* norm_w, float eps, const void* w_r
 void launch_route_fused(const float* h, const float* y_prev, int S_prev, float* h_out,
                         const void* norm_w, float eps, const void* w_router, const float* bias,
                         int T, int H, int E, int k, int dt, void* x_out, int32_t* topk_idx,
-                        float* topk_w, hipStream_t s) {
+                        float* topk_w, hipStream_t s, int32_t* counts, int32_t* list,
+                        int S_pairs) {
   RouteArgs a{};
+  a.counts = counts;
+  a.list = list;
+  a.S_pairs = S_pairs;
   a.h = h;
   a.y = y_prev;
   a.S = S_prev;

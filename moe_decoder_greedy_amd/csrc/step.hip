@@ -1,6 +1,6 @@
 // Whole FastMTP verify step on one stream: embedding gather, the decoder's
-// MoE layers (route -> permute -> grouped FFN -> combine), the greedy head and
-// the prefix-accept kernel.  All scratch lives in one caller-provided
+// MoE layers (route -> expert grouping -> grouped FFN -> combine), the greedy
+// head and the prefix-accept kernel.  All scratch lives in one caller-provided
 // workspace; nothing here allocates or synchronises, so a step can be
 // captured into a HIP graph and replayed.
 //
@@ -14,8 +14,12 @@ namespace moev {
 namespace {
 
 struct StepLayout {
-  size_t h, x, idx, w, offsets, sorted, y, ffn, head, total;
+  size_t h, x, idx, w, offsets, sorted, counts, y, ffn, head, total;
 };
+
+// Decode-sized steps route through expert lists filled by the router (no
+// permute launch); larger ones through the sorted pair order.
+bool use_lists(int T) { return T <= kListMaxTokens; }
 
 size_t esz(int dt) { return dt == MOEV_BF16 ? 2 : 4; }
 
@@ -34,10 +38,15 @@ StepLayout layout(const moev_model& m, int T) {
   L.x = take(static_cast<size_t>(T) * m.hidden * esz(m.dtype));
   L.idx = take(static_cast<size_t>(T) * m.top_k * 4);
   L.w = take(static_cast<size_t>(T) * m.top_k * 4);
+  const bool lists = use_lists(T);
   L.offsets = take(static_cast<size_t>(G + 1) * 4);
-  L.sorted = take(P * 4);
+  // sorted pair order [P], or the expert lists [G][T]
+  L.sorted = take((lists ? static_cast<size_t>(G) * T : P) * 4);
+  L.counts = take(lists ? static_cast<size_t>(m.n_layers > 0 ? m.n_layers : 1) * G * 4 : 0);
   L.y = take(P * m.hidden * 4);
-  L.ffn = take(grouped_ffn_ws_bytes(T, m.inter, m.top_k, m.n_shared, m.dtype));
+  // gate/up activations: [P, I] in sorted order, or [G*T, I] by expert list
+  L.ffn = take(lists ? static_cast<size_t>(G) * T * m.inter * esz(m.dtype)
+                     : grouped_ffn_ws_bytes(T, m.inter, m.top_k, m.n_shared, m.dtype));
   L.head = take(lmhead_ws_bytes(T, m.hidden, m.vocab, m.dtype));
   L.total = o;
   return L;
@@ -120,6 +129,7 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
   float* w = reinterpret_cast<float*>(base + L.w);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
   int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
   float* y = reinterpret_cast<float*>(base + L.y);
   void* ffn_ws = base + L.ffn;
   void* head_ws = base + L.head;
@@ -134,25 +144,37 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
   };
 
   // Launches per layer: router (with the previous layer's combine folded in),
-  // permute, gate/up, down.  The last layer's combine happens inside the
-  // head's norm kernel.
+  // permute (only without expert lists), gate/up, down.  The last layer's
+  // combine happens inside the head's norm kernel.  With expert lists the
+  // embedding kernel resets one count set per layer and the router appends
+  // each pair to its expert's list.
   const int S = k + ns;
-  launch_embed(tokens, m->emb, T, H, m->vocab, dt, h, s);
+  const int G = E + ns;
+  const bool lists = use_lists(T);
+  ExpertLists el{counts, sorted, m->n_layers, E, G, k, S};
+  launch_embed(tokens, m->emb, T, H, m->vocab, dt, h, s, lists && m->n_layers > 0 ? &el : nullptr);
   for (int l = 0; l < m->n_layers; ++l) {
     const moev_layer_weights& lw = m->layers[l];
     const float* y_prev = l > 0 ? y : nullptr;
+    int32_t* cnt = counts + static_cast<size_t>(l) * G;
     mark(MOEV_STAGE_ROUTE, l, false);
     launch_route_fused(h, y_prev, S, h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, dt, x,
-                       idx, w, s);
+                       idx, w, s, lists ? cnt : nullptr, lists ? sorted : nullptr, S);
     mark(MOEV_STAGE_ROUTE, l, true);
     mark(MOEV_STAGE_PERMUTE, l, false);
-    launch_permute(idx, T, k, E, ns, offsets, sorted, s);
+    if (!lists) launch_permute(idx, T, k, E, ns, offsets, sorted, s);
     mark(MOEV_STAGE_PERMUTE, l, true);
     mark(MOEV_STAGE_GATE_UP, l, false);
-    launch_ffn_gate_up(x, sorted, offsets, lw.w_gate, lw.w_up, T, H, I, E, k, ns, dt, ffn_ws, s);
+    if (lists)
+      launch_ffn_gate_up_lists(x, sorted, cnt, lw.w_gate, lw.w_up, T, H, I, E, k, ns, dt, ffn_ws, s);
+    else
+      launch_ffn_gate_up(x, sorted, offsets, lw.w_gate, lw.w_up, T, H, I, E, k, ns, dt, ffn_ws, s);
     mark(MOEV_STAGE_GATE_UP, l, true);
     mark(MOEV_STAGE_DOWN, l, false);
-    launch_ffn_down(ffn_ws, sorted, offsets, w, lw.w_down, T, H, I, E, k, ns, dt, y, s);
+    if (lists)
+      launch_ffn_down_lists(ffn_ws, sorted, cnt, w, lw.w_down, T, H, I, E, k, ns, dt, y, s);
+    else
+      launch_ffn_down(ffn_ws, sorted, offsets, w, lw.w_down, T, H, I, E, k, ns, dt, y, s);
     mark(MOEV_STAGE_DOWN, l, true);
   }
   mark(MOEV_STAGE_HEAD, 0, false);

@@ -66,7 +66,7 @@ def _layer(which, tiny, dec_layer, zipf_layer):
 # --------------------------------------------------------------------- route
 
 @pytest.mark.parametrize("which,T", [("tiny", 16), ("tiny", 37), ("dec", 128), ("dec", 1),
-                                     ("dec", 333), ("zipf", 130)])
+                                     ("dec", 333), ("zipf", 130), ("dec", 2061), ("tiny", 2050)])
 def test_route(ops, tiny, dec_layer, zipf_layer, which, T):
     shape, L, dt = _layer(which, tiny, dec_layer, zipf_layer)
     report("route", which=which, T=T)
@@ -102,7 +102,8 @@ def test_route(ops, tiny, dec_layer, zipf_layer, which, T):
 # ------------------------------------------------------------------- permute
 
 @pytest.mark.parametrize("T,E,k,ns", [(16, 8, 2, 1), (128, 64, 6, 2), (1, 64, 6, 2), (9760, 64, 6, 2),
-                                      (0, 64, 6, 2), (2000, 64, 6, 0), (37, 5, 5, 3), (1500, 3, 1, 8)])
+                                      (0, 64, 6, 2), (2000, 64, 6, 0), (37, 5, 5, 3), (1500, 3, 1, 8),
+                                      (3001, 64, 7, 1)])
 def test_permute(ops, T, E, k, ns):
     report("permute", T=T, E=E, k=k, ns=ns)
     rng = np.random.default_rng(T * 7 + E)
@@ -110,6 +111,19 @@ def test_permute(ops, T, E, k, ns):
     off_d, src_d = ops.moe_permute(dev_i32(idx) if T else torch.empty((0, k), dtype=torch.int32, device="cuda"),
                                    E, ns)
     torch.cuda.synchronize()
+    off, src = oracle.permute(idx, E, ns)
+    np.testing.assert_array_equal(host(off_d), off)
+    np.testing.assert_array_equal(host(src_d), src)
+
+
+def test_permute_skewed(ops):
+    """Most pairs on a few experts, spread over many 2048-pair chunks: every
+    chunk's per-expert starting points come from the counts before it."""
+    T, E, k, ns = 7000, 64, 6, 2
+    rng = np.random.default_rng(5)
+    p = 1.0 / np.arange(1, E + 1) ** 2.0
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+    off_d, src_d = ops.moe_permute(dev_i32(idx), E, ns)
     off, src = oracle.permute(idx, E, ns)
     np.testing.assert_array_equal(host(off_d), off)
     np.testing.assert_array_equal(host(src_d), src)
