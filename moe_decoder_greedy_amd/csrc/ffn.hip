@@ -96,7 +96,7 @@ struct GemmArgs {
                             // hold every token) are dispatched first
   const float* topk_w;      // [T, k] (down)
   void* out;                // gate/up: act [P, N] WT; down: y [P, N] fp32; head: pmax
-  int32_t* out_idx;         // head: partial arg max [blocks, T]
+  int32_t* out_idx;         // head: partial arg max [T, blocks]
   float* logits;            // head: optional logits [T, N]
 };
 
@@ -220,7 +220,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, unsigned char* __res
         const int oi = red_i[w * MT + tid];
         if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
       }
-      const long long o = static_cast<long long>(blockIdx.x) * a.T + m0 + tid;
+      const long long o = static_cast<long long>(m0 + tid) * gridDim.x + blockIdx.x;  // [T][blocks]
       static_cast<float*>(a.out)[o] = best;
       a.out_idx[o] = bi;
     }
@@ -472,7 +472,7 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
 constexpr int kMaxGroups = 64 + 8;       // routed + shared experts
 constexpr int kXcds = 8;
 
-template <int MODE> constexpr int tile_cols() { return MODE == kGateUp ? 128 : 256; }
+template <int MODE> constexpr int tile_cols() { return MODE == kGateUp ? 128 : 256; }  // output rows / 2 for gate/up
 
 template <typename WT, int BT> struct TileCfg {
   static_assert(BT == 128 || BT == 256, "token tile");
@@ -541,18 +541,24 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   const int q = lane >> 4;
 
   // Tile counts per group (known on the device only): thread t counts group
-  // t's tiles, then the start of its range from the counts before it.
+  // t's tiles, then the start of its range from the counts before it.  The
+  // LM head is one group of T tokens.
   int mtiles = 0, run = 0;
-  if (tid < G) {
+  if (MODE == kHead) {
+    if (tid == 0) {
+      mtiles = (a.T + BT - 1) / BT;
+      group_tiles[0] = mtiles * n_ctiles;
+    }
+  } else if (tid < G) {
     const int M = max(0, min(a.offsets[tid + 1], a.P) - max(min(a.offsets[tid], a.P), 0));
     mtiles = (M + BT - 1) / BT;
     group_tiles[tid] = mtiles * n_ctiles;
   }
   if (tid == 0) tile_info[0] = -1;
   __syncthreads();
-  if (tid < G) {
+  if (tid < (MODE == kHead ? 1 : G)) {
     for (int u = 0; u < tid; ++u) run += group_tiles[u];
-    if (tid == G - 1) tile_total = run + mtiles * n_ctiles;
+    if (tid == (MODE == kHead ? 0 : G - 1)) tile_total = run + mtiles * n_ctiles;
   }
   __syncthreads();
   // XCD-aware tile index: hardware deals consecutive block ids round-robin
@@ -562,7 +568,7 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int slot = blockIdx.x / kXcds;
   const int tile = slot < per_xcd ? (blockIdx.x % kXcds) * per_xcd + slot : total;
-  if (tid < G && tile >= run && tile < run + mtiles * n_ctiles) {
+  if (tid < (MODE == kHead ? 1 : G) && tile >= run && tile < run + mtiles * n_ctiles) {
     const int ct = (tile - run) / mtiles;
     tile_info[0] = tid;
     tile_info[1] = ct;
@@ -572,8 +578,8 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   const int g = tile_info[0];
   if (g < 0) return;
   const int ct = tile_info[1];
-  const int off = clampi(a.offsets[g], 0, a.P);
-  const int M = clampi(a.offsets[g + 1], off, a.P) - off;
+  const int off = MODE == kHead ? 0 : clampi(a.offsets[g], 0, a.P);
+  const int M = MODE == kHead ? a.T : clampi(a.offsets[g + 1], off, a.P) - off;
   const int m0 = tile_info[2] * BT;
   const int mp = min(BT, M - m0);
   const int K = a.K;
@@ -587,6 +593,9 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
     if (MODE == kGateUp) {  // f = 8 * half + 4 * (up ? 1 : 0) + i
       t = ct * (tile_cols<MODE>() / 16) + (f >> 3) * 4 + (f & 3);
       base = static_cast<const WT*>((f & 4) ? a.w1 : a.w0);
+    } else if (MODE == kHead) {  // the last column tile may run past the vocabulary
+      t = min(ct * (tile_cols<MODE>() / 16) + f, (a.N + 15) / 16 - 1);
+      base = static_cast<const WT*>(a.w0);
     } else {
       t = ct * (tile_cols<MODE>() / 16) + f;
       base = static_cast<const WT*>(a.w0);
@@ -694,6 +703,51 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
         }
       }
     }
+  } else if (MODE == kHead) {
+    // per token column: best (value, vocab index) over this wave's 128 rows,
+    // then over the two waves sharing the column (LDS), written as partial
+    // block ct of the arg max
+    float* red_v = reinterpret_cast<float*>(tile_stage<WT, BT, 0>());  // [2][BT]
+    int* red_i = reinterpret_cast<int*>(red_v + 2 * BT);                // [2][BT]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = wt * 64 + j * 16 + r16;
+      float best = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int n = ct * tile_cols<MODE>() + (wr * 8 + rt) * 16 + 4 * q + v;
+          if (n < a.N) {
+            const float val = acc[rt][j][v];
+            if (a.logits != nullptr && m < mp) a.logits[static_cast<long long>(m0 + m) * a.N + n] = val;
+            if (better(val, n, best, bi)) { best = val; bi = n; }
+          }
+        }
+#pragma unroll
+      for (int msk = 16; msk <= 32; msk <<= 1) {
+        const float ov = __shfl_xor(best, msk, kWave);
+        const int oi = __shfl_xor(bi, msk, kWave);
+        if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+      }
+      if (q == 0) {
+        red_v[wr * BT + m] = best;
+        red_i[wr * BT + m] = bi;
+      }
+    }
+    __syncthreads();
+    if (tid < mp) {
+      float best = red_v[tid];
+      int bi = red_i[tid];
+      if (better(red_v[BT + tid], red_i[BT + tid], best, bi)) {
+        best = red_v[BT + tid];
+        bi = red_i[BT + tid];
+      }
+      const long long o = static_cast<long long>(m0 + tid) * n_ctiles + ct;  // [T][blocks]
+      static_cast<float*>(a.out)[o] = best;
+      a.out_idx[o] = bi;
+    }
   } else {
     float* y = static_cast<float*>(a.out);
 #pragma unroll
@@ -740,6 +794,25 @@ void launch_tile(const GemmArgs& args, int n_ctiles, int G, int E, int k, int ns
   }
 }
 
+// LM head on the tile schedule: one group of T tokens, 256 vocabulary rows
+// per column tile, so the partial arg max blocks are the column tiles.
+#ifndef MOEV_HEAD_TILE_MIN_TOKENS
+#define MOEV_HEAD_TILE_MIN_TOKENS 64
+#endif
+constexpr int kHeadTileMinTokens = MOEV_HEAD_TILE_MIN_TOKENS;
+static_assert(tile_cols<kHead>() == 16 * kRtHead * kWavesHead, "head partial blocks");
+
+template <typename WT>
+void launch_tile_head(const GemmArgs& args, int n_ctiles, hipStream_t s) {
+  const int BT = args.T >= 512 ? 256 : 128;
+  long long n = static_cast<long long>(n_ctiles) * ((args.T + BT - 1) / BT);
+  n = (n + kXcds - 1) / kXcds * kXcds;
+  if (BT == 256)
+    tile_gemm<WT, kHead, 256><<<static_cast<int>(n), TileCfg<WT, 256>::kThreads, 0, s>>>(args, n_ctiles, 1);
+  else
+    tile_gemm<WT, kHead, 128><<<static_cast<int>(n), TileCfg<WT, 128>::kThreads, 0, s>>>(args, n_ctiles, 1);
+}
+
 // Fragment packing of row-major weights: thread i writes the 8 elements of
 // packed position i = ((g * ntiles + tile) * nkb + kb) * 64 + lane, taken from
 // row tile*16 + lane % 16, columns kb*32 + 8*(lane / 16) .. +7 (zero past N).
@@ -775,17 +848,16 @@ __global__ __launch_bounds__(256) void pack_kernel(const WT* __restrict__ src, W
 // 256 threads per 4 tokens.  With y (the last layer's expert slots) the
 // residual add happens first, in the same slot order as the combine kernel,
 // every slot load of a thread issued before the sum.
-constexpr int kNormTPB = 4;
 constexpr int kNormMaxSlots = 16;
 
-template <typename WT>
+template <typename WT, int TPB>
 __global__ __launch_bounds__(256) void norm_cast_kernel(const float* __restrict__ h,
                                                         const float* __restrict__ y, int S,
                                                         const WT* __restrict__ gamma, float eps,
                                                         int T, int H, WT* __restrict__ xo) {
-  extern __shared__ float hs[];   // [kNormTPB][H]
-  const int t0 = blockIdx.x * kNormTPB;
-  const int nt = min(kNormTPB, T - t0);
+  extern __shared__ float hs[];   // [TPB][H]
+  const int t0 = blockIdx.x * TPB;
+  const int nt = min(TPB, T - t0);
   const int h4 = H / 4;
   for (int f = threadIdx.x; f < nt * h4; f += 256) {
     const int tt = f / h4;
@@ -845,8 +917,8 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* __restri
   float best = -INFINITY;
   int bi = 0x7fffffff;
   for (int b = lane; b < nblk; b += 64) {
-    const float v = pmax[static_cast<long long>(b) * T + t];
-    const int i = pidx[static_cast<long long>(b) * T + t];
+    const float v = pmax[static_cast<long long>(t) * nblk + b];
+    const int i = pidx[static_cast<long long>(t) * nblk + b];
     if (better(v, i, best, bi)) { best = v; bi = i; }
   }
   wave_argmax(best, bi);
@@ -1023,15 +1095,28 @@ void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_
   hd.out = pmax;
   hd.out_idx = pidx;
   hd.logits = logits_out;
-  const int nb = (T + kNormTPB - 1) / kNormTPB;
-  const size_t nlds = static_cast<size_t>(kNormTPB) * H * sizeof(float);
+  // one token per block for decode-sized batches (more blocks in flight)
+  const int tpb = T <= 512 ? 1 : 4;
+  const int nb = (T + tpb - 1) / tpb;
+  const size_t nlds = static_cast<size_t>(tpb) * H * sizeof(float);
   if (dt == MOEV_BF16) {
-    norm_cast_kernel<u16><<<nb, 256, nlds, s>>>(h, y_prev, S_prev, static_cast<const u16*>(norm_f), eps,
-                                              T, H, static_cast<u16*>(xf));
-    launch_gemm<u16, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
+    if (tpb == 1)
+      norm_cast_kernel<u16, 1><<<nb, 256, nlds, s>>>(h, y_prev, S_prev, static_cast<const u16*>(norm_f),
+                                                    eps, T, H, static_cast<u16*>(xf));
+    else
+      norm_cast_kernel<u16, 4><<<nb, 256, nlds, s>>>(h, y_prev, S_prev, static_cast<const u16*>(norm_f),
+                                                    eps, T, H, static_cast<u16*>(xf));
+    if (T >= kHeadTileMinTokens) launch_tile_head<u16>(hd, nblk, s);
+    else launch_gemm<u16, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   } else {
-    norm_cast_kernel<float><<<nb, 256, nlds, s>>>(h, y_prev, S_prev, static_cast<const float*>(norm_f),
-                                                eps, T, H, static_cast<float*>(xf));
+    if (tpb == 1)
+      norm_cast_kernel<float, 1><<<nb, 256, nlds, s>>>(h, y_prev, S_prev,
+                                                      static_cast<const float*>(norm_f), eps, T, H,
+                                                      static_cast<float*>(xf));
+    else
+      norm_cast_kernel<float, 4><<<nb, 256, nlds, s>>>(h, y_prev, S_prev,
+                                                      static_cast<const float*>(norm_f), eps, T, H,
+                                                      static_cast<float*>(xf));
     launch_gemm<float, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   }
   argmax_reduce_kernel<<<T, 64, 0, s>>>(pmax, pidx, nblk, T, argmax_out, max_out);
