@@ -47,7 +47,10 @@ def log(*a):
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_verify_step_b32k3.json")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.json")
 
 
 def kernel_source_digest() -> str:
@@ -66,7 +69,7 @@ def stored_traffic(workload: str):
     (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a plain copy
     of known size), or None when that record is absent or stale."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(workload)) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -391,15 +394,23 @@ def run_layer(args, torch, np):
     lb = float(np.mean([layer_bytes(int(t), T, P, H, I, E) for t in touched]))
     lflops = 6.0 * P * H * I + 2.0 * T * E * H
     prefill = T > 1024
+    traffic = stored_traffic(wl.name)
     if prefill:
         ach = gu_flops / (dur["gate_up"] * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
     else:
         ach = gu_bytes / (dur["gate_up"] * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    roof.update({"kernel": "stream_gemm<bf16, gate/up> (moe_ffn_gate_up)", "avg_launch_us": round(dur["gate_up"], 2),
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+    # the schedule moe_ffn_gate_up takes at this size (tiles above 512 tokens,
+    # 256-token tiles once routed groups average 384 tokens)
+    if T > 512:
+        bt = 256 if T * k >= 384 * E else 128
+        kname = f"tile_gemm<bf16, gate/up, {bt}> (moe_ffn_gate_up)"
+    else:
+        kname = "stream_gemm<bf16, gate/up> (moe_ffn_gate_up)"
+    roof.update({"kernel": kname, "avg_launch_us": round(dur["gate_up"], 2),
                  "bytes_per_launch": int(gu_bytes), "flops_per_launch": gu_flops})
     return {
         "metric": "tokens/s through one MoE layer", "value": round(T / t_layer, 1), "unit": "tokens/s",
@@ -420,7 +431,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the verify step is data "
               "parallel with no cross-GPU exchange, so N GPUs are N independent copies of this "
-              "measurement; see the sharding notes in DESIGN.md", file=sys.stderr)
+              "measurement", file=sys.stderr)
         return 2
     import numpy as np
     import torch
