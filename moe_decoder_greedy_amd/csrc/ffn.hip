@@ -464,12 +464,16 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
 // two waves and one wave's MFMAs cover the other's waits.  BT = 256: 8 waves
 // and one workgroup per CU; BT = 128: 4 waves, and two workgroups per CU
 // whose epilogues (the output stores) overlap each other's MFMAs.
-// Tiles of one (group, column tile) are consecutive in the tile order and
-// consecutive tiles land on the same XCD, so the workgroups sharing a weight
-// slab run side by side and read it through one L2.  Accumulation is the
+// Consecutive tiles land on the same XCD and, within a group, cover a block
+// of token tiles x every column tile, so the workgroups sharing a weight slab
+// or a token tile run side by side and read it through one L2.  Accumulation is the
 // same single fp32 chain over K blocks in order with the same MFMA as the
 // streaming schedule: results are bitwise identical.
 constexpr int kMaxGroups = 64 + 8;       // routed + shared experts
+#ifndef MOEV_TILE_BLOCK
+#define MOEV_TILE_BLOCK 4
+#endif
+constexpr int kTileBlock = MOEV_TILE_BLOCK;  // token tiles per ordering block
 constexpr int kXcds = 8;
 
 template <int MODE> constexpr int tile_cols() { return MODE == kGateUp ? 128 : 256; }  // output rows / 2 for gate/up
@@ -530,8 +534,10 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   constexpr int kNS = TC::kStages;
   constexpr int kFB = TC::kFragBytes;
   constexpr int kNWT = BT / 64;          // waves along tokens
-  __shared__ int tile_info[3];           // group, column tile, token tile (-1: no work)
-  __shared__ int group_tiles[kMaxGroups];
+  __shared__ int group_start[kMaxGroups];  // first tile of each group
+  __shared__ int group_tiles[kMaxGroups];  // tiles of each group
+  __shared__ int group_mt[kMaxGroups];     // token tiles of each group
+  __shared__ int tile_info[2][3];          // (group, column tile, token tile), two tiles in flight
   __shared__ int tile_total;
 
   const int tid = threadIdx.x;
@@ -539,70 +545,66 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int q = lane >> 4;
+  const int ng = MODE == kHead ? 1 : G;
 
   // Tile counts per group (known on the device only): thread t counts group
   // t's tiles, then the start of its range from the counts before it.  The
   // LM head is one group of T tokens.
-  int mtiles = 0, run = 0;
-  if (MODE == kHead) {
-    if (tid == 0) {
-      mtiles = (a.T + BT - 1) / BT;
-      group_tiles[0] = mtiles * n_ctiles;
-    }
-  } else if (tid < G) {
-    const int M = max(0, min(a.offsets[tid + 1], a.P) - max(min(a.offsets[tid], a.P), 0));
-    mtiles = (M + BT - 1) / BT;
-    group_tiles[tid] = mtiles * n_ctiles;
+  if (tid < ng) {
+    int M = a.T;
+    if (MODE != kHead) M = max(0, min(a.offsets[tid + 1], a.P) - max(min(a.offsets[tid], a.P), 0));
+    const int mt = (M + BT - 1) / BT;
+    group_mt[tid] = mt;
+    group_tiles[tid] = mt * n_ctiles;
   }
-  if (tid == 0) tile_info[0] = -1;
   __syncthreads();
-  if (tid < (MODE == kHead ? 1 : G)) {
+  if (tid < ng) {
+    int run = 0;
     for (int u = 0; u < tid; ++u) run += group_tiles[u];
-    if (tid == (MODE == kHead ? 0 : G - 1)) tile_total = run + mtiles * n_ctiles;
+    group_start[tid] = run;
+    if (tid == ng - 1) tile_total = run + group_tiles[tid];
   }
   __syncthreads();
-  // XCD-aware tile index: hardware deals consecutive block ids round-robin
-  // over the XCDs, so with R = ceil(tiles / 8), tile = xcd * R + bid / 8
-  // gives each XCD an equal run of consecutive tiles (blocks past 8R idle).
+
+  // The workgroups are persistent: hardware deals consecutive block ids
+  // round-robin over the XCDs, so XCD x's workgroups walk the run of tiles
+  // [x R, (x+1) R), R = ceil(tiles / 8), at a stride of their count: the
+  // tiles an XCD works on at any moment are consecutive.  Within a group,
+  // tiles run in blocks of kTileBlock token tiles x every column tile
+  // (column-major inside the block): the ~32 tiles an XCD runs at once then
+  // share both their weight slabs and their token rows in its L2.
   const int total = tile_total;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int tile = slot < per_xcd ? (blockIdx.x % kXcds) * per_xcd + slot : total;
-  if (tid < (MODE == kHead ? 1 : G) && tile >= run && tile < run + mtiles * n_ctiles) {
-    const int ct = (tile - run) / mtiles;
-    tile_info[0] = tid;
-    tile_info[1] = ct;
-    tile_info[2] = (tile - run) - ct * mtiles;
-  }
-  __syncthreads();
-  const int g = tile_info[0];
-  if (g < 0) return;
-  const int ct = tile_info[1];
-  const int off = MODE == kHead ? 0 : clampi(a.offsets[g], 0, a.P);
-  const int M = MODE == kHead ? a.T : clampi(a.offsets[g + 1], off, a.P) - off;
-  const int m0 = tile_info[2] * BT;
-  const int mp = min(BT, M - m0);
+  const int stride = gridDim.x / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const int tile_end = min((xcd + 1) * per_xcd, total);
+  int tile = xcd * per_xcd + blockIdx.x / kXcds;
+  if (tile >= tile_end) return;
+
+  // tile -> tile_info[buf] (every thread calls it; a barrier must follow)
+  auto lookup = [&](int t, int buf) {
+    if (tid < ng) {
+      const int s0 = group_start[tid];
+      if (t >= s0 && t < s0 + group_tiles[tid]) {
+        const int r = t - s0;
+        const int mtiles = group_mt[tid];
+        const int mb0 = r / (kTileBlock * n_ctiles) * kTileBlock;
+        const int rows = min(kTileBlock, mtiles - mb0);
+        const int rr = r - mb0 * n_ctiles;
+        const int ct = rr / rows;
+        tile_info[buf][0] = tid;
+        tile_info[buf][1] = ct;
+        tile_info[buf][2] = mb0 + rr - ct * rows;
+      }
+    }
+  };
+
   const int K = a.K;
   const int nkb = K / 32;
   const int last = nkb - 1;
 
-  // 16-row weight tile of fragment f (0..15) of this workgroup
-  auto weight_tile = [&](int f) -> const WT* {
-    int t;
-    const WT* base;
-    if (MODE == kGateUp) {  // f = 8 * half + 4 * (up ? 1 : 0) + i
-      t = ct * (tile_cols<MODE>() / 16) + (f >> 3) * 4 + (f & 3);
-      base = static_cast<const WT*>((f & 4) ? a.w1 : a.w0);
-    } else if (MODE == kHead) {  // the last column tile may run past the vocabulary
-      t = min(ct * (tile_cols<MODE>() / 16) + f, (a.N + 15) / 16 - 1);
-      base = static_cast<const WT*>(a.w0);
-    } else {
-      t = ct * (tile_cols<MODE>() / 16) + f;
-      base = static_cast<const WT*>(a.w0);
-    }
-    return base + static_cast<long long>(g) * a.w_group + static_cast<long long>(t) * nkb * 512;
-  };
-
+  // the current tile: group, column tile, first token, token count, row base
+  int g = 0, ct = 0, m0 = 0, mp = 0, off = 0;
   // This wave loads weight fragments wave*kWPerWave .. and token fragments
   // wave*kXPerWave .. of every block.  Token rows past the group's end
   // repeat its last row: MFMA output columns depend on their own token row
@@ -610,13 +612,36 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   // wait counts exact.
   const WT* wsrc[TC::kWPerWave];
   const WT* xsrc[TC::kXPerWave];
+  auto setup = [&](int buf) {
+    g = tile_info[buf][0];
+    ct = tile_info[buf][1];
+    off = MODE == kHead ? 0 : clampi(a.offsets[g], 0, a.P);
+    const int M = MODE == kHead ? a.T : clampi(a.offsets[g + 1], off, a.P) - off;
+    m0 = tile_info[buf][2] * BT;
+    mp = min(BT, M - m0);
 #pragma unroll
-  for (int i = 0; i < TC::kWPerWave; ++i) wsrc[i] = weight_tile(wave * TC::kWPerWave + i) + lane * 8;
+    for (int i = 0; i < TC::kWPerWave; ++i) {
+      const int f = wave * TC::kWPerWave + i;  // 16-row weight tile f (0..15) of the tile
+      int t;
+      const WT* base;
+      if (MODE == kGateUp) {  // f = 8 * half + 4 * (up ? 1 : 0) + i
+        t = ct * (tile_cols<MODE>() / 16) + (f >> 3) * 4 + (f & 3);
+        base = static_cast<const WT*>((f & 4) ? a.w1 : a.w0);
+      } else if (MODE == kHead) {  // the last column tile may run past the vocabulary
+        t = min(ct * (tile_cols<MODE>() / 16) + f, (a.N + 15) / 16 - 1);
+        base = static_cast<const WT*>(a.w0);
+      } else {
+        t = ct * (tile_cols<MODE>() / 16) + f;
+        base = static_cast<const WT*>(a.w0);
+      }
+      wsrc[i] = base + static_cast<long long>(g) * a.w_group + static_cast<long long>(t) * nkb * 512 + lane * 8;
+    }
 #pragma unroll
-  for (int i = 0; i < TC::kXPerWave; ++i) {
-    const int row = min((wave * TC::kXPerWave + i) * 16 + r16, mp - 1);
-    xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, off, m0, row) * K + q * 8;
-  }
+    for (int i = 0; i < TC::kXPerWave; ++i) {
+      const int row = min((wave * TC::kXPerWave + i) * 16 + r16, mp - 1);
+      xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, off, m0, row) * K + q * 8;
+    }
+  };
   // K block kb into stage U: for each fragment, kDma loads of 16 B per lane
   auto issue = [&](auto U, int kb) __attribute__((always_inline)) {
     unsigned char* st = tile_stage<WT, BT, decltype(U)::value>();
@@ -634,12 +659,10 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
     }
   };
   constexpr int kLoads = (TC::kWPerWave + TC::kXPerWave) * TC::kDma;  // loads per lane per block
-
-  f32x4 acc[8][4];
-#pragma unroll
-  for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // blocks 0 .. kNS-2 of the tile set up last (clamped: K may hold fewer)
+  auto prologue = [&]() __attribute__((always_inline)) {
+    static_for<kNS - 1>([&](auto U) __attribute__((always_inline)) { issue(U, min(decltype(U)::value, last)); });
+  };
 
   const int wr = wave / kNWT;  // weight half
   const int wt = wave % kNWT;  // token quarter (BT = 256) or half (BT = 128)
@@ -653,10 +676,7 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
     }
   };
 
-  // prologue: blocks 0 .. kNS-2 (clamped: K may hold fewer blocks)
-  static_for<kNS - 1>([&](auto U) __attribute__((always_inline)) { issue(U, min(decltype(U)::value, last)); });
-  stage_barrier<(kNS - 2) * kLoads>();
-
+  f32x4 acc[8][4];
   // Block kb sits in stage kb % kNS.  Iteration kb requests block
   // kb + kNS - 1 into the stage read in the previous iteration, multiplies
   // block kb, then waits until block kb + 1 has landed (its loads and those
@@ -676,107 +696,155 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
       for (int j = 0; j < 4; ++j) acc[rt][j] = mma(A[rt], B[j], acc[rt][j]);
     stage_barrier<(kNS - 2) * kLoads>();
   };
-  int kb0 = 0;
-  for (; kb0 + kNS <= nkb; kb0 += kNS)
-    static_for<kNS>([&](auto U) __attribute__((always_inline)) { iteration(U, kb0 + decltype(U)::value); });
-  static_for<kNS>([&](auto U) __attribute__((always_inline)) {
-    if (kb0 + decltype(U)::value < nkb) iteration(U, kb0 + decltype(U)::value);
-  });
-  stage_barrier<0>();  // clamped tail loads
 
-  // epilogue: lane (r16, q) holds weight rows 4q + v of fragment wr*8 + rt
-  // for token column wt*64 + j*16 + r16
-  if (MODE == kGateUp) {
-    WT* act = static_cast<WT*>(a.out);
+  lookup(tile, 0);
+  __syncthreads();
+  int cur = 0;
+  setup(cur);
+  prologue();
+  for (;;) {
+    // Stage 0 of this tile has landed.  After an epilogue its stores are
+    // newer than the prologue's loads, so this waits for them too: correct,
+    // a little early.
+    stage_barrier<(kNS - 2) * kLoads>();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = wt * 64 + j * 16 + r16;
-      if (m < mp) {
+    for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 gv = acc[i][j], uv = acc[4 + i][j];
-          f32x4 o;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] = silu_mul(gv[v], uv[v]);
-          const int col = ct * tile_cols<MODE>() + wr * 64 + i * 16 + 4 * q;
-          store4<WT>(act + static_cast<long long>(off + m0 + m) * a.N + col, o);
-        }
-      }
+      for (int j = 0; j < 4; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int kb0 = 0;
+    for (; kb0 + kNS <= nkb; kb0 += kNS)
+      static_for<kNS>([&](auto U) __attribute__((always_inline)) { iteration(U, kb0 + decltype(U)::value); });
+    static_for<kNS>([&](auto U) __attribute__((always_inline)) {
+      if (kb0 + decltype(U)::value < nkb) iteration(U, kb0 + decltype(U)::value);
+    });
+    stage_barrier<0>();  // clamped tail loads; every stage is free again
+
+    // The next tile's first blocks are requested before this tile's
+    // epilogue, so their latency overlaps the epilogue's math and stores.
+    const int e_g = g, e_ct = ct, e_m0 = m0, e_mp = mp, e_off = off;
+    const int next = tile + stride;
+    const bool more = next < tile_end;
+    if (more) {
+      lookup(next, cur ^ 1);
+      __syncthreads();
+      cur ^= 1;
+      setup(cur);
+      prologue();
     }
-  } else if (MODE == kHead) {
-    // per token column: best (value, vocab index) over this wave's 128 rows,
-    // then over the two waves sharing the column (LDS), written as partial
-    // block ct of the arg max
-    float* red_v = reinterpret_cast<float*>(tile_stage<WT, BT, 0>());  // [2][BT]
-    int* red_i = reinterpret_cast<int*>(red_v + 2 * BT);                // [2][BT]
+
+    // epilogue: lane (r16, q) holds weight rows 4q + v of fragment wr*8 + rt
+    // for token column wt*64 + j*16 + r16
+    if constexpr (MODE == kGateUp) {
+      WT* act = static_cast<WT*>(a.out);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = wt * 64 + j * 16 + r16;
-      float best = -INFINITY;
-      int bi = 0x7fffffff;
+      for (int j = 0; j < 4; ++j) {
+        const int m = wt * 64 + j * 16 + r16;
+        if (m < e_mp) {
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 gv = acc[i][j], uv = acc[4 + i][j];
+            f32x4 o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int n = ct * tile_cols<MODE>() + (wr * 8 + rt) * 16 + 4 * q + v;
-          if (n < a.N) {
-            const float val = acc[rt][j][v];
-            if (a.logits != nullptr && m < mp) a.logits[static_cast<long long>(m0 + m) * a.N + n] = val;
-            if (better(val, n, best, bi)) { best = val; bi = n; }
+            for (int v = 0; v < 4; ++v) o[v] = silu_mul(gv[v], uv[v]);
+            const int col = e_ct * tile_cols<MODE>() + wr * 64 + i * 16 + 4 * q;
+            store4<WT>(act + static_cast<long long>(e_off + e_m0 + m) * a.N + col, o);
           }
         }
-#pragma unroll
-      for (int msk = 16; msk <= 32; msk <<= 1) {
-        const float ov = __shfl_xor(best, msk, kWave);
-        const int oi = __shfl_xor(bi, msk, kWave);
-        if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
       }
-      if (q == 0) {
-        red_v[wr * BT + m] = best;
-        red_i[wr * BT + m] = bi;
+    } else if constexpr (MODE == kHead) {
+      // per token column: best (value, vocab index) over this wave's 128
+      // rows, then over the two waves sharing the column (LDS), written as
+      // partial block e_ct of the arg max
+      __shared__ float red_v[2 * BT];
+      __shared__ int red_i[2 * BT];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = wt * 64 + j * 16 + r16;
+        float best = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int n = e_ct * tile_cols<MODE>() + (wr * 8 + rt) * 16 + 4 * q + v;
+            if (n < a.N) {
+              const float val = acc[rt][j][v];
+              if (a.logits != nullptr && m < e_mp) a.logits[static_cast<long long>(e_m0 + m) * a.N + n] = val;
+              if (better(val, n, best, bi)) { best = val; bi = n; }
+            }
+          }
+#pragma unroll
+        for (int msk = 16; msk <= 32; msk <<= 1) {
+          const float ov = __shfl_xor(best, msk, kWave);
+          const int oi = __shfl_xor(bi, msk, kWave);
+          if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+        }
+        if (q == 0) {
+          red_v[wr * BT + m] = best;
+          red_i[wr * BT + m] = bi;
+        }
       }
-    }
-    __syncthreads();
-    if (tid < mp) {
-      float best = red_v[tid];
-      int bi = red_i[tid];
-      if (better(red_v[BT + tid], red_i[BT + tid], best, bi)) {
-        best = red_v[BT + tid];
-        bi = red_i[BT + tid];
+      stage_barrier<63>();  // LDS writes visible; the prologue's loads stay in flight
+      if (tid < e_mp) {
+        float best = red_v[tid];
+        int bi = red_i[tid];
+        if (better(red_v[BT + tid], red_i[BT + tid], best, bi)) {
+          best = red_v[BT + tid];
+          bi = red_i[BT + tid];
+        }
+        const long long o = static_cast<long long>(e_m0 + tid) * n_ctiles + e_ct;  // [T][blocks]
+        static_cast<float*>(a.out)[o] = best;
+        a.out_idx[o] = bi;
       }
-      const long long o = static_cast<long long>(m0 + tid) * n_ctiles + ct;  // [T][blocks]
-      static_cast<float*>(a.out)[o] = best;
-      a.out_idx[o] = bi;
-    }
-  } else {
-    float* y = static_cast<float*>(a.out);
+      stage_barrier<63>();  // red_* free for the next tile
+    } else {
+      float* y = static_cast<float*>(a.out);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = wt * 64 + j * 16 + r16;
-      if (m < mp) {
-        const int p = clampi(a.sorted_src[off + m0 + m], 0, a.P - 1);
-        const int t = p / a.S;
-        const int slot = p - t * a.S;
-        const float wgt = slot < a.k ? a.topk_w[static_cast<long long>(t) * a.k + slot] : 1.0f;
+      for (int j = 0; j < 4; ++j) {
+        const int m = wt * 64 + j * 16 + r16;
+        if (m < e_mp) {
+          const int p = clampi(a.sorted_src[e_off + e_m0 + m], 0, a.P - 1);
+          const int t = p / a.S;
+          const int slot = p - t * a.S;
+          const float wgt = slot < a.k ? a.topk_w[static_cast<long long>(t) * a.k + slot] : 1.0f;
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-          f32x4 o = acc[rt][j];
+          for (int rt = 0; rt < 8; ++rt) {
+            f32x4 o = acc[rt][j];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] *= wgt;
-          const int row = ct * tile_cols<MODE>() + (wr * 8 + rt) * 16 + 4 * q;
-          store4<float>(y + static_cast<long long>(p) * a.N + row, o);
+            for (int v = 0; v < 4; ++v) o[v] *= wgt;
+            const int row = e_ct * tile_cols<MODE>() + (wr * 8 + rt) * 16 + 4 * q;
+            store4<float>(y + static_cast<long long>(p) * a.N + row, o);
+          }
         }
       }
     }
+    (void)e_g;
+    if (!more) break;
+    tile = next;
   }
 }
 
-// Upper bound of the tile count (groups are only known on the device): every
-// group contributes at most ceil(M_g / BT) <= M_g / BT + 1 token tiles.
-int tile_grid(int T, int k, int ns, int E, int n_ctiles, int BT) {
+// Persistent workgroups: one per CU slot (two per CU for 128-token tiles),
+// at most one per tile of the upper bound (groups are only known on the
+// device: every group contributes at most ceil(M_g / BT) <= M_g / BT + 1
+// token tiles); a multiple of the XCD count.
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+int tile_grid(int T, int k, int ns, int E, int n_ctiles, int BT, int per_cu) {
   const long long routed = (static_cast<long long>(T) * k + BT - 1) / BT + E;
   const long long shared = static_cast<long long>(ns) * ((T + BT - 1) / BT);
-  long long n = (routed + shared) * n_ctiles;
+  long long n = std::min<long long>((routed + shared) * n_ctiles, static_cast<long long>(cu_count()) * per_cu);
   n = (n + kXcds - 1) / kXcds * kXcds;
   return static_cast<int>(n);
 }
@@ -786,10 +854,10 @@ int tile_grid(int T, int k, int ns, int E, int n_ctiles, int BT) {
 template <typename WT, int MODE>
 void launch_tile(const GemmArgs& args, int n_ctiles, int G, int E, int k, int ns, hipStream_t s) {
   if (static_cast<long long>(args.T) * k >= 384LL * E) {
-    const int grid = tile_grid(args.T, k, ns, E, n_ctiles, 256);
+    const int grid = tile_grid(args.T, k, ns, E, n_ctiles, 256, TileCfg<WT, 256>::kPerCu);
     tile_gemm<WT, MODE, 256><<<grid, TileCfg<WT, 256>::kThreads, 0, s>>>(args, n_ctiles, G);
   } else {
-    const int grid = tile_grid(args.T, k, ns, E, n_ctiles, 128);
+    const int grid = tile_grid(args.T, k, ns, E, n_ctiles, 128, TileCfg<WT, 128>::kPerCu);
     tile_gemm<WT, MODE, 128><<<grid, TileCfg<WT, 128>::kThreads, 0, s>>>(args, n_ctiles, G);
   }
 }
@@ -805,7 +873,9 @@ static_assert(tile_cols<kHead>() == 16 * kRtHead * kWavesHead, "head partial blo
 template <typename WT>
 void launch_tile_head(const GemmArgs& args, int n_ctiles, hipStream_t s) {
   const int BT = args.T >= 512 ? 256 : 128;
-  long long n = static_cast<long long>(n_ctiles) * ((args.T + BT - 1) / BT);
+  long long n = std::min<long long>(static_cast<long long>(n_ctiles) * ((args.T + BT - 1) / BT),
+                                    static_cast<long long>(cu_count()) * (BT == 256 ? TileCfg<WT, 256>::kPerCu
+                                                                                    : TileCfg<WT, 128>::kPerCu));
   n = (n + kXcds - 1) / kXcds * kXcds;
   if (BT == 256)
     tile_gemm<WT, kHead, 256><<<static_cast<int>(n), TileCfg<WT, 256>::kThreads, 0, s>>>(args, n_ctiles, 1);
