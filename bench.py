@@ -32,11 +32,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="verify_step_b32k3",
-                    help="verify_step_b32k3 | zipf_verify_b{1,8,32,128}k{1,3} | decode_layer_t128 | prefill_layer_t9760")
+                    help="verify_step_b32k{3,2,1,0} | zipf_verify_b{1,8,32,128}k{1,3} | decode_layer_t128 | "
+                         "prefill_layer_t9760 | kselect_b32")
     ap.add_argument("--launch", choices=("auto", "eager", "graph"), default="auto")
     ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--graph-chunk", type=int, default=16,
+                    help="kselect_b32: verify steps captured per HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
     return ap.parse_args()
@@ -150,25 +153,12 @@ def cpu_baseline(wl, weights, tokens_np, budget_s):
             "seconds_measured": round(time.perf_counter() - t0, 2)}
 
 
-def run_verify(args, torch, np):
+def stage_inputs(dm, wl, n_steps, torch, np):
+    """Step inputs of a speculative run, staged in HBM: every sequence's greedy
+    trajectory from the GPU itself, drafts drawn against it at the workload's
+    acceptances, and the commit lengths a lossless step must produce."""
     import synth
-    from moe_decoder_greedy_amd import model as mdl
-    from moe_decoder_greedy_amd import ops
-
-    wl = synth.WORKLOADS[args.workload]
-    shape = wl.shape
-    B, K, V, H, I = wl.batch, wl.drafts, shape.vocab, shape.hidden, shape.inter
-    E, k, ns = shape.n_routed, shape.top_k, shape.n_shared
-    T, S, P = B * (K + 1), k + ns, B * (K + 1) * (k + ns)
-    t0 = time.perf_counter()
-    weights = synth.model_weights(shape)
-    log(f"weights generated in {time.perf_counter() - t0:.1f} s")
-    dm = mdl.DeviceModel(weights)
-    torch.cuda.synchronize()
-    log(f"uploaded {dm.weight_bytes() / 1e9:.2f} GB")
-
-    # greedy trajectory of every sequence (the drafts are drawn against it)
-    n_steps = args.warmup + args.steps
+    B, K, V = wl.batch, wl.drafts, wl.shape.vocab
     n_roll = n_steps * (K + 1) + K + 1
     last0 = synth.initial_tokens(B, V)
     cur = torch.from_numpy(last0).cuda()
@@ -191,8 +181,94 @@ def run_verify(args, torch, np):
                 n[b] += 1
         want_len[s] = n + 1
         pos += n + 1
-    inputs_d = torch.from_numpy(inputs).cuda()
     log(f"trajectory of {n_roll} greedy tokens, {n_steps} step inputs staged in HBM")
+    return torch.from_numpy(inputs).cuda(), want_len
+
+
+def run_kselect(args, torch, np):
+    """Choice of K (drafts per step) at B = 32: for K = 0 (plain greedy), 1, 2
+    and 3 the same model runs a loop of verify steps captured as one HIP graph
+    (chunks of consecutive steps, each reading its own staged input, no host
+    work inside a chunk). c(K) = step time / the K = 0 step time, tau(K) =
+    committed tokens per sequence per step as measured, S(K) = tau / c: the
+    decomposition the review of the pages gives for the speedup."""
+    import synth
+    from moe_decoder_greedy_amd import model as mdl
+    shape = synth.DECODER
+    weights = synth.model_weights(shape)
+    dm = mdl.DeviceModel(weights)
+    torch.cuda.synchronize()
+    chunk = max(1, min(args.graph_chunk, args.steps))
+    rows, lossless = [], True
+    for K in (0, 1, 2, 3):
+        wl = synth.WORKLOADS[f"verify_step_b32k{K}"]
+        B = wl.batch
+        n_steps = args.warmup + args.steps
+        inputs_d, want_len = stage_inputs(dm, wl, n_steps, torch, np)
+        outs = {key: torch.empty((n_steps,) + tuple(v.shape), dtype=v.dtype, device="cuda")
+                for key, v in dm.alloc_outputs(B, K).items()}
+        step_out = lambda s: {key: v[s] for key, v in outs.items()}
+        for s in range(n_steps):              # eager pass: warm-up and reference commits
+            dm.verify_step(inputs_d[s], out=step_out(s))
+        torch.cuda.synchronize()
+        ok = bool(np.array_equal(outs["commit_len"].cpu().numpy(), want_len))
+        graphs = []
+        for c0 in range(args.warmup, n_steps, chunk):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(c0, min(c0 + chunk, n_steps)):
+                    dm.verify_step(inputs_d[s], out=step_out(s))
+            graphs.append(g)
+        outs["commit_len"].zero_()
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        t_step = (time.perf_counter() - ta) / args.steps
+        got = outs["commit_len"].cpu().numpy()[args.warmup:]
+        ok = ok and bool(np.array_equal(got, want_len[args.warmup:]))
+        lossless = lossless and ok
+        tau = float(want_len[args.warmup:].sum()) / (args.steps * B)
+        rows.append({"K": K, "ms_per_step": round(t_step * 1e3, 4), "tau": round(tau, 4),
+                     "committed_tokens_per_s": round(tau * B / t_step, 1), "lossless": ok})
+        log(f"K={K}: {t_step * 1e3:.3f} ms/step (graph, {chunk} steps per graph), tau {tau:.3f}, commits ok {ok}")
+        del graphs
+    t0 = rows[0]["ms_per_step"]
+    for r in rows:
+        r["c"] = round(r["ms_per_step"] / t0, 4)
+        r["S"] = round(r["tau"] / r["c"], 4)
+    best = max(rows, key=lambda r: r["S"])
+    return {
+        "metric": "speculative speedup S = tau / c at the best K (B=32, graph-captured step loop)",
+        "value": best["S"], "unit": "x", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": best["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) bf16 weights, drafts at the first K of 0.830/0.663/0.636)",
+        "config": {"workload": "kselect_b32", "batch": 32, "layers": shape.n_layers, "vocab": shape.vocab,
+                   "graph_steps_per_replay": chunk, "best_K": best["K"]},
+        "per_K": rows, "lossless_commits": lossless, "roofline": None, "cpu_baseline": None,
+    }
+
+
+def run_verify(args, torch, np):
+    import synth
+    from moe_decoder_greedy_amd import model as mdl
+    from moe_decoder_greedy_amd import ops
+
+    wl = synth.WORKLOADS[args.workload]
+    shape = wl.shape
+    B, K, V, H, I = wl.batch, wl.drafts, shape.vocab, shape.hidden, shape.inter
+    E, k, ns = shape.n_routed, shape.top_k, shape.n_shared
+    T, S, P = B * (K + 1), k + ns, B * (K + 1) * (k + ns)
+    t0 = time.perf_counter()
+    weights = synth.model_weights(shape)
+    log(f"weights generated in {time.perf_counter() - t0:.1f} s")
+    dm = mdl.DeviceModel(weights)
+    torch.cuda.synchronize()
+    log(f"uploaded {dm.weight_bytes() / 1e9:.2f} GB")
+
+    n_steps = args.warmup + args.steps
+    inputs_d, want_len = stage_inputs(dm, wl, n_steps, torch, np)
 
     # ------------------------------------------------------------------ eager
     outs = {key: torch.empty((n_steps,) + tuple(v.shape), dtype=v.dtype, device="cuda")
@@ -443,6 +519,8 @@ def main():
         copy_probe(torch, args.copy_probe_mib)
     if args.workload.endswith(("_t128", "_t9760")):
         result = run_layer(args, torch, np)
+    elif args.workload == "kselect_b32":
+        result = run_kselect(args, torch, np)
     else:
         result = run_verify(args, torch, np)
     print(json.dumps(result), flush=True)

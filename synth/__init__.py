@@ -121,6 +121,11 @@ WORKLOADS: Dict[str, Workload] = {
     "verify_step_b32k3": Workload("verify_step_b32k3", DECODER, batch=32, drafts=3,
                                   accept=PAGE_ACCEPT, steps=64),
 }
+# The same step with K = 0 (plain greedy decoding), 1 and 2 drafts, for the
+# choice of K: drafts at the first K of the page's acceptances.
+for _k in (0, 1, 2):
+    _n = f"verify_step_b32k{_k}"
+    WORKLOADS[_n] = Workload(_n, DECODER, batch=32, drafts=_k, accept=PAGE_ACCEPT[:_k], steps=64)
 for _b in (1, 8, 32, 128):
     for _k, _acc in ((3, PAGE_ACCEPT), (1, PAGE_ACCEPT[:1])):
         _n = f"zipf_verify_b{_b}k{_k}"
