@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="verify_step_b32k3",
                     help="verify_step_b32k{3,2,1,0} | zipf_verify_b{1,8,32,128}k{1,3} | decode_layer_t128 | "
-                         "prefill_layer_t9760 | kselect_b32")
+                         "prefill_layer_t9760 | prefill_model_t9760 | kselect_b32")
     ap.add_argument("--launch", choices=("auto", "eager", "graph"), default="auto")
     ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,6 +151,99 @@ def cpu_baseline(wl, weights, tokens_np, budget_s):
                        f"{shape.n_layers} layers timed, mean extrapolated to {shape.n_layers}, "
                        f"plus head and accept; oracle step {t_step:.2f} s"),
             "seconds_measured": round(time.perf_counter() - t0, 2)}
+
+
+def cpu_baseline_prefill(weights, tokens_np, budget_s):
+    """The oracle as it stands on this host's cores over a bounded sample of
+    the prefill: the first rows of the first page through the layers, timed
+    layer by layer until the budget is spent, scaled to tokens/s (the
+    oracle's per-row work does not depend on the batch)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    shape = weights["shape"]
+    dt = weights["dtype"]
+    rows = tokens_np.reshape(-1)[:512]
+    t0 = time.perf_counter()
+    h = oracle.embed(rows, weights["emb"], dt)
+    layer_times = []
+    for layer in weights["layers"]:
+        ts = time.perf_counter()
+        h = oracle.moe_layer(h, layer, dt, shape.top_k, shape.n_routed, shape.n_shared, shape.eps, "bf16")["h_out"]
+        layer_times.append(time.perf_counter() - ts)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    per_row = float(np.mean(layer_times)) * shape.n_layers / len(rows)
+    return {"value": 1.0 / per_row, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{len(rows)} prompt rows (float64 numpy oracle): {len(layer_times)} of {shape.n_layers} "
+                       f"layers timed, mean extrapolated to {shape.n_layers}; the head for 8 rows is negligible"),
+            "seconds_measured": round(time.perf_counter() - t0, 2)}
+
+
+def run_prefill_model(args, torch, np):
+    """Page-shaped prefill: 8 pages x 1220 prompt tokens through all 12 layers,
+    the head on each page's last token (moev_prefill)."""
+    import synth
+    from moe_decoder_greedy_amd import model as mdl
+    wl = synth.WORKLOADS[args.workload]
+    shape = wl.shape
+    n_seq, T = wl.batch, wl.n_tokens
+    seq_len = T // n_seq
+    H, I, E, k, ns, V = shape.hidden, shape.inter, shape.n_routed, shape.top_k, shape.n_shared, shape.vocab
+    P = T * (k + ns)
+    weights = synth.model_weights(shape)
+    dm = mdl.DeviceModel(weights)
+    toks = synth.prompt_tokens(n_seq, seq_len, V)
+    td = torch.from_numpy(toks).cuda()
+    nt = torch.empty((n_seq,), dtype=torch.int32, device="cuda")
+    for _ in range(args.warmup):
+        dm.prefill(td, next_token=nt)
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    for _ in range(args.steps):
+        dm.prefill(td, next_token=nt)
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - ta) / args.steps
+    same = bool(np.array_equal(nt.cpu().numpy(), dm.greedy(td[:, -1].contiguous()).cpu().numpy()))
+    dur = {}
+    for st in ("route", "permute", "gate_up", "down", "head"):
+        n_ev = 1 if st == "head" else shape.n_layers
+        pend = []
+        for _ in range(max(1, args.kernel_steps // 4)):
+            bef = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+            aft = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+            dm.prefill(td, next_token=nt, probe=(st, bef, aft))
+            pend.append((bef, aft))
+        torch.cuda.synchronize()
+        dur[st] = float(np.mean([b.elapsed_time(a) for bef, aft in pend for b, a in zip(bef, aft)])) * 1e3
+    gu_flops = 4.0 * P * H * I
+    ach = gu_flops / (dur["gate_up"] * 1e-6) / 1e12
+    flops = shape.n_layers * (6.0 * P * H * I + 2.0 * T * E * H) + 2.0 * n_seq * H * V
+    bt = 256 if T * k >= 384 * E else 128
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(weights, toks, args.cpu_budget)
+    return {
+        "metric": "prefill tokens/s through 12 MoE layers + head on each page's last token",
+        "value": round(T / t, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, prompt token ids uniform over the vocabulary)",
+        "config": {"workload": wl.name, "pages": n_seq, "tokens_per_page": seq_len, "tokens": T,
+                   "layers": shape.n_layers, "hidden": H, "routed_experts": E, "top_k": k,
+                   "shared_experts": ns, "intermediate": I, "vocab": V},
+        "model_mfma_frac": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "next_token_matches_decode_path": same,
+        "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": stored_traffic(wl.name),
+                     "kernel": f"tile_gemm<bf16, gate/up, {bt}> (moe_ffn_gate_up)",
+                     "avg_launch_us": round(dur["gate_up"], 2), "flops_per_launch": gu_flops},
+        "kernel_avg_us": {n: round(v, 2) for n, v in dur.items()},
+        "cpu_baseline": cpu,
+    }
 
 
 def stage_inputs(dm, wl, n_steps, torch, np):
@@ -517,10 +610,12 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe_mib:
         copy_probe(torch, args.copy_probe_mib)
-    if args.workload.endswith(("_t128", "_t9760")):
-        result = run_layer(args, torch, np)
-    elif args.workload == "kselect_b32":
+    if args.workload == "kselect_b32":
         result = run_kselect(args, torch, np)
+    elif args.workload == "prefill_model_t9760":
+        result = run_prefill_model(args, torch, np)
+    elif args.workload.endswith(("_t128", "_t9760")):
+        result = run_layer(args, torch, np)
     else:
         result = run_verify(args, torch, np)
     print(json.dumps(result), flush=True)

@@ -270,6 +270,31 @@ moev_status moev_verify_step_probed(const moev_model* m, const int32_t* tokens, 
                                     int32_t* commit_len, int32_t* next_last, void* ws,
                                     size_t ws_bytes, const moev_step_probe* probe, void* stream);
 
+/*
+ * moev_prefill -- a page-shaped prompt through the whole decoder ("What the
+ * speed claims actually measure" on the aipolix.com page and "Start with the
+ * result" on kg.zhiyong.dev: a page brings about a thousand visual tokens plus
+ * the prompt before the first decode step).  Every one of the n_seq * seq_len
+ * prompt rows runs through all n_layers layers (route, grouped FFN, combine);
+ * the final norm, LM head and arg max run only for each sequence's last row.
+ *   tokens      int32 [n_seq, seq_len] device (row r = i * seq_len + j)
+ *   next_token  int32 [n_seq] (written): greedy token after token[i, seq_len-1]
+ *   h_out       fp32 [n_seq * seq_len, H] or NULL (written): the residual
+ *               stream after the last layer, before the final norm
+ *   ws          workspace of moev_prefill_workspace_size() bytes, 16-byte aligned
+ * The decoder has no attention (each row's result depends on its own token
+ * only), so next_token[i] equals the verify step's greedy token for the same
+ * token, bit for bit.  n_seq = 0 is a no-op; seq_len >= 1.  Same model limits
+ * as moev_verify_step.  Nothing allocates or synchronises.
+ */
+size_t moev_prefill_workspace_size(const moev_model* m, int n_seq, int seq_len);
+moev_status moev_prefill(const moev_model* m, const int32_t* tokens, int n_seq, int seq_len,
+                         int32_t* next_token, float* h_out, void* ws, size_t ws_bytes, void* stream);
+/* moev_prefill with the timing events of moev_verify_step_probed (measurement only). */
+moev_status moev_prefill_probed(const moev_model* m, const int32_t* tokens, int n_seq, int seq_len,
+                                int32_t* next_token, float* h_out, void* ws, size_t ws_bytes,
+                                const moev_step_probe* probe, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,11 @@ SIGNATURES = {
     "moev_verify_step_probed": (c_int, [ctypes.POINTER(Model), c_void_p, c_int, c_int, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         ctypes.POINTER(StepProbe), c_void_p]),
+    "moev_prefill_workspace_size": (c_size_t, [ctypes.POINTER(Model), c_int, c_int]),
+    "moev_prefill": (c_int, [ctypes.POINTER(Model), c_void_p, c_int, c_int, c_void_p, c_void_p,
+                             c_void_p, c_size_t, c_void_p]),
+    "moev_prefill_probed": (c_int, [ctypes.POINTER(Model), c_void_p, c_int, c_int, c_void_p, c_void_p,
+                                    c_void_p, c_size_t, ctypes.POINTER(StepProbe), c_void_p]),
 }
 
 _lib = None

@@ -63,6 +63,33 @@ __global__ __launch_bounds__(256) void verify_kernel(const int32_t* __restrict__
 
 }  // namespace
 
+__global__ __launch_bounds__(256) void gather_last_kernel(const float* __restrict__ h,
+                                                          const float* __restrict__ y, int S, int H4,
+                                                          int seq_len, float* __restrict__ out) {
+  const long long t = static_cast<long long>(blockIdx.x) * seq_len + seq_len - 1;
+  for (int c = threadIdx.x; c < H4; c += blockDim.x) {
+    float4 v = reinterpret_cast<const float4*>(h)[t * H4 + c];
+    if (y != nullptr) {
+      const float4* ys = reinterpret_cast<const float4*>(y) + t * S * H4 + c;
+      float4 acc = ys[0];
+      for (int sl = 1; sl < S; ++sl) {
+        const float4 w = ys[static_cast<long long>(sl) * H4];
+        acc.x += w.x;
+        acc.y += w.y;
+        acc.z += w.z;
+        acc.w += w.w;
+      }
+      v = make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
+    }
+    reinterpret_cast<float4*>(out)[static_cast<long long>(blockIdx.x) * H4 + c] = v;
+  }
+}
+
+void launch_gather_last(const float* h, const float* y, int S, int H, int n_seq, int seq_len,
+                        float* out, hipStream_t s) {
+  if (n_seq > 0) gather_last_kernel<<<n_seq, 256, 0, s>>>(h, y, S, H / 4, seq_len, out);
+}
+
 void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
                     hipStream_t s) {
   const long long n = static_cast<long long>(T) * (H / 4);

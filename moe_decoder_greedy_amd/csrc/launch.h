@@ -55,6 +55,11 @@ void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* 
                            int k, int ns, int dt, float* y_slots, hipStream_t s);
 void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
                     hipStream_t s);
+// out[i] = h[t] + the sum of y's S slots of row t (y may be NULL), t = the
+// last row of sequence i (rows i*seq_len .. (i+1)*seq_len - 1); the same
+// slot order as launch_combine.
+void launch_gather_last(const float* h, const float* y, int S, int H, int n_seq, int seq_len,
+                        float* out, hipStream_t s);
 // y_prev (optional): the last layer's expert slots, added to h before the norm.
 void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,
                    int V, int dt, int32_t* argmax_out, float* max_out, float* logits_out,

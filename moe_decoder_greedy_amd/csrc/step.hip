@@ -52,11 +52,10 @@ StepLayout layout(const moev_model& m, int T) {
   return L;
 }
 
-moev_status validate_model(const moev_model* m, int B, int K) {
+// Checks of the model and of T = B * (K + 1) (or the prefill's token count).
+moev_status validate_model_rows(const moev_model* m, long long T) {
   MOEV_REQUIRE(m != nullptr, MOEV_ERR_INVALID_ARG, "model must not be NULL");
   MOEV_CHECK(check_dtype(m->dtype), MOEV_ERR_UNSUPPORTED);
-  MOEV_REQUIRE(B >= 0 && K >= 0, MOEV_ERR_INVALID_ARG, "need B >= 0 and K >= 0 (B=%d K=%d)", B, K);
-  MOEV_REQUIRE(K <= 64, MOEV_ERR_UNSUPPORTED, "K=%d drafts exceeds 64", K);
   MOEV_REQUIRE(m->hidden >= 64 && m->hidden <= 3072 && m->hidden % 64 == 0, MOEV_ERR_UNSUPPORTED,
                "hidden size %d must be a multiple of 64 in [64, 3072]", m->hidden);
   MOEV_REQUIRE(m->inter >= 64 && m->inter <= 8192 && m->inter % 64 == 0, MOEV_ERR_UNSUPPORTED,
@@ -71,9 +70,8 @@ moev_status validate_model(const moev_model* m, int B, int K) {
                "the whole-step driver needs k + ns <= 16 (got %d)", m->top_k + m->n_shared);
   MOEV_REQUIRE(m->vocab >= 1, MOEV_ERR_INVALID_ARG, "vocabulary must be >= 1");
   MOEV_REQUIRE(m->n_layers >= 0, MOEV_ERR_INVALID_ARG, "n_layers must be >= 0");
-  const long long T = static_cast<long long>(B) * (K + 1);
   MOEV_REQUIRE(T * (m->top_k + m->n_shared) < (1ll << 31), MOEV_ERR_UNSUPPORTED,
-               "B*(K+1)*(k+ns) must be < 2^31");
+               "tokens*(k+ns) must be < 2^31 (tokens=%lld)", T);
   MOEV_CHECK(need_ptr(m->emb, "model.emb") && opt_ptr(m->norm_f, "model.norm_f") &&
                  need_ptr(m->w_lm, "model.w_lm"),
              MOEV_ERR_INVALID_ARG);
@@ -91,6 +89,31 @@ moev_status validate_model(const moev_model* m, int B, int K) {
   return MOEV_OK;
 }
 
+moev_status validate_model(const moev_model* m, int B, int K) {
+  MOEV_REQUIRE(B >= 0 && K >= 0, MOEV_ERR_INVALID_ARG, "need B >= 0 and K >= 0 (B=%d K=%d)", B, K);
+  MOEV_REQUIRE(K <= 64, MOEV_ERR_UNSUPPORTED, "K=%d drafts exceeds 64", K);
+  return validate_model_rows(m, static_cast<long long>(B) * (K + 1));
+}
+
+// Prefill workspace: the layer loop's buffers for T rows, then the last rows'
+// combined residual [n_seq, H] and their head workspace.
+struct PrefillLayout {
+  StepLayout L;
+  size_t h_last, head_last, total;
+};
+
+PrefillLayout prefill_layout(const moev_model& m, int n_seq, int seq_len) {
+  PrefillLayout P{};
+  P.L = layout(m, n_seq * seq_len);
+  size_t o = P.L.total;
+  P.h_last = o;
+  o += align_up(static_cast<size_t>(n_seq) * m.hidden * 4, 256);
+  P.head_last = o;
+  o += align_up(lmhead_ws_bytes(n_seq, m.hidden, m.vocab, m.dtype), 256);
+  P.total = o;
+  return P;
+}
+
 }  // namespace
 }  // namespace moev
 
@@ -102,27 +125,11 @@ extern "C" size_t moev_verify_step_workspace_size(const moev_model* m, int B, in
 namespace moev {
 namespace {
 
-moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, int32_t* greedy,
-                     int32_t* n_accept, int32_t* commit, int32_t* commit_len, int32_t* next_last,
-                     void* ws, size_t ws_bytes, const moev_step_probe* probe, void* stream) {
-  if (moev_status st = validate_model(m, B, K)) return st;
-  if (B == 0) return MOEV_OK;
-  MOEV_CHECK(need_ptr(tokens, "tokens", 4) && need_ptr(greedy, "greedy", 4) &&
-                 need_ptr(n_accept, "n_accept", 4) && need_ptr(commit, "commit", 4),
-             MOEV_ERR_INVALID_ARG);
-  if (probe != nullptr) {
-    MOEV_REQUIRE(probe->stage >= MOEV_STAGE_ROUTE && probe->stage <= MOEV_STAGE_HEAD &&
-                     probe->n >= 0 && (probe->n == 0 || (probe->before && probe->after)),
-                 MOEV_ERR_INVALID_ARG, "bad probe");
-  }
-  const int T = B * (K + 1);
-  const StepLayout L = layout(*m, T);
-  MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE,
-               "workspace must be non-NULL and 16-byte aligned");
-  MOEV_REQUIRE(ws_bytes >= L.total, MOEV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
-               ws_bytes, L.total);
-
-  unsigned char* base = static_cast<unsigned char*>(ws);
+// Embedding and the decoder layers for T rows.  On return h holds the residual
+// stream before the last layer's expert outputs, y those outputs: the caller
+// folds the last combine into whatever reads h next.
+void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLayout& L,
+                unsigned char* base, const moev_step_probe* probe, hipStream_t s) {
   float* h = reinterpret_cast<float*>(base + L.h);
   void* x = base + L.x;
   int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
@@ -132,8 +139,6 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
   int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
   float* y = reinterpret_cast<float*>(base + L.y);
   void* ffn_ws = base + L.ffn;
-  void* head_ws = base + L.head;
-  const hipStream_t s = as_stream(stream);
   const int H = m->hidden, E = m->n_routed, k = m->top_k, ns = m->n_shared, I = m->inter;
   const int dt = m->dtype;
 
@@ -177,6 +182,40 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
       launch_ffn_down(ffn_ws, sorted, offsets, w, lw.w_down, T, H, I, E, k, ns, dt, y, s);
     mark(MOEV_STAGE_DOWN, l, true);
   }
+}
+
+moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, int32_t* greedy,
+                     int32_t* n_accept, int32_t* commit, int32_t* commit_len, int32_t* next_last,
+                     void* ws, size_t ws_bytes, const moev_step_probe* probe, void* stream) {
+  if (moev_status st = validate_model(m, B, K)) return st;
+  if (B == 0) return MOEV_OK;
+  MOEV_CHECK(need_ptr(tokens, "tokens", 4) && need_ptr(greedy, "greedy", 4) &&
+                 need_ptr(n_accept, "n_accept", 4) && need_ptr(commit, "commit", 4),
+             MOEV_ERR_INVALID_ARG);
+  if (probe != nullptr) {
+    MOEV_REQUIRE(probe->stage >= MOEV_STAGE_ROUTE && probe->stage <= MOEV_STAGE_HEAD &&
+                     probe->n >= 0 && (probe->n == 0 || (probe->before && probe->after)),
+                 MOEV_ERR_INVALID_ARG, "bad probe");
+  }
+  const int T = B * (K + 1);
+  const StepLayout L = layout(*m, T);
+  MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE,
+               "workspace must be non-NULL and 16-byte aligned");
+  MOEV_REQUIRE(ws_bytes >= L.total, MOEV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+               ws_bytes, L.total);
+
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  const hipStream_t s = as_stream(stream);
+  run_layers(m, tokens, T, L, base, probe, s);
+  const int S = m->top_k + m->n_shared;
+  float* h = reinterpret_cast<float*>(base + L.h);
+  float* y = reinterpret_cast<float*>(base + L.y);
+  void* head_ws = base + L.head;
+  auto mark = [&](int stage, int index, bool after) {
+    if (probe == nullptr || probe->stage != stage || index >= probe->n) return;
+    hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
+  };
+  const int H = m->hidden, dt = m->dtype;
   mark(MOEV_STAGE_HEAD, 0, false);
   launch_lmhead(h, m->norm_f, m->eps, m->w_lm, T, H, m->vocab, dt, greedy, nullptr, nullptr,
                 head_ws, s, m->n_layers > 0 ? y : nullptr, S);
@@ -185,8 +224,76 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
   return launch_status("moev_verify_step");
 }
 
+// Prefill: every prompt row through the layers; the head only for each
+// sequence's last row.
+moev_status run_prefill(const moev_model* m, const int32_t* tokens, int n_seq, int seq_len,
+                        int32_t* next_token, float* h_out, void* ws, size_t ws_bytes,
+                        const moev_step_probe* probe, void* stream) {
+  MOEV_REQUIRE(n_seq >= 0 && seq_len >= 1, MOEV_ERR_INVALID_ARG,
+               "need n_seq >= 0 and seq_len >= 1 (n_seq=%d seq_len=%d)", n_seq, seq_len);
+  const long long T64 = static_cast<long long>(n_seq) * seq_len;
+  MOEV_REQUIRE(T64 < (1ll << 31), MOEV_ERR_UNSUPPORTED, "n_seq*seq_len must be < 2^31");
+  if (moev_status st = validate_model_rows(m, T64)) return st;
+  if (n_seq == 0) return MOEV_OK;
+  MOEV_CHECK(need_ptr(tokens, "tokens", 4) && need_ptr(next_token, "next_token", 4) &&
+                 opt_ptr(h_out, "h_out"),
+             MOEV_ERR_INVALID_ARG);
+  if (probe != nullptr) {
+    MOEV_REQUIRE(probe->stage >= MOEV_STAGE_ROUTE && probe->stage <= MOEV_STAGE_HEAD &&
+                     probe->n >= 0 && (probe->n == 0 || (probe->before && probe->after)),
+                 MOEV_ERR_INVALID_ARG, "bad probe");
+  }
+  const int T = static_cast<int>(T64);
+  const PrefillLayout P = prefill_layout(*m, n_seq, seq_len);
+  MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE,
+               "workspace must be non-NULL and 16-byte aligned");
+  MOEV_REQUIRE(ws_bytes >= P.total, MOEV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+               ws_bytes, P.total);
+
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  const hipStream_t s = as_stream(stream);
+  run_layers(m, tokens, T, P.L, base, probe, s);
+  const int S = m->top_k + m->n_shared;
+  float* h = reinterpret_cast<float*>(base + P.L.h);
+  const float* y = m->n_layers > 0 ? reinterpret_cast<const float*>(base + P.L.y) : nullptr;
+  float* h_last = reinterpret_cast<float*>(base + P.h_last);
+  // the last layer's combine: for every row when the caller wants the
+  // residual stream, else only for the rows the head reads
+  if (h_out != nullptr) {
+    if (y != nullptr) launch_combine(y, h, T, m->hidden, S, h_out, s);
+    else hipMemcpyAsync(h_out, h, static_cast<size_t>(T) * m->hidden * 4, hipMemcpyDeviceToDevice, s);
+  }
+  launch_gather_last(h, y, S, m->hidden, n_seq, seq_len, h_last, s);
+  auto mark = [&](int stage, int index, bool after) {
+    if (probe == nullptr || probe->stage != stage || index >= probe->n) return;
+    hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
+  };
+  mark(MOEV_STAGE_HEAD, 0, false);
+  launch_lmhead(h_last, m->norm_f, m->eps, m->w_lm, n_seq, m->hidden, m->vocab, m->dtype, next_token,
+                nullptr, nullptr, base + P.head_last, s);
+  mark(MOEV_STAGE_HEAD, 0, true);
+  return launch_status("moev_prefill");
+}
+
 }  // namespace
 }  // namespace moev
+
+extern "C" size_t moev_prefill_workspace_size(const moev_model* m, int n_seq, int seq_len) {
+  if (m == nullptr || n_seq < 0 || seq_len < 1) return 0;
+  return moev::prefill_layout(*m, n_seq, seq_len).total;
+}
+
+extern "C" moev_status moev_prefill(const moev_model* m, const int32_t* tokens, int n_seq, int seq_len,
+                                    int32_t* next_token, float* h_out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  return moev::run_prefill(m, tokens, n_seq, seq_len, next_token, h_out, ws, ws_bytes, nullptr, stream);
+}
+
+extern "C" moev_status moev_prefill_probed(const moev_model* m, const int32_t* tokens, int n_seq,
+                                           int seq_len, int32_t* next_token, float* h_out, void* ws,
+                                           size_t ws_bytes, const moev_step_probe* probe, void* stream) {
+  return moev::run_prefill(m, tokens, n_seq, seq_len, next_token, h_out, ws, ws_bytes, probe, stream);
+}
 
 extern "C" moev_status moev_verify_step(const moev_model* m, const int32_t* tokens, int B, int K,
                                         int32_t* greedy, int32_t* n_accept, int32_t* commit,

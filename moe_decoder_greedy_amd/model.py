@@ -116,6 +116,40 @@ class DeviceModel:
             ctypes.byref(probe), stream_handle(stream)))
         return out
 
+    def prefill_workspace(self, n_seq: int, seq_len: int) -> torch.Tensor:
+        key = ("prefill", n_seq, seq_len)
+        if key not in self._ws:
+            n = lib().moev_prefill_workspace_size(self.c_model, n_seq, seq_len)
+            self._ws[key] = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        return self._ws[key]
+
+    def prefill(self, tokens: torch.Tensor, next_token: Optional[torch.Tensor] = None,
+                h_out: Optional[torch.Tensor] = None, probe=None, stream=None) -> torch.Tensor:
+        """``tokens`` int32 [n_seq, seq_len] on the GPU through every layer; the
+        greedy token after each sequence's last prompt token.  ``h_out`` (fp32
+        [n_seq*seq_len, H], optional) receives the final residual stream.
+        ``probe`` = (stage, before_events, after_events) records HIP events
+        around that stage's launches."""
+        n_seq, seq_len = tokens.shape
+        nt = torch.empty((n_seq,), dtype=torch.int32, device=self.device) if next_token is None else next_token
+        ws = self.prefill_workspace(n_seq, seq_len)
+        if probe is None:
+            check("moev_prefill", lib().moev_prefill(
+                self.c_model, ptr(tokens), n_seq, seq_len, ptr(nt), ptr(h_out), ptr(ws), ws.numel(),
+                stream_handle(stream)))
+        else:
+            stage, before, after = probe
+            for e in list(before) + list(after):
+                e.record()
+            n = len(before)
+            arr_b = (ctypes.c_void_p * n)(*[e.cuda_event for e in before])
+            arr_a = (ctypes.c_void_p * n)(*[e.cuda_event for e in after])
+            pr = _lib.StepProbe(_lib.STAGES[stage], n, arr_b, arr_a)
+            check("moev_prefill_probed", lib().moev_prefill_probed(
+                self.c_model, ptr(tokens), n_seq, seq_len, ptr(nt), ptr(h_out), ptr(ws), ws.numel(),
+                ctypes.byref(pr), stream_handle(stream)))
+        return nt
+
     def greedy(self, tokens: torch.Tensor) -> torch.Tensor:
         """Greedy successor of every token (a K = 0 step)."""
         return self.verify_step(tokens.reshape(-1, 1).to(torch.int32).contiguous())["greedy"].reshape(-1)

@@ -36,7 +36,7 @@ import numpy as np
 
 __all__ = [
     "ModelShape", "Workload", "TINY", "DECODER", "WORKLOADS",
-    "model_weights", "hidden_states", "initial_tokens", "draft_tokens",
+    "model_weights", "hidden_states", "initial_tokens", "prompt_tokens", "draft_tokens",
     "zipf_bias", "f32_to_bf16_bits", "splitmix64", "counter_uniform",
     "counter_randint", "weight_bytes",
 ]
@@ -90,7 +90,7 @@ class Workload:
     shape: ModelShape
     batch: int = 0                  # B sequences (verify workloads)
     drafts: int = 0                 # K drafts per sequence
-    tokens: int = 0                 # T for single-layer workloads (h given)
+    tokens: int = 0                 # T for single-layer and prefill workloads
     accept: Tuple[float, ...] = ()  # per-position draft-correct probability
     draft_mode: str = "exclude"     # "exclude": a wrong draft avoids the truth
     steps: int = 0                  # verify steps in a trajectory run
@@ -98,7 +98,7 @@ class Workload:
 
     @property
     def n_tokens(self) -> int:
-        return self.tokens if self.layer_only else self.batch * (1 + self.drafts)
+        return self.tokens if (self.layer_only or self.tokens) else self.batch * (1 + self.drafts)
 
 
 # Conditional draft acceptance by position, K=3: 0.830 / 0.663 / 0.636
@@ -117,6 +117,9 @@ WORKLOADS: Dict[str, Workload] = {
     # One decoder layer at prefill shape: 8 pages x (1156 visual + 64 prompt).
     "prefill_layer_t9760": Workload("prefill_layer_t9760", replace(DECODER, n_layers=1),
                                     tokens=9760, layer_only=True),
+    # Page-shaped prefill through all 12 layers + the head on each page's
+    # last token: 8 pages x (1156 visual + 64 prompt) tokens.
+    "prefill_model_t9760": Workload("prefill_model_t9760", DECODER, batch=8, tokens=9760),
     # The full verify step: 12 layers + head, 32 sequences x (1+3).
     "verify_step_b32k3": Workload("verify_step_b32k3", DECODER, batch=32, drafts=3,
                                   accept=PAGE_ACCEPT, steps=64),
@@ -297,6 +300,15 @@ def initial_tokens(batch: int, vocab: int, seed: int = 2) -> np.ndarray:
     """First committed token of each sequence, uniform over the vocabulary."""
     b = np.arange(batch)
     return counter_randint(vocab, seed, b, -1, -1, 0).astype(np.int32)
+
+
+def prompt_tokens(n_seq: int, seq_len: int, vocab: int, seed: int = 5) -> np.ndarray:
+    """Page-shaped prompts [n_seq, seq_len], token ids uniform over the
+    vocabulary (standing in for the visual and prompt tokens of a page)."""
+    i = np.arange(n_seq)[:, None]
+    j = np.arange(seq_len)[None, :]
+    return counter_randint(vocab, seed, np.broadcast_to(i, (n_seq, seq_len)),
+                           np.broadcast_to(j, (n_seq, seq_len)), -1, 1).astype(np.int32)
 
 
 def draft_tokens(cont: np.ndarray, pos: np.ndarray, accept: Sequence[float], vocab: int,

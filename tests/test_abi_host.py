@@ -116,3 +116,22 @@ def test_step_validation(lib):
     m.top_k = 65
     assert lib.moev_verify_step(ctypes.byref(m), FAKE, 32, 3, FAKE, FAKE, FAKE, None, None, FAKE,
                                 ws, None) == UNSUPPORTED
+
+
+def test_prefill_validation(lib):
+    layers = (_lib.LayerWeights * 1)(_lib.LayerWeights(None, FAKE, None, FAKE, FAKE, None))
+    m = _lib.Model(1280, 64, 896, 6, 2, 129280, 1, BF16, 1e-6, FAKE, None, FAKE, layers)
+    ws = lib.moev_prefill_workspace_size(ctypes.byref(m), 8, 1220)
+    # at least the layer loop's activations for 9760 rows
+    assert ws > 9760 * 1280 * 4 + 9760 * 8 * 1280 * 4
+    assert lib.moev_prefill_workspace_size(ctypes.byref(m), 8, 0) == 0
+    call = lambda n_seq=8, seq_len=1220, nt=FAKE, n=ws: lib.moev_prefill(
+        ctypes.byref(m), FAKE, n_seq, seq_len, nt, None, FAKE, n, None)
+    assert call() == INVALID and "w_down" in _err(lib)     # the layer's missing down weights
+    m.n_layers = 0
+    assert call(seq_len=0) == INVALID
+    assert call(nt=None) == INVALID
+    assert call(n=ws - 1) == WORKSPACE
+    assert call(n_seq=0) == OK                              # nothing to do
+    m.hidden = 1300
+    assert call() == UNSUPPORTED
