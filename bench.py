@@ -490,7 +490,7 @@ def run_verify(args, torch, np):
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(wl, weights, inputs[args.warmup], args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(wl, weights, inputs_d[args.warmup].cpu().numpy(), args.cpu_budget)
     else:
         result["cpu_baseline"] = None
     return result

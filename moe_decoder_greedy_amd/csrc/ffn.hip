@@ -865,7 +865,7 @@ void launch_tile(const GemmArgs& args, int n_ctiles, int G, int E, int k, int ns
 // LM head on the tile schedule: one group of T tokens, 256 vocabulary rows
 // per column tile, so the partial arg max blocks are the column tiles.
 #ifndef MOEV_HEAD_TILE_MIN_TOKENS
-#define MOEV_HEAD_TILE_MIN_TOKENS 64
+#define MOEV_HEAD_TILE_MIN_TOKENS 32
 #endif
 constexpr int kHeadTileMinTokens = MOEV_HEAD_TILE_MIN_TOKENS;
 static_assert(tile_cols<kHead>() == 16 * kRtHead * kWavesHead, "head partial blocks");
