@@ -33,7 +33,16 @@ Sources are three web pages on Jina-OCR-v1:
    disagreement (or after the last draft, the bonus token) is committed too, so
    every step commits n+1 tokens.  The committed stream equals plain greedy
    decoding ("lossless").
-4. tau = mean committed tokens per step; for independent per-position draft
+4. FastMTP draft block ([P1] "The speed comes from three layers working
+   together": one dense draft block proposes up to three tokens by being
+   applied recursively; [P2] "A document parser, not just a text recognizer":
+   a shared block drafts three positions; [P3] Summary / Scope & Claims,
+   Section 3.1).  The pages give no more of its structure; ``draft_block``
+   takes the multi-token-prediction module reading listed in the design
+   notes (hidden state and next-token embedding, each RMS-normalised,
+   projected to H; one pre-norm dense SwiGLU with residual; the verifier's
+   LM head behind the block's own final norm).
+5. tau = mean committed tokens per step; for independent per-position draft
    acceptances a_1..a_K its expectation is 1 + sum_m prod_{j<=m} a_j, which
    with Table 8's 0.830/0.663/0.636 gives the printed 2.73 ([P3] Strengths,
    speculative-decoding analysis).
@@ -59,6 +68,7 @@ __all__ = [
     "pair_groups", "permute", "grouped_ffn", "combine", "moe_layer",
     "embed", "lm_head", "first_argmax", "mtp_verify", "model_greedy",
     "verify_step", "greedy_rollout", "expected_tau", "acceptance_rate",
+    "draft_dense", "draft_block",
 ]
 
 
@@ -363,6 +373,67 @@ def greedy_rollout(last: np.ndarray, model: dict, n_tokens: int, operands: str =
         cur = model_greedy(cur, model, operands)["argmax"].astype(np.int32)
         out[:, i] = cur
     return out
+
+
+# ---------------------------------------------------------------------------
+# FastMTP draft block
+
+def draft_dense(draft: dict) -> dict:
+    """The dense matrices of a draft block stored as slices: W_p [H, 2H] =
+    [w_proj[0] | w_proj[1]], W_gate / W_up [n*I, H] = the slices stacked along
+    the intermediate axis, W_down [H, n*I] = the down slices side by side."""
+    dt = draft["dtype"]
+    wp = to_f64(draft["w_proj"], dt)
+    return {
+        "w_p": np.concatenate([wp[0], wp[1]], axis=1),
+        "w_gate": np.concatenate(list(to_f64(draft["w_gate"], dt)), axis=0),
+        "w_up": np.concatenate(list(to_f64(draft["w_up"], dt)), axis=0),
+        "w_down": np.concatenate(list(to_f64(draft["w_down"], dt)), axis=1),
+    }
+
+
+def draft_block(z0: np.ndarray, t0: np.ndarray, draft: dict, model: dict, K: int,
+                operands: str = "bf16") -> dict:
+    """K recursive steps of the FastMTP draft block (see the module notes).
+
+    Step j (j = 1..K), from the hidden state z_{j-1} (z_0 = the verifier's
+    final residual state at the position that produced the last committed
+    token) and the token t_{j-1} (t_0 = that token):
+        u   = [RMSNorm(z_{j-1}) * norm_z ; RMSNorm(Emb[t_{j-1}]) * norm_e]
+        z'  = W_p u
+        x   = RMSNorm(z') * norm_ffn
+        z_j = z' + W_down (SiLU(W_gate x) * (W_up x))
+        t_j = arg max W_lm (RMSNorm(z_j) * norm_out)   (lowest index on ties)
+    With ``operands="bf16"`` and bf16 weights, u, x, the SwiGLU activation and
+    the head's input are rounded to bf16 as the GEMMs that consume them take
+    them.  Returns drafts [B, K] int32, z [B, H] (= z_K), and per step the head
+    gap (``gap`` [B, K]) and z_j (``zs`` [K, B, H]).
+    """
+    shape = model["shape"]
+    dt = model["dtype"]
+    eps = shape.eps
+    dd = draft_dense(draft)
+    rb = (lambda a: round_bf16(a)) if (operands == "bf16" and dt == "bf16") else (lambda a: a)
+    z = np.asarray(z0, np.float64)
+    t = np.asarray(t0, np.int64).reshape(-1)
+    B = z.shape[0]
+    drafts = np.zeros((B, K), np.int32)
+    gaps = np.zeros((B, K))
+    zs = np.zeros((K, B, z.shape[1]))
+    for j in range(K):
+        u = np.concatenate([rmsnorm(z, to_f64(draft["norm_z"], dt), eps),
+                            rmsnorm(embed(t, model["emb"], dt), to_f64(draft["norm_e"], dt), eps)],
+                           axis=1)
+        zp = rb(u) @ dd["w_p"].T
+        x = rb(rmsnorm(zp, to_f64(draft["norm_ffn"], dt), eps))
+        a = silu(x @ dd["w_gate"].T) * (x @ dd["w_up"].T)
+        z = zp + rb(a) @ dd["w_down"].T
+        head = lm_head(z, draft["norm_out"], model["w_lm"], dt, eps, operands)
+        t = head["argmax"].astype(np.int64)
+        drafts[:, j] = t
+        gaps[:, j] = head["gap"]
+        zs[j] = z
+    return {"drafts": drafts, "z": z, "gap": gaps, "zs": zs}
 
 
 def expected_tau(accept: Sequence[float]) -> float:

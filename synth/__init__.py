@@ -38,11 +38,13 @@ __all__ = [
     "ModelShape", "Workload", "TINY", "DECODER", "WORKLOADS",
     "model_weights", "hidden_states", "initial_tokens", "prompt_tokens", "draft_tokens",
     "zipf_bias", "f32_to_bf16_bits", "splitmix64", "counter_uniform",
-    "counter_randint", "weight_bytes",
+    "counter_randint", "weight_bytes", "draft_weights", "draft_states",
 ]
 
 # tensor codes in the spawn key
 _ROUTER, _GATE, _UP, _DOWN, _LM, _EMB, _HIDDEN, _ZIPF = 0, 1, 2, 3, 4, 5, 6, 7
+_DPROJ, _DGATE, _DUP, _DDOWN, _DSTATE = 8, 9, 10, 11, 12
+_DRAFT_LAYER = 1000  # layer field of the draft block's streams
 _ROW_CHUNK = 4096  # rows per stream for the vocabulary-sized tensors
 
 
@@ -238,6 +240,50 @@ def model_weights(shape: ModelShape, seed: int = 0, layers: Optional[Sequence[in
             jobs.append((out["emb"][c:c + _ROW_CHUNK], seed, (mid, 0, _EMB, ci), shape.emb_std, bf16))
             jobs.append((out["w_lm"][c:c + _ROW_CHUNK], seed, (mid, 0, _LM, ci), std, bf16))
     _fill(jobs, workers)
+    return out
+
+
+def draft_weights(shape: ModelShape, seed: int = 0, workers: Optional[int] = None) -> dict:
+    """Synthetic weights of the FastMTP draft block for a decoder of ``shape``.
+
+    Stored as the slices the kernels consume (see the oracle for the dense
+    block they make up): ``w_proj`` [2, H, H] (slice g = columns g*H..(g+1)*H-1
+    of the [H, 2H] input projection: g = 0 acts on the normalised hidden state,
+    g = 1 on the normalised token embedding), ``w_gate`` / ``w_up`` [n, I, H]
+    and ``w_down`` [n, H, I] (the dense SwiGLU of width n*I split along its
+    intermediate axis, n = top_k + n_shared), and RMSNorm weights ``norm_z``,
+    ``norm_e`` (the two inputs), ``norm_ffn`` (before the FFN) and ``norm_out``
+    (before the shared LM head), all ones.
+    """
+    bf16 = shape.dtype == "bf16"
+    H, I = shape.hidden, shape.inter
+    n = shape.top_k + shape.n_shared
+    mid, std = shape.model_id, shape.weight_std
+    d = {
+        "dtype": shape.dtype, "n_slices": n,
+        "norm_z": _ones(H, bf16), "norm_e": _ones(H, bf16),
+        "norm_ffn": _ones(H, bf16), "norm_out": _ones(H, bf16),
+        "w_proj": _empty((2, H, H), bf16),
+        "w_gate": _empty((n, I, H), bf16),
+        "w_up": _empty((n, I, H), bf16),
+        "w_down": _empty((n, H, I), bf16),
+    }
+    jobs = []
+    for g in range(2):
+        jobs.append((d["w_proj"][g], seed, (mid, _DRAFT_LAYER, _DPROJ, g), std, bf16))
+    for s in range(n):
+        jobs.append((d["w_gate"][s], seed, (mid, _DRAFT_LAYER, _DGATE, s), std, bf16))
+        jobs.append((d["w_up"][s], seed, (mid, _DRAFT_LAYER, _DUP, s), std, bf16))
+        jobs.append((d["w_down"][s], seed, (mid, _DRAFT_LAYER, _DDOWN, s), std, bf16))
+    _fill(jobs, workers)
+    return d
+
+
+def draft_states(shape: ModelShape, batch: int, seed: int = 4) -> np.ndarray:
+    """Hidden states entering a draft block, float32 [batch, H] ~ N(0, 1)."""
+    out = np.empty((batch, shape.hidden), np.float32)
+    out[:] = _normal_block(seed, (shape.model_id, _DRAFT_LAYER, _DSTATE, 0), batch * shape.hidden,
+                           1.0, False).reshape(batch, shape.hidden)
     return out
 
 

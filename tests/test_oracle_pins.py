@@ -453,3 +453,114 @@ def test_y_slots_layout_per_slot():
             ref = wt * _torch_swiglu(st["x"][t:t + 1], layer["w_gate"][e], layer["w_up"][e],
                                      layer["w_down"][e])[0]
             np.testing.assert_allclose(st["y_slots"][t, r], ref, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# FastMTP draft block (oracle.draft_block): closed forms under special weights
+
+def _tiny_draft(model, rng=None, std=0.2):
+    """Draft weights for the tiny model (fp32), random or to be overwritten."""
+    d = synth.draft_weights(synth.TINY)
+    if rng is not None:
+        for key in ("w_proj", "w_gate", "w_up", "w_down"):
+            d[key] = (rng.standard_normal(d[key].shape) * std).astype(np.float32)
+    return d
+
+
+def _zero_ffn(d):
+    d["w_down"] = np.zeros_like(d["w_down"])
+    return d
+
+
+def test_draft_copy_through_is_the_verifier_head(tiny_model):
+    """W_p = [I | 0] and no FFN: z_1 = RMSNorm(z_0), so the draft is the
+    verifier head's greedy token of z_0 (RMSNorm is idempotent up to eps)."""
+    H = synth.TINY.hidden
+    d = _zero_ffn(_tiny_draft(tiny_model))
+    d["w_proj"] = np.stack([np.eye(H), np.zeros((H, H))]).astype(np.float32)
+    d["norm_out"] = np.asarray(tiny_model["norm_f"])
+    z0 = synth.draft_states(synth.TINY, 16)
+    t0 = np.arange(16) * 7
+    out = oracle.draft_block(z0, t0, d, tiny_model, 1, "exact")
+    ref = oracle.lm_head(z0, tiny_model["norm_f"], tiny_model["w_lm"], "f32", synth.TINY.eps, "exact")
+    assert np.all(ref["gap"] > 1e-6)
+    np.testing.assert_array_equal(out["drafts"][:, 0], ref["argmax"])
+    ms = np.mean(np.asarray(z0, np.float64) ** 2, axis=1, keepdims=True)
+    np.testing.assert_allclose(out["z"], z0 / np.sqrt(ms + synth.TINY.eps), rtol=1e-12)
+
+
+def test_draft_embedding_echo_repeats_the_token(tiny_model):
+    """W_p = [0 | I], no FFN, head tied to an embedding whose rows all have the
+    same norm: the draft maximises e_v . e_t over v, which by Cauchy-Schwarz is
+    v = t, at every one of the K recursive steps."""
+    H, V = synth.TINY.hidden, synth.TINY.vocab
+    rng = np.random.default_rng(11)
+    emb = rng.standard_normal((V, H))
+    emb = (emb / np.linalg.norm(emb, axis=1, keepdims=True)).astype(np.float32)
+    model = dict(tiny_model, emb=emb, w_lm=emb)
+    d = _zero_ffn(_tiny_draft(model))
+    d["w_proj"] = np.stack([np.zeros((H, H)), np.eye(H)]).astype(np.float32)
+    # a negative norm_z would flip the echo if it were applied to the embedding half
+    d["norm_z"] = np.full(H, -1.0, np.float32)
+    d["norm_e"] = np.full(H, 2.0, np.float32)
+    t0 = rng.integers(0, V, 24)
+    z0 = synth.draft_states(synth.TINY, 24)
+    out = oracle.draft_block(z0, t0, d, model, 3, "exact")
+    np.testing.assert_array_equal(out["drafts"], np.repeat(t0[:, None], 3, axis=1))
+
+
+@pytest.mark.parametrize("s,i", [(0, 0), (2, 17), (1, 63)])
+def test_draft_single_unit_ffn_closed_form(tiny_model, s, i):
+    """Only unit i of slice s of the dense FFN is non-zero (gate row a, up row
+    b, down column c): z_1 = z' + c * SiLU(a.x) * (b.x), x = RMSNorm(z'), with
+    z' = RMSNorm(z_0) from W_p = [I | 0]."""
+    H = synth.TINY.hidden
+    rng = np.random.default_rng(5 + s * 100 + i)
+    d = _tiny_draft(tiny_model)
+    for key in ("w_gate", "w_up", "w_down"):
+        d[key] = np.zeros_like(d[key])
+    a, b, c = (rng.standard_normal(H) for _ in range(3))
+    d["w_gate"][s, i] = a
+    d["w_up"][s, i] = b
+    d["w_down"][s, :, i] = c
+    d["w_proj"] = np.stack([np.eye(H), np.zeros((H, H))]).astype(np.float32)
+    gz, gf, ge = (rng.uniform(0.5, 1.5, H).astype(np.float32) for _ in range(3))
+    d["norm_z"], d["norm_ffn"], d["norm_e"] = gz, gf, ge
+    z0 = synth.draft_states(synth.TINY, 8).astype(np.float64)
+    out = oracle.draft_block(z0, np.zeros(8, np.int64), d, tiny_model, 1, "exact")
+    eps = synth.TINY.eps
+    zp = z0 / np.sqrt(np.mean(z0 ** 2, axis=1, keepdims=True) + eps) * gz
+    x = zp / np.sqrt(np.mean(zp ** 2, axis=1, keepdims=True) + eps) * gf
+    ga = x @ a.astype(np.float32).astype(np.float64)
+    ub = x @ b.astype(np.float32).astype(np.float64)
+    want = zp + np.outer(ga / (1 + np.exp(-ga)) * ub, c.astype(np.float32).astype(np.float64))
+    np.testing.assert_allclose(out["z"], want, rtol=1e-10, atol=1e-12)
+
+
+def test_draft_recursion_feeds_state_and_token(tiny_model):
+    """K = 3 in one call equals three calls of K = 1, each fed the previous
+    call's (z, draft token)."""
+    d = _tiny_draft(tiny_model, np.random.default_rng(3))
+    z = synth.draft_states(synth.TINY, 12)
+    t = np.arange(12) * 31 % synth.TINY.vocab
+    full = oracle.draft_block(z, t, d, tiny_model, 3)
+    for j in range(3):
+        one = oracle.draft_block(z, t, d, tiny_model, 1)
+        np.testing.assert_array_equal(one["drafts"][:, 0], full["drafts"][:, j])
+        np.testing.assert_array_equal(one["z"], full["zs"][j])
+        z, t = one["z"], one["drafts"][:, 0]
+
+
+def test_draft_dense_slices_layout():
+    """The stored slices make up the dense matrices as documented: column
+    block g of W_p is w_proj[g]; intermediate rows s*I..(s+1)*I-1 of W_gate are
+    w_gate[s]; columns s*I.. of W_down are w_down[s]."""
+    d = synth.draft_weights(synth.TINY)
+    H, I, n = synth.TINY.hidden, synth.TINY.inter, d["n_slices"]
+    dd = oracle.draft_dense(d)
+    assert dd["w_p"].shape == (H, 2 * H) and dd["w_gate"].shape == (n * I, H)
+    assert dd["w_down"].shape == (H, n * I)
+    np.testing.assert_array_equal(dd["w_p"][:, H:], d["w_proj"][1])
+    np.testing.assert_array_equal(dd["w_gate"][2 * I:3 * I], d["w_gate"][2])
+    np.testing.assert_array_equal(dd["w_up"][I:2 * I], d["w_up"][1])
+    np.testing.assert_array_equal(dd["w_down"][:, (n - 1) * I:], d["w_down"][n - 1])
