@@ -295,6 +295,76 @@ moev_status moev_prefill_probed(const moev_model* m, const int32_t* tokens, int 
                                 int32_t* next_token, float* h_out, void* ws, size_t ws_bytes,
                                 const moev_step_probe* probe, void* stream);
 
+/*
+ * FastMTP draft block ("The speed comes from three layers working together" on
+ * kg.zhiyong.dev: one dense draft block proposes up to three tokens, applied
+ * recursively; the aipolix.com page's "A document parser, not just a text
+ * recognizer": a shared block drafts three positions).  The pages give no
+ * more of its structure; this library computes, for draft step j = 1..K from
+ * the hidden state z (fp32 [H]) and token t of step j-1:
+ *   u   = [RMSNorm(z) * norm_z ; RMSNorm(Emb[t]) * norm_e]        (2H)
+ *   z'  = W_p u                                                   (H)
+ *   z_j = z' + W_down (SiLU(W_gate x) * (W_up x)),  x = RMSNorm(z') * norm_ffn
+ *   t_j = arg max W_lm (RMSNorm(z_j) * norm_out)  (the model's LM head and
+ *         embedding; lowest index on exact ties)
+ * Weights are stored as the slices the grouped GEMMs take, each
+ * fragment-packed by moev_pack_weights:
+ *   w_proj [2][H][H]  slice g = columns g*H .. (g+1)*H-1 of W_p (g = 0: the
+ *                     hidden-state half, g = 1: the embedding half)
+ *   w_gate, w_up [n][I][H] and w_down [n][H][I]: the dense SwiGLU of width n*I
+ *                     split along its intermediate axis (I = the model's inter)
+ * norm_* are dt [H] or NULL (ones).  n_slices in [1, 16].
+ */
+typedef struct moev_draft_weights {
+  const void* norm_z;
+  const void* norm_e;
+  const void* w_proj;
+  const void* norm_ffn;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* norm_out;
+  int n_slices;
+} moev_draft_weights;
+
+/*
+ * moev_draft -- K recursive draft steps for B sequences.
+ *   z0      fp32 [B, H] device: hidden state entering step 1
+ *   t0      int32 [B] device: token entering step 1
+ *   drafts  int32 [B, K] (written): t_1 .. t_K
+ *   z_out   fp32 [B, H] or NULL (written): z_K
+ *   ws      workspace of moev_draft_workspace_size() bytes, 16-byte aligned
+ * B = 0 or K = 0 is a no-op.  Token ids outside [0, V) are clamped.  Nothing
+ * allocates or synchronises.
+ */
+size_t moev_draft_workspace_size(const moev_model* m, const moev_draft_weights* d, int B);
+moev_status moev_draft(const moev_model* m, const moev_draft_weights* d, const float* z0,
+                       const int32_t* t0, int B, int K, int32_t* drafts, float* z_out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * moev_spec_step -- one whole speculative step on the device: the verify pass
+ * of moev_verify_step on tokens [B, K+1], then K draft steps for the next
+ * pass, started from the verifier's final residual state at each sequence's
+ * last accepted position (row b*(K+1) + n_accept[b], whose greedy token is
+ * next_last[b]) and from next_last[b] itself.
+ *   greedy, n_accept, commit, commit_len: as moev_verify_step
+ *   next_tokens int32 [B, K+1] (written): next_last, then the K drafts -- the
+ *               tokens argument of the next call
+ *   h_final     fp32 [B*(K+1), H] or NULL (written): the residual stream after
+ *               the last layer, before the final norm
+ *   ws          workspace of moev_spec_step_workspace_size() bytes
+ * K >= 1.  A chain of calls, each fed the previous next_tokens, runs the
+ * speculative loop without the host.
+ */
+size_t moev_spec_step_workspace_size(const moev_model* m, const moev_draft_weights* d, int B,
+                                     int K);
+moev_status moev_spec_step(const moev_model* m, const moev_draft_weights* d,
+                           const int32_t* tokens, int B, int K, int32_t* greedy,
+                           int32_t* n_accept, int32_t* commit, int32_t* commit_len,
+                           int32_t* next_tokens, float* h_final, void* ws, size_t ws_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,6 +31,12 @@ class StepProbe(ctypes.Structure):
                 ("after", ctypes.POINTER(c_void_p))]
 
 
+class DraftWeights(ctypes.Structure):
+    _fields_ = [("norm_z", c_void_p), ("norm_e", c_void_p), ("w_proj", c_void_p),
+                ("norm_ffn", c_void_p), ("w_gate", c_void_p), ("w_up", c_void_p),
+                ("w_down", c_void_p), ("norm_out", c_void_p), ("n_slices", c_int)]
+
+
 STAGES = {"route": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4, "head": 5}
 
 # name -> (restype, argtypes); mirrors include/moev.h
@@ -65,6 +71,14 @@ SIGNATURES = {
     "moev_verify_step_probed": (c_int, [ctypes.POINTER(Model), c_void_p, c_int, c_int, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         ctypes.POINTER(StepProbe), c_void_p]),
+    "moev_draft_workspace_size": (c_size_t, [ctypes.POINTER(Model), ctypes.POINTER(DraftWeights), c_int]),
+    "moev_draft": (c_int, [ctypes.POINTER(Model), ctypes.POINTER(DraftWeights), c_void_p, c_void_p, c_int,
+                           c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moev_spec_step_workspace_size": (c_size_t, [ctypes.POINTER(Model), ctypes.POINTER(DraftWeights), c_int,
+                                                 c_int]),
+    "moev_spec_step": (c_int, [ctypes.POINTER(Model), ctypes.POINTER(DraftWeights), c_void_p, c_int, c_int,
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                               c_size_t, c_void_p]),
     "moev_prefill_workspace_size": (c_size_t, [ctypes.POINTER(Model), c_int, c_int]),
     "moev_prefill": (c_int, [ctypes.POINTER(Model), c_void_p, c_int, c_int, c_void_p, c_void_p,
                              c_void_p, c_size_t, c_void_p]),

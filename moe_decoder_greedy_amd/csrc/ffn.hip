@@ -924,7 +924,8 @@ template <typename WT, int TPB>
 __global__ __launch_bounds__(256) void norm_cast_kernel(const float* __restrict__ h,
                                                         const float* __restrict__ y, int S,
                                                         const WT* __restrict__ gamma, float eps,
-                                                        int T, int H, WT* __restrict__ xo) {
+                                                        int T, int H, WT* __restrict__ xo,
+                                                        float* __restrict__ h_out) {
   extern __shared__ float hs[];   // [TPB][H]
   const int t0 = blockIdx.x * TPB;
   const int nt = min(TPB, T - t0);
@@ -933,7 +934,7 @@ __global__ __launch_bounds__(256) void norm_cast_kernel(const float* __restrict_
     const int tt = f / h4;
     const int i = (f - tt * h4) * 4;
     const long long t = t0 + tt;
-    float4 v = *reinterpret_cast<const float4*>(h + t * H + i);
+    float4 v = h != nullptr ? *reinterpret_cast<const float4*>(h + t * H + i) : make_float4(0.f, 0.f, 0.f, 0.f);
     if (y != nullptr) {
       const float4* ys = reinterpret_cast<const float4*>(y + t * S * H + i);
       float4 sv[kNormMaxSlots];
@@ -949,8 +950,9 @@ __global__ __launch_bounds__(256) void norm_cast_kernel(const float* __restrict_
           acc.z += sv[sl].z;
           acc.w += sv[sl].w;
         }
-      v = make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
+      v = h != nullptr ? make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w) : acc;
     }
+    if (h_out != nullptr) *reinterpret_cast<float4*>(h_out + t * H + i) = v;
     *reinterpret_cast<float4*>(hs + tt * H + i) = v;
   }
   __syncthreads();
@@ -981,6 +983,7 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* __restri
                                                            const int32_t* __restrict__ pidx,
                                                            int nblk, int T,
                                                            int32_t* __restrict__ argmax_out,
+                                                           int out_stride,
                                                            float* __restrict__ max_out) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
@@ -993,7 +996,7 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* __restri
   }
   wave_argmax(best, bi);
   if (lane == 0) {
-    argmax_out[t] = bi;
+    argmax_out[static_cast<long long>(t) * out_stride] = bi;
     if (max_out) max_out[t] = best;
   }
 }
@@ -1145,9 +1148,33 @@ void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t*
   launch_ffn_down(ws, sorted_src, offsets, topk_w, w_down, T, H, I, E, k, ns, dt, y_slots, s);
 }
 
+void launch_norm_cast(const float* h, const float* y, int S, const void* gamma, float eps, int T,
+                      int H, int dt, void* xo, float* h_out, hipStream_t s) {
+  // one token per block for decode-sized batches (more blocks in flight)
+  const int tpb = T <= 512 ? 1 : 4;
+  const int nb = (T + tpb - 1) / tpb;
+  const size_t nlds = static_cast<size_t>(tpb) * H * sizeof(float);
+  if (dt == MOEV_BF16) {
+    if (tpb == 1)
+      norm_cast_kernel<u16, 1><<<nb, 256, nlds, s>>>(h, y, S, static_cast<const u16*>(gamma), eps, T, H,
+                                                    static_cast<u16*>(xo), h_out);
+    else
+      norm_cast_kernel<u16, 4><<<nb, 256, nlds, s>>>(h, y, S, static_cast<const u16*>(gamma), eps, T, H,
+                                                    static_cast<u16*>(xo), h_out);
+  } else {
+    if (tpb == 1)
+      norm_cast_kernel<float, 1><<<nb, 256, nlds, s>>>(h, y, S, static_cast<const float*>(gamma), eps, T,
+                                                      H, static_cast<float*>(xo), h_out);
+    else
+      norm_cast_kernel<float, 4><<<nb, 256, nlds, s>>>(h, y, S, static_cast<const float*>(gamma), eps, T,
+                                                      H, static_cast<float*>(xo), h_out);
+  }
+}
+
 void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,
                    int V, int dt, int32_t* argmax_out, float* max_out, float* logits_out,
-                   void* ws, hipStream_t s, const float* y_prev, int S_prev) {
+                   void* ws, hipStream_t s, const float* y_prev, int S_prev, float* h_out,
+                   int out_stride) {
   const size_t xf_bytes = align_up(static_cast<size_t>(T) * H * esize(dt), 256);
   const int nblk = head_blocks(V);
   const size_t part = align_up(static_cast<size_t>(nblk) * T * 4, 256);
@@ -1165,31 +1192,14 @@ void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_
   hd.out = pmax;
   hd.out_idx = pidx;
   hd.logits = logits_out;
-  // one token per block for decode-sized batches (more blocks in flight)
-  const int tpb = T <= 512 ? 1 : 4;
-  const int nb = (T + tpb - 1) / tpb;
-  const size_t nlds = static_cast<size_t>(tpb) * H * sizeof(float);
+  launch_norm_cast(h, y_prev, S_prev, norm_f, eps, T, H, dt, xf, h_out, s);
   if (dt == MOEV_BF16) {
-    if (tpb == 1)
-      norm_cast_kernel<u16, 1><<<nb, 256, nlds, s>>>(h, y_prev, S_prev, static_cast<const u16*>(norm_f),
-                                                    eps, T, H, static_cast<u16*>(xf));
-    else
-      norm_cast_kernel<u16, 4><<<nb, 256, nlds, s>>>(h, y_prev, S_prev, static_cast<const u16*>(norm_f),
-                                                    eps, T, H, static_cast<u16*>(xf));
     if (T >= kHeadTileMinTokens) launch_tile_head<u16>(hd, nblk, s);
     else launch_gemm<u16, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   } else {
-    if (tpb == 1)
-      norm_cast_kernel<float, 1><<<nb, 256, nlds, s>>>(h, y_prev, S_prev,
-                                                      static_cast<const float*>(norm_f), eps, T, H,
-                                                      static_cast<float*>(xf));
-    else
-      norm_cast_kernel<float, 4><<<nb, 256, nlds, s>>>(h, y_prev, S_prev,
-                                                      static_cast<const float*>(norm_f), eps, T, H,
-                                                      static_cast<float*>(xf));
     launch_gemm<float, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   }
-  argmax_reduce_kernel<<<T, 64, 0, s>>>(pmax, pidx, nblk, T, argmax_out, max_out);
+  argmax_reduce_kernel<<<T, 64, 0, s>>>(pmax, pidx, nblk, T, argmax_out, out_stride, max_out);
 }
 
 moev_status validate_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,

@@ -46,6 +46,21 @@ void launch_ffn_gate_up(const void* x, const int32_t* sorted_src, const int32_t*
 void launch_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* offsets,
                      const float* topk_w, const void* w_down, int T, int H, int I, int E, int k,
                      int ns, int dt, float* y_slots, hipStream_t s);
+// Model checks shared by the whole-step entry points (T rows).
+moev_status validate_model_rows(const moev_model* m, long long T);
+
+// FastMTP draft block (draft.hip).  run_draft enqueues K draft steps for B
+// rows: step 1 reads z_src row b*K1 + n_accept[b] (row b when n_accept is
+// NULL) and token t0[b]; draft j lands in out[b*out_stride + out_col0 + j-1]
+// and is step j+1's token; t0_copy (optional) receives t0 at
+// t0_copy[b*out_stride]; z_out (optional) receives z_K.
+size_t draft_ws_bytes(const moev_model& m, const moev_draft_weights& d, int B);
+moev_status validate_draft(const moev_model* m, const moev_draft_weights* d, int B);
+void run_draft(const moev_model& m, const moev_draft_weights& d, const float* z_src,
+               const int32_t* n_accept, int K1, const int32_t* t0, int B, int K, int32_t* out,
+               int out_stride, int out_col0, int32_t* t0_copy, float* z_out, unsigned char* ws,
+               hipStream_t s);
+
 // Expert GEMMs reading expert lists (T <= kListMaxTokens): act holds G*T rows.
 void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t* counts,
                               const void* w_gate, const void* w_up, int T, int H, int I, int E,
@@ -61,9 +76,16 @@ void launch_combine(const float* y, const float* h_in, int T, int H, int S, floa
 void launch_gather_last(const float* h, const float* y, int S, int H, int n_seq, int seq_len,
                         float* out, hipStream_t s);
 // y_prev (optional): the last layer's expert slots, added to h before the norm.
+// h_out (optional): the combined residual h + sum of y_prev's slots, fp32;
+// argmax_out[t * out_stride] receives token t's arg max.
 void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,
                    int V, int dt, int32_t* argmax_out, float* max_out, float* logits_out,
-                   void* ws, hipStream_t s, const float* y_prev = nullptr, int S_prev = 0);
+                   void* ws, hipStream_t s, const float* y_prev = nullptr, int S_prev = 0,
+                   float* h_out = nullptr, int out_stride = 1);
+// xo = RMSNorm(v) * gamma cast to dt, v = h (NULL: zeros) + the S slots of y
+// (NULL: none) in slot order; h_out (optional) receives v in fp32.
+void launch_norm_cast(const float* h, const float* y, int S, const void* gamma, float eps, int T,
+                      int H, int dt, void* xo, float* h_out, hipStream_t s);
 void launch_verify(const int32_t* tokens, const int32_t* greedy, int B, int K, int32_t* n_accept,
                    int32_t* commit, int32_t* commit_len, int32_t* next_last, hipStream_t s);
 

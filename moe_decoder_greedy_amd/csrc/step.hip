@@ -52,6 +52,8 @@ StepLayout layout(const moev_model& m, int T) {
   return L;
 }
 
+}  // namespace
+
 // Checks of the model and of T = B * (K + 1) (or the prefill's token count).
 moev_status validate_model_rows(const moev_model* m, long long T) {
   MOEV_REQUIRE(m != nullptr, MOEV_ERR_INVALID_ARG, "model must not be NULL");
@@ -88,6 +90,8 @@ moev_status validate_model_rows(const moev_model* m, long long T) {
   }
   return MOEV_OK;
 }
+
+namespace {
 
 moev_status validate_model(const moev_model* m, int B, int K) {
   MOEV_REQUIRE(B >= 0 && K >= 0, MOEV_ERR_INVALID_ARG, "need B >= 0 and K >= 0 (B=%d K=%d)", B, K);
@@ -186,7 +190,8 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
 
 moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, int32_t* greedy,
                      int32_t* n_accept, int32_t* commit, int32_t* commit_len, int32_t* next_last,
-                     void* ws, size_t ws_bytes, const moev_step_probe* probe, void* stream) {
+                     void* ws, size_t ws_bytes, const moev_step_probe* probe, void* stream,
+                     float* h_final = nullptr) {
   if (moev_status st = validate_model(m, B, K)) return st;
   if (B == 0) return MOEV_OK;
   MOEV_CHECK(need_ptr(tokens, "tokens", 4) && need_ptr(greedy, "greedy", 4) &&
@@ -218,7 +223,7 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
   const int H = m->hidden, dt = m->dtype;
   mark(MOEV_STAGE_HEAD, 0, false);
   launch_lmhead(h, m->norm_f, m->eps, m->w_lm, T, H, m->vocab, dt, greedy, nullptr, nullptr,
-                head_ws, s, m->n_layers > 0 ? y : nullptr, S);
+                head_ws, s, m->n_layers > 0 ? y : nullptr, S, h_final);
   mark(MOEV_STAGE_HEAD, 0, true);
   launch_verify(tokens, greedy, B, K, n_accept, commit, commit_len, next_last, s);
   return launch_status("moev_verify_step");
@@ -310,4 +315,67 @@ extern "C" moev_status moev_verify_step_probed(const moev_model* m, const int32_
                                                const moev_step_probe* probe, void* stream) {
   return moev::run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last, ws,
                         ws_bytes, probe, stream);
+}
+
+namespace moev {
+namespace {
+
+// Speculative step workspace: the verify step's, then the final residual
+// [T, H] (when the caller passes none), next_last [B] and the draft block's.
+struct SpecLayout {
+  size_t h_final, next_last, draft, total;
+};
+
+SpecLayout spec_layout(const moev_model& m, const moev_draft_weights& d, int B, int K) {
+  SpecLayout S{};
+  const int T = B * (K + 1);
+  size_t o = layout(m, T).total;
+  S.h_final = o;
+  o += align_up(static_cast<size_t>(T) * m.hidden * 4, 256);
+  S.next_last = o;
+  o += align_up(static_cast<size_t>(B) * 4, 256);
+  S.draft = o;
+  o += draft_ws_bytes(m, d, B);
+  S.total = o;
+  return S;
+}
+
+}  // namespace
+}  // namespace moev
+
+extern "C" size_t moev_spec_step_workspace_size(const moev_model* m, const moev_draft_weights* d,
+                                                int B, int K) {
+  if (m == nullptr || d == nullptr || B < 0 || K < 0 || d->n_slices < 1) return 0;
+  return moev::spec_layout(*m, *d, B, K).total;
+}
+
+extern "C" moev_status moev_spec_step(const moev_model* m, const moev_draft_weights* d,
+                                      const int32_t* tokens, int B, int K, int32_t* greedy,
+                                      int32_t* n_accept, int32_t* commit, int32_t* commit_len,
+                                      int32_t* next_tokens, float* h_final, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  using namespace moev;
+  clear_error();
+  MOEV_REQUIRE(B >= 0 && K >= 1, MOEV_ERR_INVALID_ARG, "need B >= 0 and K >= 1 (B=%d K=%d)", B, K);
+  if (moev_status st = validate_model(m, B, K)) return st;
+  if (moev_status st = validate_draft(m, d, B)) return st;
+  if (B == 0) return MOEV_OK;
+  MOEV_CHECK(need_ptr(next_tokens, "next_tokens", 4) && opt_ptr(h_final, "h_final"),
+             MOEV_ERR_INVALID_ARG);
+  const SpecLayout S = spec_layout(*m, *d, B, K);
+  MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE,
+               "workspace must be non-NULL and 16-byte aligned");
+  MOEV_REQUIRE(ws_bytes >= S.total, MOEV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+               ws_bytes, S.total);
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  float* hf = h_final != nullptr ? h_final : reinterpret_cast<float*>(base + S.h_final);
+  int32_t* next_last = reinterpret_cast<int32_t*>(base + S.next_last);
+  if (moev_status st = run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last,
+                                ws, ws_bytes, nullptr, stream, hf))
+    return st;
+  // drafts for the next pass: from row b*(K+1) + n_accept[b] of the final
+  // residual and from next_last[b], which also becomes column 0
+  run_draft(*m, *d, hf, n_accept, K + 1, next_last, B, K, next_tokens, K + 1, 1, next_tokens,
+            nullptr, base + S.draft, as_stream(stream));
+  return launch_status("moev_spec_step");
 }

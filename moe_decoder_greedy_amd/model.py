@@ -150,6 +150,63 @@ class DeviceModel:
                 ctypes.byref(pr), stream_handle(stream)))
         return nt
 
+    # ------------------------------------------------------------ draft block
+    def attach_draft(self, draft: dict) -> None:
+        """Upload FastMTP draft-block weights (as ``synth.draft_weights``)."""
+        dt = self.dtype
+        D = {key: to_device(draft[key], dt, self.device)
+             for key in ("norm_z", "norm_e", "norm_ffn", "norm_out")}
+        for key in ("w_proj", "w_gate", "w_up", "w_down"):
+            D[key] = pack_weights(to_device(draft[key], dt, self.device))
+        self.draft_w = D
+        self._c_draft = _lib.DraftWeights(ptr(D["norm_z"]), ptr(D["norm_e"]), ptr(D["w_proj"]),
+                                          ptr(D["norm_ffn"]), ptr(D["w_gate"]), ptr(D["w_up"]),
+                                          ptr(D["w_down"]), ptr(D["norm_out"]), int(draft["n_slices"]))
+
+    @property
+    def c_draft(self):
+        return ctypes.byref(self._c_draft)
+
+    def draft_bytes(self) -> int:
+        return sum(t.nbytes for t in self.draft_w.values())
+
+    def _ws_named(self, key, n: int) -> torch.Tensor:
+        if key not in self._ws:
+            self._ws[key] = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        return self._ws[key]
+
+    def draft(self, z0: torch.Tensor, t0: torch.Tensor, K: int, drafts: Optional[torch.Tensor] = None,
+              z_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """K draft tokens per row from hidden states ``z0`` (fp32 [B, H]) and
+        tokens ``t0`` (int32 [B]); ``z_out`` (optional) receives z_K."""
+        B = z0.shape[0]
+        d = torch.empty((B, K), dtype=torch.int32, device=self.device) if drafts is None else drafts
+        ws = self._ws_named(("draft", B), lib().moev_draft_workspace_size(self.c_model, self.c_draft, B))
+        check("moev_draft", lib().moev_draft(self.c_model, self.c_draft, ptr(z0), ptr(t0), B, K, ptr(d),
+                                             ptr(z_out), ptr(ws), ws.numel(), stream_handle(stream)))
+        return d
+
+    def alloc_spec_outputs(self, B: int, K: int) -> dict:
+        out = self.alloc_outputs(B, K)
+        del out["next_last"]
+        out["next_tokens"] = torch.empty((B, K + 1), dtype=torch.int32, device=self.device)
+        return out
+
+    def spec_step(self, tokens: torch.Tensor, out: Optional[dict] = None,
+                  h_final: Optional[torch.Tensor] = None, stream=None) -> dict:
+        """Verify ``tokens`` (int32 [B, K+1]) and draft the next pass's tokens
+        (``out["next_tokens"]``) in one call into ``moev_spec_step``."""
+        B, K1 = tokens.shape
+        K = K1 - 1
+        out = self.alloc_spec_outputs(B, K) if out is None else out
+        ws = self._ws_named(("spec", B, K),
+                            lib().moev_spec_step_workspace_size(self.c_model, self.c_draft, B, K))
+        check("moev_spec_step", lib().moev_spec_step(
+            self.c_model, self.c_draft, ptr(tokens), B, K, ptr(out["greedy"]), ptr(out["n_accept"]),
+            ptr(out["commit"]), ptr(out["commit_len"]), ptr(out["next_tokens"]), ptr(h_final), ptr(ws),
+            ws.numel(), stream_handle(stream)))
+        return out
+
     def greedy(self, tokens: torch.Tensor) -> torch.Tensor:
         """Greedy successor of every token (a K = 0 step)."""
         return self.verify_step(tokens.reshape(-1, 1).to(torch.int32).contiguous())["greedy"].reshape(-1)

@@ -135,3 +135,36 @@ def test_prefill_validation(lib):
     assert call(n_seq=0) == OK                              # nothing to do
     m.hidden = 1300
     assert call() == UNSUPPORTED
+
+
+def test_draft_and_spec_step_validation(lib):
+    layers = (_lib.LayerWeights * 1)(_lib.LayerWeights(None, FAKE, None, FAKE, FAKE, FAKE))
+    m = _lib.Model(1280, 64, 896, 6, 2, 129280, 1, BF16, 1e-6, FAKE, None, FAKE, layers)
+    d = _lib.DraftWeights(None, None, FAKE, None, FAKE, FAKE, FAKE, None, 8)
+    ws = lib.moev_draft_workspace_size(ctypes.byref(m), ctypes.byref(d), 32)
+    # at least the dense FFN's activations and slot outputs for 32 rows
+    assert ws > 8 * 32 * 896 * 2 + 32 * 8 * 1280 * 4
+    spec = lib.moev_spec_step_workspace_size(ctypes.byref(m), ctypes.byref(d), 32, 3)
+    assert spec > ws + lib.moev_verify_step_workspace_size(ctypes.byref(m), 32, 3)
+    assert lib.moev_draft_workspace_size(ctypes.byref(m), None, 32) == 0
+    draft = lambda dw=ctypes.byref(d), B=32, K=3, z0=FAKE, out=FAKE, n=ws: lib.moev_draft(
+        ctypes.byref(m), dw, z0, FAKE, B, K, out, None, FAKE, n, None)
+    assert draft(dw=None) == INVALID
+    assert draft(K=-1) == INVALID
+    assert draft(z0=None) == INVALID
+    assert draft(out=None) == INVALID
+    assert draft(n=ws - 1) == WORKSPACE
+    assert draft(B=0) == OK and draft(K=0) == OK         # nothing to do
+    d.w_up = None
+    assert draft() == INVALID and "w_up" in _err(lib)
+    d.w_up = FAKE
+    d.n_slices = 17
+    assert draft() == UNSUPPORTED
+    d.n_slices = 8
+    step = lambda K=3, nt=FAKE, n=spec: lib.moev_spec_step(
+        ctypes.byref(m), ctypes.byref(d), FAKE, 32, K, FAKE, FAKE, FAKE, None, nt, None, FAKE, n, None)
+    assert step(K=0) == INVALID                         # a speculative step drafts at least one token
+    assert step(nt=None) == INVALID
+    assert step(n=spec - 1) == WORKSPACE
+    m.hidden = 1300
+    assert step() == UNSUPPORTED
