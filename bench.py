@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="verify_step_b32k3",
                     help="verify_step_b32k{3,2,1,0} | zipf_verify_b{1,8,32,128}k{1,3} | decode_layer_t128 | "
-                         "prefill_layer_t9760 | prefill_model_t9760 | kselect_b32")
+                         "prefill_layer_t9760 | prefill_model_t9760 | kselect_b32 | spec_loop_b32k3")
     ap.add_argument("--launch", choices=("auto", "eager", "graph"), default="auto")
     ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -343,6 +343,135 @@ def run_kselect(args, torch, np):
     }
 
 
+def draft_step_bytes(H: int, I: int, n: int, V: int, B: int, es: int = 2) -> int:
+    """One draft step: the input projection [H, 2H], the dense SwiGLU of width
+    n*I (three matrices), the LM head, the B hidden rows in and out, and the
+    B embedding rows read."""
+    return 2 * H * H * es + 3 * n * I * H * es + V * H * es + B * H * (4 + 4 + es)
+
+
+def run_spec(args, torch, np):
+    """The whole speculative loop on the device: each moev_spec_step verifies
+    the previous call's tokens and drafts the next K with the FastMTP draft
+    block, so a chain of calls runs without the host.  Chunks of chained
+    steps are captured as HIP graphs.  The draft block's weights are seeded
+    and untrained, so its drafts are rarely accepted: this measures the cost
+    of a speculative step (verify + K draft steps), and the committed stream
+    is checked against the GPU's own greedy rollout (lossless)."""
+    import synth
+    from moe_decoder_greedy_amd import model as mdl
+    B, K = 32, 3
+    shape = synth.DECODER
+    H, I, V = shape.hidden, shape.inter, shape.vocab
+    n_sl = shape.top_k + shape.n_shared
+    T = B * (K + 1)
+    weights = synth.model_weights(shape)
+    dm = mdl.DeviceModel(weights)
+    dm.attach_draft(synth.draft_weights(shape))
+    torch.cuda.synchronize()
+    n_steps = args.warmup + args.steps
+    last0 = synth.initial_tokens(B, V)
+    start = np.concatenate([last0[:, None], synth.counter_randint(V, 6, 0, np.arange(B * K)).reshape(B, K)],
+                           axis=1).astype(np.int32)
+    start_d = torch.from_numpy(start).cuda()
+
+    # eager chain: every step's outputs kept for the losslessness check
+    outs = [dm.alloc_spec_outputs(B, K) for _ in range(n_steps)]
+    for s in range(n_steps):
+        dm.spec_step(start_d if s == 0 else outs[s - 1]["next_tokens"], out=outs[s])
+    torch.cuda.synchronize()
+    commits = [[] for _ in range(B)]
+    for o in outs:
+        c, ln = o["commit"].cpu().numpy(), o["commit_len"].cpu().numpy()
+        for b in range(B):
+            commits[b].extend(c[b, :ln[b]].tolist())
+    n_com = min(len(c) for c in commits)
+    cur = torch.from_numpy(last0).cuda()
+    roll = []
+    for _ in range(n_com):
+        cur = dm.greedy(cur)
+        roll.append(cur)
+    roll = torch.stack(roll, 1).cpu().numpy()
+    lossless = all(commits[b][:n_com] == roll[b].tolist() for b in range(B))
+    committed = sum(len(c) for c in commits) / n_steps      # per step, all sequences
+    log(f"eager chain of {n_steps} speculative steps, lossless vs greedy rollout: {lossless}, "
+        f"tau {committed / B:.3f}")
+
+    # timed: chunks of chained steps as HIP graphs; the next chunk starts from
+    # the last step's next_tokens (copied between replays)
+    chunk = max(1, min(args.graph_chunk, args.steps))
+    tok_static = start_d.clone()
+    gouts = [dm.alloc_spec_outputs(B, K) for _ in range(chunk)]
+
+    def chain():
+        for i in range(chunk):
+            dm.spec_step(tok_static if i == 0 else gouts[i - 1]["next_tokens"], out=gouts[i])
+
+    chain()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain()
+    tok_static.copy_(start_d)
+    n_rep_w = max(1, args.warmup // chunk)
+    n_rep = max(1, args.steps // chunk)
+    for _ in range(n_rep_w):
+        g.replay()
+        tok_static.copy_(gouts[-1]["next_tokens"])
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    for _ in range(n_rep):
+        g.replay()
+        tok_static.copy_(gouts[-1]["next_tokens"])
+    torch.cuda.synchronize()
+    t_spec = (time.perf_counter() - ta) / (n_rep * chunk)
+    del g
+
+    # the draft block alone (K steps for B rows) and the verify step alone
+    z0 = torch.from_numpy(synth.draft_states(shape, B)).cuda()
+    t0 = outs[-1]["next_tokens"][:, 0].contiguous()
+    dbuf = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(3):
+        dm.draft(z0, t0, K, drafts=dbuf)
+    ev[0].record()
+    for _ in range(args.steps):
+        dm.draft(z0, t0, K, drafts=dbuf)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_draft = ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
+    vout = dm.alloc_outputs(B, K)
+    for _ in range(3):
+        dm.verify_step(start_d, out=vout)
+    ev[0].record()
+    for _ in range(args.steps):
+        dm.verify_step(start_d, out=vout)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_verify = ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
+    d_bytes = K * draft_step_bytes(H, I, n_sl, V, B)
+    d_gbs = d_bytes / t_draft / 1e9
+    log(f"spec step {t_spec * 1e3:.3f} ms (graph), verify alone {t_verify * 1e3:.3f} ms, "
+        f"draft alone {t_draft * 1e3:.3f} ms ({d_gbs:.0f} GB/s)")
+    return {
+        "metric": "verified tokens/s per speculative step (verify + on-device FastMTP draft, 32 seq x K=3)",
+        "value": round(T / t_spec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": n_rep * chunk,
+        "warmup": n_rep_w * chunk, "ms_per_step": round(t_spec * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dm.dtype,
+        "data": "synthetic (seeded N(0,0.02) bf16 weights; untrained seeded draft block)",
+        "config": {"workload": "spec_loop_b32k3", "batch": B, "drafts": K, "layers": shape.n_layers,
+                   "vocab": V, "draft_width": n_sl * I, "graph_steps_per_replay": chunk},
+        "committed_tokens_per_s": round(committed / t_spec, 1), "tau": round(committed / B, 4),
+        "lossless_commits": bool(lossless),
+        "ms_verify_alone": round(t_verify * 1e3, 4), "ms_draft_alone": round(t_draft * 1e3, 4),
+        "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(d_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "draft block, K steps (moev_draft)", "bytes_per_launch": int(d_bytes),
+                     "avg_launch_us": round(t_draft * 1e6, 2)},
+        "cpu_baseline": None,
+    }
+
+
 def run_verify(args, torch, np):
     import synth
     from moe_decoder_greedy_amd import model as mdl
@@ -612,6 +741,8 @@ def main():
         copy_probe(torch, args.copy_probe_mib)
     if args.workload == "kselect_b32":
         result = run_kselect(args, torch, np)
+    elif args.workload == "spec_loop_b32k3":
+        result = run_spec(args, torch, np)
     elif args.workload == "prefill_model_t9760":
         result = run_prefill_model(args, torch, np)
     elif args.workload.endswith(("_t128", "_t9760")):
