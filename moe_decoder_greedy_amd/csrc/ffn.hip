@@ -486,13 +486,26 @@ template <typename WT, int BT> struct TileCfg {
   static constexpr int kFrags = 16 + kXFrags;                            // per K block
   static constexpr int kFragBytes = 512 * static_cast<int>(sizeof(WT));  // 16 x 32 operand block
   static constexpr int kDma = kFragBytes / 1024;                         // 16-B loads per lane
-  static constexpr int kStageBytes = kFrags * kFragBytes;
+  // Token pairs (bf16, BT = 256).  A bf16 token row holds 64 B of one 32-wide
+  // K block, half a 128-byte line.  With kXPair the token rows are staged two
+  // K blocks at a time in a ring of two regions of their own, so that every
+  // token load instruction reads 8 rows x 128 B, whole lines, while the
+  // weight fragments keep their ring of kStages single-block stages (see
+  // tile_gemm).
+  static constexpr bool kXPair = sizeof(WT) == 2 && BT == 256;
+  static constexpr int kStageBytes = (kXPair ? 16 : kFrags) * kFragBytes;
+  static constexpr int kXRegionBytes = kXPair ? BT * 128 : 0;
   static constexpr int kWPerWave = 16 / kWaves;                          // fragments each wave loads
   static constexpr int kXPerWave = kXFrags / kWaves;
+  // loads per lane: weight fragments per K block; token rows per K block,
+  // or per pair of K blocks with kXPair
+  static constexpr int kWLoads = kWPerWave * kDma;
+  static constexpr int kXLoads = kXPair ? BT / 8 / kWaves : kXPerWave * kDma;
   // LDS: 160 KB per CU.  bf16 with BT = 128 keeps two workgroups per CU.
   static constexpr int kStages = sizeof(WT) == 4 ? 2 : (BT == 256 ? 4 : 3);
   static constexpr int kPerCu = (BT == 128 && sizeof(WT) == 2) ? 2 : 1;
-  static_assert(kStages * kStageBytes * kPerCu <= 160 * 1024, "LDS budget");
+  static_assert((kStages * kStageBytes + 2 * kXRegionBytes) * kPerCu <= 160 * 1024, "LDS budget");
+  static_assert(!kXPair || (kDma == 1 && kStages == 4), "token pairs: bf16, four weight stages");
 };
 
 typedef const void __attribute__((address_space(1)))* gptr_t;
@@ -525,6 +538,16 @@ template <typename WT, int BT, int U> __device__ __forceinline__ unsigned char* 
   else if constexpr (U == 1) return s1;
   else if constexpr (U == 2) return s2;
   else return s3;
+}
+
+// The two token regions of the kXPair layout.
+template <typename WT, int BT, int P> __device__ __forceinline__ unsigned char* tile_xregion() {
+  constexpr int B = TileCfg<WT, BT>::kXRegionBytes > 0 ? TileCfg<WT, BT>::kXRegionBytes : 16;
+  __shared__ __attribute__((aligned(1024))) unsigned char x0[B];
+  __shared__ __attribute__((aligned(1024))) unsigned char x1[B];
+  static_assert(P == 0 || P == 1, "two token regions");
+  if constexpr (P == 0) return x0;
+  else return x1;
 }
 
 template <typename WT, int MODE, int BT>
@@ -602,6 +625,7 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   const int K = a.K;
   const int nkb = K / 32;
   const int last = nkb - 1;
+  const int last_pair = nkb / 2 - 1;  // kXPair: K is a multiple of 64
 
   // the current tile: group, column tile, first token, token count, row base
   int g = 0, ct = 0, m0 = 0, mp = 0, off = 0;
@@ -610,8 +634,17 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   // repeat its last row: MFMA output columns depend on their own token row
   // only, the epilogue drops those columns, and unconditional loads keep the
   // wait counts exact.
+  //
+  // Token pairs (kXPair): load instruction i (0..BT/8-1) of a pair covers
+  // tokens 8i..8i+7 and the pair's 64 K values, 128 B per row.  Lane L
+  // fetches row r = L / 8, 16-byte chunk c = (L % 8) ^ r ^ (i % 2), and the
+  // load writes it to slot L of the instruction's 1 KB in LDS: slot
+  // r*8 + (c ^ r ^ (i % 2)) holds (token 8i + r, chunk c).  A fragment read of
+  // the pair's K block s (chunks 4s..4s+3) then has its 16 lanes of one chunk
+  // on 16 distinct 16-byte bank groups.
+  constexpr int kXPtr = TC::kXPair ? TC::kXLoads : TC::kXPerWave;
   const WT* wsrc[TC::kWPerWave];
-  const WT* xsrc[TC::kXPerWave];
+  const WT* xsrc[kXPtr];
   auto setup = [&](int buf) {
     g = tile_info[buf][0];
     ct = tile_info[buf][1];
@@ -636,15 +669,42 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
       }
       wsrc[i] = base + static_cast<long long>(g) * a.w_group + static_cast<long long>(t) * nkb * 512 + lane * 8;
     }
+    if constexpr (TC::kXPair) {
 #pragma unroll
-    for (int i = 0; i < TC::kXPerWave; ++i) {
-      const int row = min((wave * TC::kXPerWave + i) * 16 + r16, mp - 1);
-      xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, off, m0, row) * K + q * 8;
+      for (int i = 0; i < kXPtr; ++i) {
+        const int ii = wave * kXPtr + i;  // load instruction of the pair
+        const int r = lane >> 3;
+        const int row = min(ii * 8 + r, mp - 1);
+        const int c = (lane & 7) ^ r ^ (ii & 1);
+        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, off, m0, row) * K + c * 8;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kXPtr; ++i) {
+        const int row = min((wave * TC::kXPerWave + i) * 16 + r16, mp - 1);
+        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, off, m0, row) * K + q * 8;
+      }
     }
   };
+  // token pair pr (K blocks 2pr, 2pr+1) into region P (kXPair)
+  auto issue_x = [&](auto P, int pr) __attribute__((always_inline)) {
+    unsigned char* xr = tile_xregion<WT, BT, decltype(P)::value>();
+#pragma unroll
+    for (int i = 0; i < kXPtr; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(xsrc[i] + pr * 64), (lptr_t)(xr + (wave * kXPtr + i) * 1024), 16,
+                                       0, 0);
+  };
   // K block kb into stage U: for each fragment, kDma loads of 16 B per lane
+  // (the weights only with kXPair)
   auto issue = [&](auto U, int kb) __attribute__((always_inline)) {
     unsigned char* st = tile_stage<WT, BT, decltype(U)::value>();
+    if constexpr (TC::kXPair) {
+#pragma unroll
+      for (int i = 0; i < TC::kWPerWave; ++i)
+        __builtin_amdgcn_global_load_lds((gptr_t)(wsrc[i] + kb * 512),
+                                         (lptr_t)(st + (wave * TC::kWPerWave + i) * kFB), 16, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < TC::kDma; ++h) {
 #pragma unroll
@@ -658,11 +718,24 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
                                          0, 0);
     }
   };
-  constexpr int kLoads = (TC::kWPerWave + TC::kXPerWave) * TC::kDma;  // loads per lane per block
-  // blocks 0 .. kNS-2 of the tile set up last (clamped: K may hold fewer)
+  // loads per lane per block (without kXPair)
+  constexpr int kLoads = TC::kWLoads + TC::kXLoads;
+  // blocks 0 .. kNS-2 of the tile set up last (clamped: K may hold fewer);
+  // with kXPair the first token pair goes first
   auto prologue = [&]() __attribute__((always_inline)) {
+    if constexpr (TC::kXPair) issue_x(std::integral_constant<int, 0>{}, 0);
     static_for<kNS - 1>([&](auto U) __attribute__((always_inline)) { issue(U, min(decltype(U)::value, last)); });
   };
+  // Wait counts (loads complete in order).  Without kXPair: block kb + 1 has
+  // landed once at most the kNS - 2 newer blocks' loads are outstanding.  With
+  // kXPair, iteration kb requests weight block kb + 3 and, for even kb, token
+  // pair kb/2 + 1; at its end block kb + 1 needs weight block kb + 1 (three
+  // iterations old) and token pair (kb + 1)/2 (requested at iteration
+  // kb - 2 for odd kb + 1, at kb - 1 for even kb + 1): even kb may leave its
+  // own and iteration kb - 1's requests outstanding, odd kb only its own.
+  constexpr int kWaitTop = TC::kXPair ? (kNS - 2) * TC::kWLoads : (kNS - 2) * kLoads;
+  constexpr int kWaitEven = TC::kXPair ? 2 * TC::kWLoads + TC::kXLoads : (kNS - 2) * kLoads;
+  constexpr int kWaitOdd = TC::kXPair ? TC::kWLoads : (kNS - 2) * kLoads;
 
   const int wr = wave / kNWT;  // weight half
   const int wt = wave % kNWT;  // token quarter (BT = 256) or half (BT = 128)
@@ -676,25 +749,49 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
     }
   };
 
+  // kXPair: this lane's byte offsets, in a token region, of its fragments of
+  // the pair's K block s (token column wt*64 + j*16 + r16 sits at + j * 2048)
+  int xoff[2];
+  if constexpr (TC::kXPair) {
+    const int h = (lane >> 3) & 1, r = lane & 7;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) xoff[s] = (wt * 8 + h) * 1024 + (r * 8 + ((s * 4 + q) ^ r ^ h)) * 16;
+  }
+
   f32x4 acc[8][4];
-  // Block kb sits in stage kb % kNS.  Iteration kb requests block
-  // kb + kNS - 1 into the stage read in the previous iteration, multiplies
-  // block kb, then waits until block kb + 1 has landed (its loads and those
-  // of every other wave: the barrier).
+  // Block kb sits in stage kb % kNS (its token rows, with kXPair, in region
+  // (kb / 2) % 2).  Iteration kb requests block kb + kNS - 1 into the stage
+  // read in the previous iteration (and, for even kb with kXPair, token pair
+  // kb/2 + 1 into the region the previous pair used), multiplies block kb,
+  // then waits until block kb + 1 has landed (its loads and those of every
+  // other wave: the barrier).  Iterations run in groups of kNS from a
+  // multiple of kNS, so kb % kNS = U and, with kXPair, kb % 2 = U % 2 and
+  // (kb / 2) % 2 = U / 2.
   auto iteration = [&](auto U, int kb) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
     issue(std::integral_constant<int, (u + kNS - 1) % kNS>{}, min(kb + kNS - 1, last));
+    if constexpr (TC::kXPair && u % 2 == 0)
+      issue_x(std::integral_constant<int, (u / 2 + 1) % 2>{}, min(kb / 2 + 1, last_pair));
+    // Keep the requests at the top of the iteration: the scheduler would
+    // otherwise sink them to the wait at its end.
+    __builtin_amdgcn_sched_barrier(0);
     const unsigned char* st = tile_stage<WT, BT, u>();
     Frag<WT> A[8], B[4];
+    if constexpr (TC::kXPair) {
+      const unsigned char* xr = tile_xregion<WT, BT, (u / 2) % 2>();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) frag(st, 16 + wt * 4 + j, B[j]);
+      for (int j = 0; j < 4; ++j) B[j].v = *reinterpret_cast<const bf16x8*>(xr + xoff[u % 2] + j * 2048);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) frag(st, 16 + wt * 4 + j, B[j]);
+    }
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt) frag(st, wr * 8 + rt, A[rt]);
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[rt][j] = mma(A[rt], B[j], acc[rt][j]);
-    stage_barrier<(kNS - 2) * kLoads>();
+    stage_barrier<(u % 2 == 0) ? kWaitEven : kWaitOdd>();
   };
 
   lookup(tile, 0);
@@ -706,7 +803,7 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
     // Stage 0 of this tile has landed.  After an epilogue its stores are
     // newer than the prologue's loads, so this waits for them too: correct,
     // a little early.
-    stage_barrier<(kNS - 2) * kLoads>();
+    stage_barrier<kWaitTop>();
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -853,7 +950,7 @@ int tile_grid(int T, int k, int ns, int E, int n_ctiles, int BT, int per_cu) {
 // padding in ragged last tiles below that).
 template <typename WT, int MODE>
 void launch_tile(const GemmArgs& args, int n_ctiles, int G, int E, int k, int ns, hipStream_t s) {
-  if (static_cast<long long>(args.T) * k >= 384LL * E) {
+  if (static_cast<long long>(args.T) * k >= 384LL * E && (!TileCfg<WT, 256>::kXPair || args.K % 64 == 0)) {
     const int grid = tile_grid(args.T, k, ns, E, n_ctiles, 256, TileCfg<WT, 256>::kPerCu);
     tile_gemm<WT, MODE, 256><<<grid, TileCfg<WT, 256>::kThreads, 0, s>>>(args, n_ctiles, G);
   } else {
@@ -872,7 +969,7 @@ static_assert(tile_cols<kHead>() == 16 * kRtHead * kWavesHead, "head partial blo
 
 template <typename WT>
 void launch_tile_head(const GemmArgs& args, int n_ctiles, hipStream_t s) {
-  const int BT = args.T >= 512 ? 256 : 128;
+  const int BT = (args.T >= 512 && (!TileCfg<WT, 256>::kXPair || args.K % 64 == 0)) ? 256 : 128;
   long long n = std::min<long long>(static_cast<long long>(n_ctiles) * ((args.T + BT - 1) / BT),
                                     static_cast<long long>(cu_count()) * (BT == 256 ? TileCfg<WT, 256>::kPerCu
                                                                                     : TileCfg<WT, 128>::kPerCu));
