@@ -195,6 +195,34 @@ def test_grouped_ffn_prefill_sampled(ops, dec_layer):
     assert e < 1e-3
 
 
+def test_grouped_ffn_tile_remainder(ops):
+    """The 256-token tile schedule on a shape whose contraction length is not a
+    multiple of four K blocks (H = 320: ten 32-wide blocks, so the token-pair
+    ring ends on a partial group of iterations) with ragged last tiles in
+    every group: against the oracle, and bit for bit against the streaming
+    schedule (a 400-token call) on the first 400 tokens."""
+    shape = dataclasses.replace(synth.DECODER, name="tile_remainder", hidden=320, n_routed=8, top_k=2,
+                                n_shared=1, inter=128, n_layers=1)
+    L = synth.model_weights(shape, head=False)["layers"][0]
+    dt, T = "bf16", 2000          # T * k = 4000 >= 384 * E: 256-token tiles
+    report("grouped_ffn_tile_remainder", T=T, H=shape.hidden)
+    x_op, idx, w32, off, src = _ffn_case(shape, L, dt, T, seed=23)
+    wg, wu, wd = (ops.pack_weights(dev_bits(L[key], dt)) for key in ("w_gate", "w_up", "w_down"))
+    y = host(ops.moe_grouped_ffn(dev_operand(x_op, dt), dev_i32(src), dev_i32(off), dev_f32(w32), wg, wu, wd,
+                                 shape.n_routed, shape.top_k, shape.n_shared))
+    args = (x_op, src, off, w32, L["w_gate"], L["w_up"], L["w_down"], dt, shape.top_k, shape.n_shared)
+    e_tight = max_abs(y, oracle.grouped_ffn(*args, round_act=True))
+    e_exact = max_abs(y, oracle.grouped_ffn(*args, round_act=False))
+    report("grouped_ffn_tile_remainder", err_vs_bf16_operands=e_tight, err_vs_exact=e_exact)
+    assert e_exact < BAR[dt]
+    assert e_tight < 1e-3
+    Ts = 400                      # T <= 512: the streaming schedule
+    off_s, src_s = oracle.permute(idx[:Ts], shape.n_routed, shape.n_shared)
+    y_s = host(ops.moe_grouped_ffn(dev_operand(x_op[:Ts], dt), dev_i32(src_s), dev_i32(off_s), dev_f32(w32[:Ts]),
+                                   wg, wu, wd, shape.n_routed, shape.top_k, shape.n_shared))
+    assert np.array_equal(y_s.view(np.uint32), y[:Ts].view(np.uint32))
+
+
 # ------------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("T,S,H", [(128, 8, 1280), (37, 3, 128), (1, 1, 64)])
@@ -223,7 +251,7 @@ def _head_case(V, H, dt, seed, std=0.02):
 
 @pytest.mark.parametrize("V,H,T,dt", [(512, 128, 16, "f32"), (129280, 1280, 128, "bf16"),
                                       (1000, 256, 37, "bf16"), (129280, 1280, 1, "bf16"),
-                                      (77, 64, 300, "f32")])
+                                      (77, 64, 300, "f32"), (1000, 320, 600, "bf16")])
 def test_lmhead(ops, V, H, T, dt):
     report("lmhead", V=V, H=H, T=T, dt=dt)
     w_lm = _head_case(V, H, dt, seed=V + T)
