@@ -101,8 +101,15 @@ struct RouteArgs {
 // COMBINE: phase 0 first adds the previous layer's expert slots to the
 // residual (the same left-to-right slot order as the combine kernel, so the
 // bits are identical) and writes the new residual.
-template <typename WT, int NCH, bool COMBINE, int kRouteTPB>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
+// PRELOAD: the router rows are fetched into registers before phase 0 (as
+// fp32), so that fetch overlaps it; without PRELOAD each chunk of them is
+// fetched (as raw bf16 / fp32) inside the logit loop, which keeps the block
+// small enough for two per CU (8 waves per SIMD: the second launch bound):
+// while one block computes logits, the other
+// streams its residual rows and expert slots.  The arithmetic of every logit
+// is the same either way.
+template <typename WT, int NCH, bool COMBINE, int kRouteTPB, bool PRELOAD>
+__global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(RouteArgs a) {
   extern __shared__ float smem[];
   const int H = a.H, E = a.E, k = a.k, T = a.T;
   const WT* __restrict__ wr = static_cast<const WT*>(a.wr);
@@ -119,14 +126,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   // router rows of this wave's experts, fetched before anything else so the
   // fetch overlaps the RMSNorm phase
   const int e0 = wave * kExpertsPerWave;
-  float4 wv[kExpertsPerWave][NCH];
+  float4 wv[kExpertsPerWave][PRELOAD ? NCH : 1];
+  if constexpr (PRELOAD) {
 #pragma unroll
-  for (int u = 0; u < kExpertsPerWave; ++u) {
-    const int e = min(e0 + u, E - 1);
+    for (int u = 0; u < kExpertsPerWave; ++u) {
+      const int e = min(e0 + u, E - 1);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int i = min(lane * 4 + c * 256, H - 4);
-      wv[u][c] = Vec4<WT>::load(wr + static_cast<size_t>(e) * H + i);
+      for (int c = 0; c < NCH; ++c) {
+        const int i = min(lane * 4 + c * 256, H - 4);
+        wv[u][c] = Vec4<WT>::load(wr + static_cast<size_t>(e) * H + i);
+      }
     }
   }
 
@@ -150,19 +159,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
       float4 v = *reinterpret_cast<const float4*>(a.h + t * H + i);
       if (COMBINE) {
         const float4* ys = reinterpret_cast<const float4*>(a.y + t * a.S * H + i);
-        float4 sv[kMaxSlots];
+        float4 acc;
+        if constexpr (PRELOAD) {
+          float4 sv[kMaxSlots];
 #pragma unroll
-        for (int sl = 0; sl < kMaxSlots; ++sl)
-          if (sl < a.S) sv[sl] = ys[static_cast<size_t>(sl) * h4];
-        float4 acc = sv[0];
+          for (int sl = 0; sl < kMaxSlots; ++sl)
+            if (sl < a.S) sv[sl] = ys[static_cast<size_t>(sl) * h4];
+          acc = sv[0];
 #pragma unroll
-        for (int sl = 1; sl < kMaxSlots; ++sl)
-          if (sl < a.S) {
-            acc.x += sv[sl].x;
-            acc.y += sv[sl].y;
-            acc.z += sv[sl].z;
-            acc.w += sv[sl].w;
-          }
+          for (int sl = 1; sl < kMaxSlots; ++sl)
+            if (sl < a.S) {
+              acc.x += sv[sl].x;
+              acc.y += sv[sl].y;
+              acc.z += sv[sl].z;
+              acc.w += sv[sl].w;
+            }
+        } else {  // the same left-to-right sum, each slot added as it arrives
+          acc = ys[0];
+#pragma unroll
+          for (int sl = 1; sl < kMaxSlots; ++sl)
+            if (sl < a.S) {
+              const float4 yv = ys[static_cast<size_t>(sl) * h4];
+              acc.x += yv.x;
+              acc.y += yv.y;
+              acc.z += yv.z;
+              acc.w += yv.w;
+            }
+        }
         v = make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
         *reinterpret_cast<float4*>(a.h_out + t * H + i) = v;
       }
@@ -219,12 +242,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
       for (int c = 0; c < NCH; ++c) {
         const int i = lane * 4 + c * 256;
         if (i < H) {
+          const int cw = PRELOAD ? c : 0;
+          if constexpr (!PRELOAD) {
+#pragma unroll
+            for (int u = 0; u < kExpertsPerWave; ++u)
+              wv[u][0] = Vec4<WT>::load(wr + static_cast<size_t>(min(e0 + u, E - 1)) * H + i);
+          }
 #pragma unroll
           for (int tt = 0; tt < kRouteGroup; ++tt) {
             const float4 x = *reinterpret_cast<const float4*>(xs + (t1 + tt) * H + i);
 #pragma unroll
             for (int u = 0; u < kExpertsPerWave; ++u)
-              acc[u][tt] += x.x * wv[u][c].x + x.y * wv[u][c].y + x.z * wv[u][c].z + x.w * wv[u][c].w;
+              acc[u][tt] += x.x * wv[u][cw].x + x.y * wv[u][cw].y + x.z * wv[u][cw].z + x.w * wv[u][cw].w;
           }
         }
       }
@@ -280,11 +309,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 
 }
 
-template <typename WT, bool COMBINE, int TPB>
+template <typename WT, bool COMBINE, int TPB, bool PRELOAD>
 void launch_route_t(int nch, dim3 grid, size_t lds, hipStream_t s, const RouteArgs& a) {
 #define MOEV_ROUTE_CASE(N)                                                               \
   case N:                                                                                \
-    route_kernel<WT, N, COMBINE, TPB><<<grid, kRouteThreads, lds, s>>>(a);                \
+    route_kernel<WT, N, COMBINE, TPB, PRELOAD><<<grid, kRouteThreads, lds, s>>>(a);       \
     break;
   switch (nch) {
     MOEV_ROUTE_CASE(1) MOEV_ROUTE_CASE(2) MOEV_ROUTE_CASE(3) MOEV_ROUTE_CASE(4)
@@ -296,23 +325,24 @@ void launch_route_t(int nch, dim3 grid, size_t lds, hipStream_t s, const RouteAr
 #undef MOEV_ROUTE_CASE
 }
 
-template <typename WT, int TPB>
+template <typename WT, int TPB, bool PRELOAD>
 void launch_route_tpb(const RouteArgs& a, hipStream_t s) {
   const dim3 grid((a.T + TPB - 1) / TPB);
   const size_t lds = (static_cast<size_t>(TPB) * a.H + 3 * TPB * 64) * sizeof(float);
   const int nch = (a.H + 255) / 256;
-  if (a.y != nullptr) launch_route_t<WT, true, TPB>(nch, grid, lds, s, a);
-  else launch_route_t<WT, false, TPB>(nch, grid, lds, s, a);
+  if (a.y != nullptr) launch_route_t<WT, true, TPB, PRELOAD>(nch, grid, lds, s, a);
+  else launch_route_t<WT, false, TPB, PRELOAD>(nch, grid, lds, s, a);
 }
 
-// Tokens per block: 1 for decode-sized batches (more blocks in flight), 16
-// once there are enough tokens to fill the GPU that way (and their LDS copy
-// fits), else 4.
+// Tokens per block: 1 for decode-sized batches (more blocks in flight, router
+// rows preloaded), 4 for mid-sized ones, and 8 once there are enough tokens
+// to fill the GPU with two blocks per CU (router rows fetched per chunk; the
+// LDS copy of 8 rows fits twice).
 template <typename WT>
 void launch_route_dispatch(const RouteArgs& a, hipStream_t s) {
-  if (a.T >= 2048 && a.H <= 2048) launch_route_tpb<WT, 16>(a, s);
-  else if (a.T > 256) launch_route_tpb<WT, 4>(a, s);
-  else launch_route_tpb<WT, 1>(a, s);
+  if (a.T >= 2048 && a.H <= 2048) launch_route_tpb<WT, 8, false>(a, s);
+  else if (a.T > 256) launch_route_tpb<WT, 4, true>(a, s);
+  else launch_route_tpb<WT, 1, true>(a, s);
 }
 
 moev_status check_hidden(int H) {
