@@ -14,8 +14,10 @@
 // projection is the down GEMM over 2 groups (the z half and the embedding half
 // of W_p, each holding every row, weight 1), summed in group order; the dense
 // SwiGLU of width n*I is the grouped FFN over its n intermediate slices, each
-// holding every row, again summed in slice order.  That sum order is fixed,
-// so a row's draft does not depend on the batch.  Per step: one input kernel,
+// holding every row, again summed in slice order.  These GEMMs span only 2 or
+// n groups, so each runs split K (a workgroup's four waves take a quarter of
+// the contraction each and add in wave order).  Every sum order is fixed, so
+// a row's draft does not depend on the batch.  Per step: one input kernel,
 // the projection GEMM, one norm kernel (z' and x), gate/up, down, and the LM
 // head, whose norm kernel also forms z_j = z' + the slice sum.
 #include "launch.h"
@@ -206,10 +208,11 @@ void run_draft(const moev_model& m, const moev_draft_weights& d, const float* z_
     if (dt == MOEV_BF16) draft_in_kernel<u16><<<B, kDraftThreads, 0, s>>>(a);
     else draft_in_kernel<float><<<B, kDraftThreads, 0, s>>>(a);
     // z' = W_p[:, :H] u_z + W_p[:, H:] u_e: two groups of K = H, weight 1
-    launch_ffn_down_lists(x2, lists_p, counts_p, nullptr, d.w_proj, B, H, H, 0, 0, 2, dt, yp, s);
+    // (these GEMMs cover 2 or n groups only: split K fills the GPU)
+    launch_ffn_down_lists(x2, lists_p, counts_p, nullptr, d.w_proj, B, H, H, 0, 0, 2, dt, yp, s, true);
     launch_norm_cast(nullptr, yp, 2, d.norm_ffn, m.eps, B, H, dt, xf, zp, s);
-    launch_ffn_gate_up_lists(xf, lists_f, counts_f, d.w_gate, d.w_up, B, H, I, 0, 0, n, dt, act, s);
-    launch_ffn_down_lists(act, lists_f, counts_f, nullptr, d.w_down, B, H, I, 0, 0, n, dt, yf, s);
+    launch_ffn_gate_up_lists(xf, lists_f, counts_f, d.w_gate, d.w_up, B, H, I, 0, 0, n, dt, act, s, true);
+    launch_ffn_down_lists(act, lists_f, counts_f, nullptr, d.w_down, B, H, I, 0, 0, n, dt, yf, s, true);
     float* zj = (j == K - 1 && z_out != nullptr) ? z_out : zb[j & 1];
     launch_lmhead(zp, d.norm_out, m.eps, m.w_lm, B, H, m.vocab, dt, out + out_col0 + j, nullptr,
                   nullptr, ws + L.head, s, yf, n, zj, out_stride);

@@ -230,16 +230,26 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, unsigned char* __res
 // Direct pass (mp <= 16 * NTX <= 32): both fragments come from global memory
 // through one register ring kNBD K blocks deep; no LDS, no barriers.  Token
 // rows past mp read row 0 of the pass and are dropped by the epilogue.
-template <typename WT, int MODE, int RT, int MT, int NTX, int W>
+//
+// KS > 1 (split K): the workgroup's KS = W waves share one row tile, wave w
+// takes K blocks [w*nkb/KS, (w+1)*nkb/KS) in order, and wave 0 adds the
+// other waves' partial sums (w = 1, 2, ... in turn, through LDS) before its
+// epilogue.  The sum order is fixed, so a token's result does not depend on
+// its pass companions; it differs in rounding from the single-chain order
+// of KS = 1, so a caller uses one KS for all its sizes.
+template <typename WT, int MODE, int RT, int MT, int NTX, int W, int KS = 1>
 __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned char* __restrict__ lds,
                                                  int off, int m0, int mp,
                                                  const WT* const (&wp)[RT],
                                                  const int (&rowbase)[RT]) {
+  static_assert(KS == 1 || (KS == W && MODE != kHead), "split K: one K range per wave, expert GEMMs");
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int q = lane >> 4;
   const int K = a.K;
-  const int nkb = K / 32;
+  const int wave = threadIdx.x >> 6;
+  const int kb_lo = KS > 1 ? wave * (K / 32) / KS : 0;
+  const int nkb = KS > 1 ? (wave + 1) * (K / 32) / KS : K / 32;  // end of this wave's range
   const WT* __restrict__ xsrc = static_cast<const WT*>(a.x);
   const WT* xp[NTX];
 #pragma unroll
@@ -256,13 +266,13 @@ __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned cha
   Frag<WT> rw[kNBD][RT], rx[kNBD][NTX];
 #pragma unroll
   for (int u = 0; u < kNBD; ++u)
-    if (u < nkb) {
+    if (kb_lo + u < nkb) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) rw[u][rt].load(wp[rt] + u * kFrag);
+      for (int rt = 0; rt < RT; ++rt) rw[u][rt].load(wp[rt] + (kb_lo + u) * kFrag);
 #pragma unroll
-      for (int j = 0; j < NTX; ++j) rx[u][j].load(xp[j] + u * 32);
+      for (int j = 0; j < NTX; ++j) rx[u][j].load(xp[j] + (kb_lo + u) * 32);
     }
-  for (int kb0 = 0; kb0 < nkb; kb0 += kNBD) {
+  for (int kb0 = kb_lo; kb0 < nkb; kb0 += kNBD) {
 #pragma unroll
     for (int u = 0; u < kNBD; ++u) {
       const int kb = kb0 + u;
@@ -280,7 +290,32 @@ __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned cha
       }
     }
   }
-  epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
+  if constexpr (KS > 1) {
+    __shared__ f32x4 red[KS - 1][RT][NTX][kWave];
+    if (wave > 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int j = 0; j < NTX; ++j) red[wave - 1][rt][j][lane] = acc[rt][j];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int j = 0; j < NTX; ++j) {
+            const f32x4 o = red[w][rt][j][lane];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[rt][j][v] += o[v];
+          }
+      epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
+    }
+    __syncthreads();  // red is free for the next pass
+  } else {
+    epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
+  }
 }
 
 // LDS-staged pass: mt = ceil(mp / 16) <= NTX column tiles.  NTX is a
@@ -375,8 +410,9 @@ __device__ __forceinline__ void gemm_pass_lds(const GemmArgs& a, unsigned char* 
   epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
 }
 
-template <typename WT, int MODE, int RT, int MT, int W>
+template <typename WT, int MODE, int RT, int MT, int W, int KS = 1>
 __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
+  static_assert(KS == 1 || MT == 32, "split K runs direct passes of at most 32 tokens");
   using C = Cfg<WT, MT>;
   constexpr int NT = C::kTiles;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::kLdsBytes];
@@ -407,12 +443,15 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
   const int ntiles = (a.N + 15) / 16;
 
   // this wave's weight tiles; lane pointer = its 16 bytes of the first fragment
+  // (split K: every wave of the workgroup has the same tiles)
   const WT* wp[RT];
   int rowbase[RT];
+  constexpr int kWaveTiles = KS > 1 ? 1 : W;  // row tiles (of 16 x RT rows) per workgroup
+  const int wt = KS > 1 ? 0 : wave;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int rb = (MODE == kGateUp) ? blockIdx.x * (16 * W) + wave * 16
-                                     : blockIdx.x * (16 * RT * W) + wave * (16 * RT) + rt * 16;
+    const int rb = (MODE == kGateUp) ? blockIdx.x * (16 * kWaveTiles) + wt * 16
+                                     : blockIdx.x * (16 * RT * kWaveTiles) + wt * (16 * RT) + rt * 16;
     rowbase[rt] = rb;
     const int tile = min(rb / 16, ntiles - 1);
     const WT* base = (MODE == kGateUp && rt == 1) ? w1 : w0;
@@ -424,9 +463,9 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
     const int mp = min(MT, M - m0);
     // the branches are uniform across the workgroup
     if (mp <= 16) {
-      gemm_pass_direct<WT, MODE, RT, MT, 1, W>(a, lds, off, m0, mp, wp, rowbase);
+      gemm_pass_direct<WT, MODE, RT, MT, 1, W, KS>(a, lds, off, m0, mp, wp, rowbase);
     } else if (mp <= 32) {
-      gemm_pass_direct<WT, MODE, RT, MT, 2, W>(a, lds, off, m0, mp, wp, rowbase);
+      gemm_pass_direct<WT, MODE, RT, MT, 2, W, KS>(a, lds, off, m0, mp, wp, rowbase);
     } else if constexpr (NT >= 4) {
       if (mp <= 64 || NT == 4)
         gemm_pass_lds<WT, MODE, RT, MT, 4, W>(a, lds, off, m0, mp, wp, rowbase);
@@ -1201,7 +1240,7 @@ void launch_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* 
 
 void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t* counts,
                               const void* w_gate, const void* w_up, int T, int H, int I, int E,
-                              int k, int ns, int dt, void* act, hipStream_t s) {
+                              int k, int ns, int dt, void* act, hipStream_t s, bool split_k) {
   GemmArgs up = ffn_args(list, nullptr, T, H, I, k, ns);
   up.counts = counts;
   up.w0 = w_gate;
@@ -1211,6 +1250,14 @@ void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t*
   up.K = H;
   up.x = x;
   up.out = act;
+  if (split_k) {
+    const dim3 grid(I / 16, E + ns);
+    if (dt == MOEV_BF16)
+      stream_gemm<u16, kGateUp, 2, 32, kWavesFfn, kWavesFfn><<<grid, kWavesFfn * 64, 0, s>>>(up);
+    else
+      stream_gemm<float, kGateUp, 2, 32, kWavesFfn, kWavesFfn><<<grid, kWavesFfn * 64, 0, s>>>(up);
+    return;
+  }
   const dim3 grid(I / (16 * kWavesFfn), E + ns);
   if (dt == MOEV_BF16)
     launch_gemm<u16, kGateUp, 2, kWavesFfn>(up, grid, s);
@@ -1220,7 +1267,7 @@ void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t*
 
 void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* counts,
                            const float* topk_w, const void* w_down, int T, int H, int I, int E,
-                           int k, int ns, int dt, float* y_slots, hipStream_t s) {
+                           int k, int ns, int dt, float* y_slots, hipStream_t s, bool split_k) {
   GemmArgs dn = ffn_args(list, nullptr, T, H, I, k, ns);
   dn.counts = counts;
   dn.w0 = w_down;
@@ -1230,6 +1277,14 @@ void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* 
   dn.x = act;
   dn.topk_w = topk_w;
   dn.out = y_slots;
+  if (split_k) {
+    const dim3 grid(H / (16 * kRtDown), E + ns);
+    if (dt == MOEV_BF16)
+      stream_gemm<u16, kDown, kRtDown, 32, kWavesFfn, kWavesFfn><<<grid, kWavesFfn * 64, 0, s>>>(dn);
+    else
+      stream_gemm<float, kDown, kRtDown, 32, kWavesFfn, kWavesFfn><<<grid, kWavesFfn * 64, 0, s>>>(dn);
+    return;
+  }
   const dim3 grid(H / (16 * kRtDown * kWavesFfn), E + ns);
   if (dt == MOEV_BF16)
     launch_gemm<u16, kDown, kRtDown, kWavesFfn>(dn, grid, s);

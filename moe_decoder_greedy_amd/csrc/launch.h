@@ -62,12 +62,17 @@ void run_draft(const moev_model& m, const moev_draft_weights& d, const float* z_
                hipStream_t s);
 
 // Expert GEMMs reading expert lists (T <= kListMaxTokens): act holds G*T rows.
+// split_k: each workgroup's waves split one row tile's K range (passes of at
+// most 32 tokens, every size): several times the workgroups for GEMMs over a
+// few groups, with rounding that differs from split_k = false, so a caller
+// keeps one setting.
 void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t* counts,
                               const void* w_gate, const void* w_up, int T, int H, int I, int E,
-                              int k, int ns, int dt, void* act, hipStream_t s);
+                              int k, int ns, int dt, void* act, hipStream_t s, bool split_k = false);
 void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* counts,
                            const float* topk_w, const void* w_down, int T, int H, int I, int E,
-                           int k, int ns, int dt, float* y_slots, hipStream_t s);
+                           int k, int ns, int dt, float* y_slots, hipStream_t s,
+                           bool split_k = false);
 void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
                     hipStream_t s);
 // out[i] = h[t] + the sum of y's S slots of row t (y may be NULL), t = the
