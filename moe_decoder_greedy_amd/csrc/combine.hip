@@ -52,10 +52,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const int32_t* __restrict__
   if (b >= B) return;
   const int32_t* tk = tokens + static_cast<long long>(b) * (K + 1);
   const int32_t* gr = greedy + static_cast<long long>(b) * (K + 1);
-  int n = 0;
-  while (n < K && tk[n + 1] == gr[n]) ++n;
-  int32_t* cm = commit + static_cast<long long>(b) * (K + 1);
-  for (int j = 0; j <= K; ++j) cm[j] = j < n ? tk[j + 1] : (j == n ? gr[n] : -1);
+  const int n = accept_prefix(tk, gr, K, commit + static_cast<long long>(b) * (K + 1));
   n_accept[b] = n;
   if (commit_len) commit_len[b] = n + 1;
   if (next_last) next_last[b] = gr[n];

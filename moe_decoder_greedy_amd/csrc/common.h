@@ -112,6 +112,19 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
+// Greedy prefix acceptance of one sequence ("The speed comes from three
+// layers working together", Jina-OCR-v1 explainer on kg.zhiyong.dev):
+// tk = (last committed token, d_1 .. d_K), gr = the main model's greedy token
+// at each of those K+1 positions.  n = the number of leading drafts with
+// d_j == gr[j-1]; cm (K+1 entries) receives d_1 .. d_n, then gr[n] (the
+// correction, or the extra token when n == K), then -1 padding.  Returns n.
+__device__ __forceinline__ int accept_prefix(const int32_t* tk, const int32_t* gr, int K, int32_t* cm) {
+  int n = 0;
+  while (n < K && tk[n + 1] == gr[n]) ++n;
+  for (int j = 0; j <= K; ++j) cm[j] = j < n ? tk[j + 1] : (j == n ? gr[n] : -1);
+  return n;
+}
+
 // ------------------------------------------------------------ MFMA fragments
 //
 // One 16x16 output tile accumulates over K in blocks of 32.  Lane l supplies

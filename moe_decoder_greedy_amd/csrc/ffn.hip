@@ -1137,6 +1137,44 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* __restri
   }
 }
 
+// One block per sequence: wave j reduces row b*(K+1) + j exactly as
+// argmax_reduce_kernel does, then one thread applies the prefix acceptance to
+// the sequence's K+1 greedy tokens (K + 1 <= 16).
+constexpr int kVerifyFuseMaxRows = 16;
+__global__ __launch_bounds__(64 * kVerifyFuseMaxRows) void argmax_verify_kernel(const float* __restrict__ pmax,
+                                                                              const int32_t* __restrict__ pidx,
+                                                                              int nblk,
+                                                                              int32_t* __restrict__ greedy,
+                                                                              VerifyFuse v) {
+  __shared__ int32_t tok_s[kVerifyFuseMaxRows];
+  __shared__ int32_t gr_s[kVerifyFuseMaxRows];
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int K1 = v.K + 1;
+  const long long t = static_cast<long long>(b) * K1 + wave;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int blk = lane; blk < nblk; blk += 64) {
+    const float val = pmax[t * nblk + blk];
+    const int i = pidx[t * nblk + blk];
+    if (better(val, i, best, bi)) { best = val; bi = i; }
+  }
+  wave_argmax(best, bi);
+  if (lane == 0) {
+    greedy[t] = bi;
+    gr_s[wave] = bi;
+    tok_s[wave] = v.tokens[t];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int n = accept_prefix(tok_s, gr_s, v.K, v.commit + static_cast<long long>(b) * K1);
+    v.n_accept[b] = n;
+    if (v.commit_len) v.commit_len[b] = n + 1;
+    if (v.next_last) v.next_last[b] = gr_s[n];
+  }
+}
+
 // Token-pass variant by batch size: every group holds at most T rows (the
 // shared experts hold exactly T), so T <= MT means one pass per group.
 template <typename WT, int MODE, int RT, int W>
@@ -1326,7 +1364,7 @@ void launch_norm_cast(const float* h, const float* y, int S, const void* gamma, 
 void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,
                    int V, int dt, int32_t* argmax_out, float* max_out, float* logits_out,
                    void* ws, hipStream_t s, const float* y_prev, int S_prev, float* h_out,
-                   int out_stride) {
+                   int out_stride, const VerifyFuse* vf) {
   const size_t xf_bytes = align_up(static_cast<size_t>(T) * H * esize(dt), 256);
   const int nblk = head_blocks(V);
   const size_t part = align_up(static_cast<size_t>(nblk) * T * 4, 256);
@@ -1351,7 +1389,14 @@ void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_
   } else {
     launch_gemm<float, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   }
+  if (vf != nullptr && vf->K + 1 <= kVerifyFuseMaxRows && out_stride == 1 && max_out == nullptr) {
+    argmax_verify_kernel<<<vf->B, 64 * (vf->K + 1), 0, s>>>(pmax, pidx, nblk, argmax_out, *vf);
+    return;
+  }
   argmax_reduce_kernel<<<T, 64, 0, s>>>(pmax, pidx, nblk, T, argmax_out, out_stride, max_out);
+  if (vf != nullptr)
+    launch_verify(vf->tokens, argmax_out, vf->B, vf->K, vf->n_accept, vf->commit, vf->commit_len,
+                  vf->next_last, s);
 }
 
 moev_status validate_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,

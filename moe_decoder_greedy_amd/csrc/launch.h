@@ -80,13 +80,24 @@ void launch_combine(const float* y, const float* h_in, int T, int H, int S, floa
 // slot order as launch_combine.
 void launch_gather_last(const float* h, const float* y, int S, int H, int n_seq, int seq_len,
                         float* out, hipStream_t s);
+// Prefix acceptance fused into the head's last kernel: rows b*(K+1) .. of the
+// head are sequence b's (last, d_1 .. d_K), tokens as mtp_verify takes them.
+struct VerifyFuse {
+  const int32_t* tokens;
+  int B, K;
+  int32_t* n_accept;
+  int32_t* commit;
+  int32_t* commit_len;
+  int32_t* next_last;
+};
 // y_prev (optional): the last layer's expert slots, added to h before the norm.
 // h_out (optional): the combined residual h + sum of y_prev's slots, fp32;
-// argmax_out[t * out_stride] receives token t's arg max.
+// argmax_out[t * out_stride] receives token t's arg max.  vf (optional): run
+// the prefix acceptance too (argmax_out then holds T = B*(K+1) contiguous rows).
 void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_lm, int T, int H,
                    int V, int dt, int32_t* argmax_out, float* max_out, float* logits_out,
                    void* ws, hipStream_t s, const float* y_prev = nullptr, int S_prev = 0,
-                   float* h_out = nullptr, int out_stride = 1);
+                   float* h_out = nullptr, int out_stride = 1, const VerifyFuse* vf = nullptr);
 // xo = RMSNorm(v) * gamma cast to dt, v = h (NULL: zeros) + the S slots of y
 // (NULL: none) in slot order; h_out (optional) receives v in fp32.
 void launch_norm_cast(const float* h, const float* y, int S, const void* gamma, float eps, int T,

@@ -221,11 +221,12 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
     hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
   };
   const int H = m->hidden, dt = m->dtype;
+  // the head's last kernel also applies the prefix acceptance
+  const VerifyFuse vf{tokens, B, K, n_accept, commit, commit_len, next_last};
   mark(MOEV_STAGE_HEAD, 0, false);
   launch_lmhead(h, m->norm_f, m->eps, m->w_lm, T, H, m->vocab, dt, greedy, nullptr, nullptr,
-                head_ws, s, m->n_layers > 0 ? y : nullptr, S, h_final);
+                head_ws, s, m->n_layers > 0 ? y : nullptr, S, h_final, 1, &vf);
   mark(MOEV_STAGE_HEAD, 0, true);
-  launch_verify(tokens, greedy, B, K, n_accept, commit, commit_len, next_last, s);
   return launch_status("moev_verify_step");
 }
 
