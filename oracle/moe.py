@@ -42,7 +42,12 @@ Sources are three web pages on Jina-OCR-v1:
    notes (hidden state and next-token embedding, each RMS-normalised,
    projected to H; one pre-norm dense SwiGLU with residual; the verifier's
    LM head behind the block's own final norm).
-5. tau = mean committed tokens per step; for independent per-position draft
+5. Decode attention (the causal self-attention sublayer of a decoder layer,
+   which the verify pass runs for its K+1 rows against each sequence's
+   cached prefix; the pages name the decoder but not its attention, so
+   ``attn_decode`` takes the plain multi-head reading listed in the design
+   notes: no positional rotation, scale 1/sqrt(head width)).
+6. tau = mean committed tokens per step; for independent per-position draft
    acceptances a_1..a_K its expectation is 1 + sum_m prod_{j<=m} a_j, which
    with Table 8's 0.830/0.663/0.636 gives the printed 2.73 ([P3] Strengths,
    speculative-decoding analysis).
@@ -68,7 +73,7 @@ __all__ = [
     "pair_groups", "permute", "grouped_ffn", "combine", "moe_layer",
     "embed", "lm_head", "first_argmax", "mtp_verify", "model_greedy",
     "verify_step", "greedy_rollout", "expected_tau", "acceptance_rate",
-    "draft_dense", "draft_block",
+    "draft_dense", "draft_block", "attn_decode",
 ]
 
 
@@ -434,6 +439,39 @@ def draft_block(z0: np.ndarray, t0: np.ndarray, draft: dict, model: dict, K: int
         gaps[:, j] = head["gap"]
         zs[j] = z
     return {"drafts": drafts, "z": z, "gap": gaps, "zs": zs}
+
+
+# ---------------------------------------------------------------------------
+# decode attention
+
+def attn_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos: np.ndarray,
+                rows: int, n_heads: int, dtype: str) -> np.ndarray:
+    """Causal multi-head attention of each sequence's verify rows over its
+    cache (see the module notes).
+
+    q [B*rows, H] (row b*rows + i is row i of sequence b, at position
+    pos[b] + i); k_cache, v_cache [B, L, H] in the stored dtype, holding the
+    sequence's prefix at positions 0..pos[b]-1 and the verify rows' own keys
+    and values at pos[b]..pos[b]+rows-1.  Row i attends to positions
+    0..pos[b]+i; per head (columns h*d .. (h+1)*d - 1, d = H / n_heads):
+        o = sum_j softmax_j(q . k_j / sqrt(d)) v_j.
+    Returns float64 [B*rows, H].
+    """
+    q = np.asarray(q, np.float64)
+    B, L, H = k_cache.shape
+    d = H // n_heads
+    out = np.zeros((B * rows, H))
+    for b in range(B):
+        K = to_f64(k_cache[b], dtype)
+        V = to_f64(v_cache[b], dtype)
+        for i in range(rows):
+            n = int(pos[b]) + i + 1
+            for h in range(n_heads):
+                c = slice(h * d, (h + 1) * d)
+                s = K[:n, c] @ q[b * rows + i, c] / np.sqrt(d)
+                p = np.exp(s - s.max())
+                out[b * rows + i, c] = (p @ V[:n, c]) / p.sum()
+    return out
 
 
 def expected_tau(accept: Sequence[float]) -> float:

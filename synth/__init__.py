@@ -38,13 +38,15 @@ __all__ = [
     "ModelShape", "Workload", "TINY", "DECODER", "WORKLOADS",
     "model_weights", "hidden_states", "initial_tokens", "prompt_tokens", "draft_tokens",
     "zipf_bias", "f32_to_bf16_bits", "splitmix64", "counter_uniform",
-    "counter_randint", "weight_bytes", "draft_weights", "draft_states",
+    "counter_randint", "weight_bytes", "draft_weights", "draft_states", "attention_inputs",
 ]
 
 # tensor codes in the spawn key
 _ROUTER, _GATE, _UP, _DOWN, _LM, _EMB, _HIDDEN, _ZIPF = 0, 1, 2, 3, 4, 5, 6, 7
 _DPROJ, _DGATE, _DUP, _DDOWN, _DSTATE = 8, 9, 10, 11, 12
+_AQ, _AK, _AV = 13, 14, 15
 _DRAFT_LAYER = 1000  # layer field of the draft block's streams
+_ATTN_LAYER = 2000   # layer field of the attention inputs' streams
 _ROW_CHUNK = 4096  # rows per stream for the vocabulary-sized tensors
 
 
@@ -295,6 +297,33 @@ def weight_bytes(w: dict) -> int:
         if k in w:
             n += w[k].nbytes
     return n
+
+
+def attention_inputs(batch: int, rows: int, hidden: int, max_len: int, prefix: Tuple[int, int],
+                     seed: int = 7, kv_std: float = 0.72, bf16: bool = True) -> dict:
+    """Inputs of decode attention for ``batch`` sequences of ``rows`` verify
+    rows each: queries float32 [batch*rows, hidden] ~ N(0, 1); a key and a
+    value cache [batch, max_len, hidden] ~ N(0, kv_std^2) (bf16 bit patterns
+    when ``bf16``), standing in for a page prefix and the verify rows' own keys;
+    and per sequence the number of cached positions before its first verify
+    row, uniform in [prefix[0], prefix[1]] and at most max_len - rows.  The
+    default kv_std is the spread of a 1280-wide N(0, 0.02) projection of a
+    unit-RMS state."""
+    lo, hi = prefix
+    hi = min(hi, max_len - rows)
+    assert 0 <= lo <= hi, "prefix range does not fit max_len"
+    key = lambda code, i: (0, _ATTN_LAYER, code, i)
+    q = _normal_block(seed, key(_AQ, 0), batch * rows * hidden, 1.0, False).reshape(batch * rows, hidden)
+    kc = _empty((batch, max_len, hidden), bf16)
+    vc = _empty((batch, max_len, hidden), bf16)
+    jobs = []
+    for b in range(batch):
+        jobs.append((kc[b], seed, key(_AK, b), kv_std, bf16))
+        jobs.append((vc[b], seed, key(_AV, b), kv_std, bf16))
+    _fill(jobs)
+    pos = (lo + counter_randint(hi - lo + 1, seed, np.arange(batch), -2)).astype(np.int32)
+    return {"q": q, "k_cache": kc, "v_cache": vc, "pos": pos, "rows": rows,
+            "dtype": "bf16" if bf16 else "f32"}
 
 
 def hidden_states(shape: ModelShape, n_tokens: int, seed: int = 1) -> np.ndarray:
