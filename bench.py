@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="verify_step_b32k3",
                     help="verify_step_b32k{3,2,1,0} | zipf_verify_b{1,8,32,128}k{1,3} | decode_layer_t128 | "
-                         "prefill_layer_t9760 | prefill_model_t9760 | kselect_b32 | spec_loop_b32k3")
+                         "prefill_layer_t9760 | prefill_model_t9760 | kselect_b32 | spec_loop_b32k3 | attn_decode_b32k3")
     ap.add_argument("--launch", choices=("auto", "eager", "graph"), default="auto")
     ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -472,6 +472,60 @@ def run_spec(args, torch, np):
     }
 
 
+def run_attn(args, torch, np):
+    """Decode attention of a verify pass (moev_attn_decode): 32 sequences x
+    (1 + K=3) rows at the decoder's width (10 heads of 128) against cached
+    prefixes of 1220-2300 positions (a page prompt of 1156 visual + 64 prompt
+    tokens plus part of the ~1085 generated ones), seeded bf16 caches.  HBM
+    bound: every visible key and value row is read once per head."""
+    import synth
+    from moe_decoder_greedy_amd import ops
+    B, rows, H, heads, L = 32, 4, 1280, 10, 2400
+    a = synth.attention_inputs(B, rows, H, L, (1220, 2300), seed=7)
+    kc = torch.from_numpy(a["k_cache"].view(np.int16)).cuda().view(torch.bfloat16)
+    vc = torch.from_numpy(a["v_cache"].view(np.int16)).cuda().view(torch.bfloat16)
+    q = torch.from_numpy(a["q"]).cuda()
+    pos = torch.from_numpy(a["pos"]).cuda()
+    out = torch.empty((B * rows, H), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        ops.attn_decode(q, kc, vc, pos, rows, heads, out=out)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(args.steps):
+        ops.attn_decode(q, kc, vc, pos, rows, heads, out=out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
+    visible = int((a["pos"].astype(np.int64) + rows).sum())
+    nbytes = visible * H * 2 * 2 + 2 * B * rows * H * 4
+    gbs = nbytes / t / 1e9
+    log(f"attention: {t * 1e6:.1f} us per launch, {nbytes / 1e6:.1f} MB, {gbs:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        ns = 2
+        sub = {key: a[key][:ns] for key in ("k_cache", "v_cache", "pos")}
+        t0 = time.perf_counter()
+        oracle.attn_decode(a["q"][:ns * rows], sub["k_cache"], sub["v_cache"], sub["pos"], rows, heads, "bf16")
+        dt_cpu = time.perf_counter() - t0
+        cpu = {"value": round(ns * rows / dt_cpu, 2), "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"{ns} of the {B} sequences (float64 numpy, per-row loops)"}
+    return {
+        "metric": "decode attention rows/s (32 seq x (1+K=3) rows, 1220-2300 cached positions) + % HBM peak",
+        "value": round(B * rows / t, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 cache, fp32 math", "data": "synthetic (seeded caches and queries)",
+        "config": {"workload": "attn_decode_b32k3", "batch": B, "rows": rows, "hidden": H, "heads": heads,
+                   "max_len": L, "visible_positions": visible},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_decode_kernel<bf16, 128> (moev_attn_decode)", "bytes_per_launch": nbytes,
+                     "avg_launch_us": round(t * 1e6, 2)},
+        "cpu_baseline": cpu,
+    }
+
+
 def run_verify(args, torch, np):
     import synth
     from moe_decoder_greedy_amd import model as mdl
@@ -743,6 +797,8 @@ def main():
         result = run_kselect(args, torch, np)
     elif args.workload == "spec_loop_b32k3":
         result = run_spec(args, torch, np)
+    elif args.workload == "attn_decode_b32k3":
+        result = run_attn(args, torch, np)
     elif args.workload == "prefill_model_t9760":
         result = run_prefill_model(args, torch, np)
     elif args.workload.endswith(("_t128", "_t9760")):

@@ -365,6 +365,30 @@ moev_status moev_spec_step(const moev_model* m, const moev_draft_weights* d,
                            int32_t* next_tokens, float* h_final, void* ws, size_t ws_bytes,
                            void* stream);
 
+/*
+ * moev_attn_decode -- causal multi-head attention of each sequence's verify
+ * rows over its cached prefix (the decoder's attention sublayer in a verify
+ * pass: "The speed comes from three layers working together" on
+ * kg.zhiyong.dev has the main decoder check all K drafts in one pass; the
+ * pages do not describe its attention, so this is plain multi-head attention,
+ * scale 1/sqrt(head width), no positional rotation).  Row i of sequence b is
+ * at position pos[b] + i and sees positions 0 .. pos[b] + i; per head
+ * (columns h*D .. (h+1)*D - 1, D = H / n_heads):
+ *   out = sum_j softmax_j(q . k_j / sqrt(D)) v_j
+ *   q        fp32 [B*rows, H] device (row b*rows + i)
+ *   k_cache, v_cache  dt [B, max_len, H] device: the prefix at positions
+ *            0 .. pos[b]-1 and the verify rows' own keys and values at
+ *            pos[b] .. pos[b]+rows-1 (caller-owned; not modified)
+ *   pos      int32 [B] device; clamped on the device so that at most max_len
+ *            positions are read
+ *   out      fp32 [B*rows, H] device (written)
+ * 1 <= rows <= 16; D in {64, 128, 256}.  B = 0 is a no-op.  Nothing
+ * allocates or synchronises.
+ */
+moev_status moev_attn_decode(const float* q, const void* k_cache, const void* v_cache, const int32_t* pos,
+                             int B, int rows, int max_len, int H, int n_heads, int dt, float* out,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

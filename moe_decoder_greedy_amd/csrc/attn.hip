@@ -1,0 +1,264 @@
+// Decode attention: each sequence's verify rows (its last committed token and
+// K drafts, run as one pass by the FastMTP verifier -- "The speed comes from
+// three layers working together", Jina-OCR-v1 explainer on kg.zhiyong.dev)
+// attend causally to the sequence's cached prefix and to each other.  The
+// pages do not describe the decoder's attention; this is plain multi-head
+// attention with scale 1/sqrt(head width) and no positional rotation: row i
+// of sequence b, at position pos[b] + i, sees positions 0 .. pos[b] + i.
+//
+// One workgroup per (sequence, head) with kAttnWaves wavefronts that split the
+// visible positions (those of the sequence's last row) into equal contiguous
+// ranges.  A wave walks its range in chunks of 64: lane l scores position
+// c0 + l against every verify row's query (staged in LDS, rows masked
+// causally), each row's chunk maximum updates that row's running maximum of
+// an online softmax, and the values are accumulated position by position in
+// order, each lane holding D/64 adjacent output columns of every row,
+// so every key and value row is read once per workgroup with coalesced
+// loads.  At the end the waves' partial (maximum, sum, output) triples are
+// merged in wave order through LDS.  All arithmetic is fp32; a row's result
+// depends only on its own query and cache.
+#include "launch.h"
+
+namespace moev {
+namespace {
+
+constexpr int kAttnMaxRows = 16;   // verify rows per sequence
+
+// N consecutive cache elements as fp32, in one load where the width allows
+template <typename WT, int N> __device__ __forceinline__ void ldn(const WT* p, float (&v)[N]) {
+  if constexpr (sizeof(WT) == 2 && N == 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf16_to_f32(w[e] & 0xFFFF);
+      v[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+    }
+  } else if constexpr (sizeof(WT) == 2 && N == 2) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = bf16_to_f32(u & 0xFFFF);
+    v[1] = bf16_to_f32(u >> 16);
+  } else if constexpr (sizeof(WT) == 2 && N == 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    v[0] = bf16_to_f32(u.x & 0xFFFF);
+    v[1] = bf16_to_f32(u.x >> 16);
+    v[2] = bf16_to_f32(u.y & 0xFFFF);
+    v[3] = bf16_to_f32(u.y >> 16);
+  } else if constexpr (sizeof(WT) == 4 && N == 2) {
+    const float2 u = *reinterpret_cast<const float2*>(p);
+    v[0] = u.x;
+    v[1] = u.y;
+  } else if constexpr (sizeof(WT) == 4 && N == 4) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) v[e] = to_f32<WT>(p[e]);
+  }
+}
+
+constexpr int kAttnWaves = 8;  // wavefronts per workgroup (key-range split)
+
+template <typename WT, int D, int R>
+__global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
+    const float* __restrict__ q, const WT* __restrict__ kc, const WT* __restrict__ vc,
+    const int32_t* __restrict__ pos, int rows, int max_len, int H, float scale, float* __restrict__ out) {
+  // value walk: a value row is read as D / kEpl 16-byte pieces (kLpk lanes);
+  // the kNg lane groups of a wave take every kNg-th position of a chunk
+  constexpr int kEpl = 16 / static_cast<int>(sizeof(WT));  // elements per 16-byte load
+  constexpr int kLpk = D / kEpl;                           // lanes per value row
+  constexpr int kNg = kWave / kLpk;                        // position groups
+  static_assert(kLpk * kNg == kWave && kLpk >= 1, "head width");
+  // LDS: queries [R][D] and per-wave softmax weights [waves][R][64] during
+  // the walk; the same space then holds the per-wave outputs [waves][R][D]
+  constexpr int kWalk = R * D + kAttnWaves * R * kWave;
+  constexpr int kMerge = kAttnWaves * R * D;
+  __shared__ float smem[(kWalk > kMerge ? kWalk : kMerge) + 2 * kAttnWaves * R];
+  float (*q_s)[D] = reinterpret_cast<float (*)[D]>(smem);
+  float (*p_s)[R][kWave] = reinterpret_cast<float (*)[R][kWave]>(smem + R * D);
+  float (*o_s)[R][D] = reinterpret_cast<float (*)[R][D]>(smem);
+  float (*m_s)[R] = reinterpret_cast<float (*)[R]>(smem + (kWalk > kMerge ? kWalk : kMerge));
+  float (*l_s)[R] = m_s + kAttnWaves;
+  const int b = blockIdx.x;
+  const int h = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col0 = h * D;
+  for (int i = threadIdx.x; i < R * D; i += blockDim.x) {
+    const int r = i / D, c = i - r * D;
+    q_s[r][c] = r < rows ? q[(static_cast<long long>(b) * rows + r) * H + col0 + c] * scale : 0.f;
+  }
+  __syncthreads();
+
+  const int p0 = min(max(pos[b], 0), max_len - rows);  // row r sees positions 0 .. p0 + r
+  const int n_all = p0 + rows;
+  const int lo = static_cast<int>(static_cast<long long>(wave) * n_all / kAttnWaves);
+  const int hi = static_cast<int>(static_cast<long long>(wave + 1) * n_all / kAttnWaves);
+  const WT* kb = kc + static_cast<long long>(b) * max_len * H + col0;
+  const WT* vb = vc + static_cast<long long>(b) * max_len * H + col0;
+  const int vg = lane / kLpk;           // this lane's position group
+  const int vc0 = (lane % kLpk) * kEpl;  // and its columns vc0 .. vc0 + kEpl - 1
+  float m_run[R], l_run[R], o[R][kEpl];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kEpl; ++e) o[r][e] = 0.f;
+  }
+
+  for (int c0 = lo; c0 < hi; c0 += kWave) {
+    const int j = c0 + lane;
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = 0.f;
+    if (j < hi) {
+      const WT* kr = kb + static_cast<long long>(j) * H;
+#pragma unroll
+      for (int c = 0; c < D; c += 8) {
+        float kv[8];
+        if constexpr (sizeof(WT) == 2) {
+          const uint4 u = *reinterpret_cast<const uint4*>(kr + c);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv[2 * e] = bf16_to_f32(w[e] & 0xFFFF);
+            kv[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+          }
+        } else {
+          const float4 a = *reinterpret_cast<const float4*>(kr + c);
+          const float4 bq = *reinterpret_cast<const float4*>(kr + c + 4);
+          kv[0] = a.x; kv[1] = a.y; kv[2] = a.z; kv[3] = a.w;
+          kv[4] = bq.x; kv[5] = bq.y; kv[6] = bq.z; kv[7] = bq.w;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[r] += q_s[r][c + e] * kv[e];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool vis = j < hi && j <= p0 + r && r < rows;
+      const float sv = vis ? s[r] : -INFINITY;
+      const float m_new = fmaxf(m_run[r], wave_max(sv));
+      // m_new = -inf: nothing of this row visible yet (a row sees fewer
+      // positions than the last one); keep its state unchanged
+      const float corr = m_new == -INFINITY ? 1.f : expf(m_run[r] - m_new);
+      const float pv = vis ? expf(sv - m_new) : 0.f;
+      l_run[r] = l_run[r] * corr + wave_sum(pv);
+#pragma unroll
+      for (int e = 0; e < kEpl; ++e) o[r][e] *= corr;
+      m_run[r] = m_new;
+      p_s[wave][r][lane] = pv;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // position jj = it * kNg + vg of the chunk; positions past hi have
+    // weight 0 and read the chunk's first row instead
+#pragma unroll
+    for (int it = 0; it < kWave / kNg; ++it) {
+      const int jj = it * kNg + vg;
+      const int jr = c0 + jj < hi ? c0 + jj : c0;
+      float vv[kEpl];
+      ldn<WT, kEpl>(vb + static_cast<long long>(jr) * H + vc0, vv);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float pj = p_s[wave][r][jj];
+#pragma unroll
+        for (int e = 0; e < kEpl; ++e) o[r][e] += pj * vv[e];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // p_s is rewritten by the next chunk
+  }
+
+  // merge the waves' partial softmax states, in wave order (every wave is
+  // done with the queries and weights before the space is reused)
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (lane == 0) {
+      m_s[wave][r] = m_run[r];
+      l_s[wave][r] = l_run[r];
+    }
+    // add the position groups' partial outputs (same columns kLpk lanes apart)
+#pragma unroll
+    for (int e = 0; e < kEpl; ++e) {
+      float v = o[r][e];
+#pragma unroll
+      for (int m = kLpk; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+      if (vg == 0) o_s[wave][r][vc0 + e] = v;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < rows * D; i += blockDim.x) {
+    const int r = i / D, c = i - r * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][r]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float f = m_s[w][r] == -INFINITY ? 0.f : expf(m_s[w][r] - M);
+      L += l_s[w][r] * f;
+      O += o_s[w][r][c] * f;
+    }
+    out[(static_cast<long long>(b) * rows + r) * H + col0 + c] = O / L;
+  }
+}
+
+template <typename WT, int D>
+void launch_attn_d(const float* q, const WT* k, const WT* v, const int32_t* pos, int B, int rows, int max_len,
+                   int H, int n_heads, float scale, float* out, hipStream_t s) {
+  const dim3 grid(B, n_heads);
+  const dim3 block(kWave * kAttnWaves);
+  if (rows <= 1) attn_decode_kernel<WT, D, 1><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
+  else if (rows <= 4) attn_decode_kernel<WT, D, 4><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
+  else if (rows <= 8) attn_decode_kernel<WT, D, 8><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
+  else attn_decode_kernel<WT, D, 16><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
+}
+
+template <typename WT>
+void launch_attn_t(const float* q, const void* kc, const void* vc, const int32_t* pos, int B, int rows,
+                   int max_len, int H, int n_heads, float* out, hipStream_t s) {
+  const int D = H / n_heads;
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const WT* k = static_cast<const WT*>(kc);
+  const WT* v = static_cast<const WT*>(vc);
+  switch (D) {
+    case 64: launch_attn_d<WT, 64>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, out, s); break;
+    case 128: launch_attn_d<WT, 128>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, out, s); break;
+    case 256: launch_attn_d<WT, 256>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, out, s); break;
+    default: break;  // validated
+  }
+}
+
+}  // namespace
+}  // namespace moev
+
+extern "C" moev_status moev_attn_decode(const float* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* pos, int B, int rows, int max_len, int H,
+                                        int n_heads, int dt, float* out, void* stream) {
+  using namespace moev;
+  clear_error();
+  MOEV_CHECK(check_dtype(dt), MOEV_ERR_UNSUPPORTED);
+  MOEV_REQUIRE(B >= 0, MOEV_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+  MOEV_REQUIRE(rows >= 1 && rows <= kAttnMaxRows, MOEV_ERR_UNSUPPORTED, "rows=%d must be in [1, %d]", rows,
+               kAttnMaxRows);
+  MOEV_REQUIRE(n_heads >= 1 && H >= 1 && H % n_heads == 0, MOEV_ERR_UNSUPPORTED,
+               "H=%d must be a positive multiple of n_heads=%d", H, n_heads);
+  const int D = H / n_heads;
+  MOEV_REQUIRE(D == 64 || D == 128 || D == 256, MOEV_ERR_UNSUPPORTED,
+               "head width %d must be 64, 128 or 256", D);
+  MOEV_REQUIRE(max_len >= rows, MOEV_ERR_INVALID_ARG, "max_len=%d must be >= rows=%d", max_len, rows);
+  if (B == 0) return MOEV_OK;
+  MOEV_CHECK(need_ptr(q, "q") && need_ptr(k_cache, "k_cache") && need_ptr(v_cache, "v_cache") &&
+                 need_ptr(pos, "pos", 4) && need_ptr(out, "out"),
+             MOEV_ERR_INVALID_ARG);
+  if (dt == MOEV_BF16)
+    launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, out, as_stream(stream));
+  else
+    launch_attn_t<float>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, out, as_stream(stream));
+  return launch_status("moev_attn_decode");
+}

@@ -168,3 +168,22 @@ def test_draft_and_spec_step_validation(lib):
     assert step(n=spec - 1) == WORKSPACE
     m.hidden = 1300
     assert step() == UNSUPPORTED
+
+
+def test_attn_decode_validation(lib):
+    s = None
+
+    def call(q=FAKE, k=FAKE, v=FAKE, pos=FAKE, B=2, rows=4, L=64, H=1280, heads=10, dt=BF16, out=FAKE):
+        return lib.moev_attn_decode(q, k, v, pos, B, rows, L, H, heads, dt, out, s)
+
+    assert call(rows=0) == UNSUPPORTED and "rows" in _err(lib)
+    assert call(rows=17) == UNSUPPORTED
+    assert call(H=1280, heads=3) == UNSUPPORTED
+    assert call(H=1280, heads=16) == UNSUPPORTED and "head width" in _err(lib)  # 80-wide heads
+    assert call(H=1280, heads=40) == UNSUPPORTED                                  # 32-wide heads
+    assert call(L=3) == INVALID and "max_len" in _err(lib)
+    assert call(dt=7) == UNSUPPORTED
+    assert call(B=-1) == INVALID
+    assert call(B=0, q=None, k=None, v=None, pos=None, out=None) == OK
+    assert call(q=None) == INVALID and "q" in _err(lib)
+    assert call(pos=FAKE + 2) == INVALID and "aligned" in _err(lib)

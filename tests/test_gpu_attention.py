@@ -1,0 +1,55 @@
+"""Decode attention on the GPU (moev_attn_decode) against the oracle's
+attn_decode, on seeded caches."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import dev_f32, dev_i32, host, max_abs, need_gpu, report
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    need_gpu()
+    from moe_decoder_greedy_amd import ops as _ops
+    return _ops
+
+
+def _dev_cache(a):
+    if a["dtype"] == "bf16":
+        return tuple(torch.from_numpy(a[key].view(np.int16)).cuda().view(torch.bfloat16)
+                     for key in ("k_cache", "v_cache"))
+    return tuple(torch.from_numpy(a[key]).cuda() for key in ("k_cache", "v_cache"))
+
+
+@pytest.mark.parametrize("B,rows,H,heads,L,prefix,bf16", [
+    (8, 4, 1280, 10, 1400, (1100, 1300), True),    # decoder width, page-length prefixes, K = 3
+    (5, 1, 256, 4, 300, (0, 299), False),          # greedy rows, fp32 cache, 64-wide heads
+    (3, 16, 512, 2, 40, (0, 0), True),             # 256-wide heads, no prefix: row 0 sees only itself
+    (4, 2, 256, 4, 90, (88, 88), True),            # 64-wide bf16 heads, the last positions of the cache
+])
+def test_attn_decode_matches_oracle(ops, B, rows, H, heads, L, prefix, bf16):
+    a = synth.attention_inputs(B, rows, H, L, prefix, seed=11 + B, bf16=bf16)
+    report("attn_decode", B=B, rows=rows, H=H, heads=heads, L=L, pos=a["pos"].tolist())
+    kc, vc = _dev_cache(a)
+    out = host(ops.attn_decode(dev_f32(a["q"]), kc, vc, dev_i32(a["pos"]), rows, heads))
+    want = oracle.attn_decode(a["q"], a["k_cache"], a["v_cache"], a["pos"], rows, heads, a["dtype"])
+    err = max_abs(out, want)
+    report("attn_decode", err=err, scale=float(np.abs(want).max()))
+    assert err < 2e-5
+
+
+def test_attn_decode_rows_do_not_depend_on_the_batch(ops):
+    """A sequence's outputs are the same bits alone and in a batch."""
+    B, rows, H, heads, L = 6, 4, 1280, 10, 600
+    a = synth.attention_inputs(B, rows, H, L, (100, 590), seed=21)
+    kc, vc = _dev_cache(a)
+    q, pos = dev_f32(a["q"]), dev_i32(a["pos"])
+    full = host(ops.attn_decode(q, kc, vc, pos, rows, heads))
+    for b in (0, 3, 5):
+        one = host(ops.attn_decode(q[b * rows:(b + 1) * rows].contiguous(), kc[b:b + 1].contiguous(),
+                                   vc[b:b + 1].contiguous(), pos[b:b + 1].contiguous(), rows, heads))
+        np.testing.assert_array_equal(one.view(np.uint32), full[b * rows:(b + 1) * rows].view(np.uint32))
