@@ -73,7 +73,8 @@ __all__ = [
     "pair_groups", "permute", "grouped_ffn", "combine", "moe_layer",
     "embed", "lm_head", "first_argmax", "mtp_verify", "model_greedy",
     "verify_step", "greedy_rollout", "expected_tau", "acceptance_rate",
-    "draft_dense", "draft_block", "attn_decode",
+    "draft_dense", "draft_block", "attn_decode", "attn_sublayer", "cached_greedy",
+    "cached_verify_step", "cached_rollout",
 ]
 
 
@@ -82,12 +83,15 @@ __all__ = [
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     """Stored tensor -> float64.  "bf16": uint16 bit patterns (the bf16 value is
-    the float32 whose upper half is those bits); "f32": float32 values."""
+    the float32 whose upper half is those bits); "f32": float32 values; "f64":
+    float64 values (the oracle's own caches)."""
     a = np.asarray(a)
     if dtype == "bf16":
         assert a.dtype == np.uint16
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     if dtype == "f32":
+        return a.astype(np.float64)
+    if dtype == "f64":
         return a.astype(np.float64)
     raise ValueError(dtype)
 
@@ -471,6 +475,81 @@ def attn_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos: np
                 s = K[:n, c] @ q[b * rows + i, c] / np.sqrt(d)
                 p = np.exp(s - s.max())
                 out[b * rows + i, c] = (p @ V[:n, c]) / p.sum()
+    return out
+
+
+def attn_sublayer(h: np.ndarray, attn: dict, cache: dict, pos: np.ndarray, rows: int, n_heads: int,
+                  dtype: str, eps: float, operands: str = "bf16") -> np.ndarray:
+    """Pre-norm causal attention sublayer with residual, for B sequences of
+    ``rows`` rows (h [B*rows, H]; row i of sequence b at position pos[b] + i).
+
+    x = RMSNorm(h) (gain 1); q, k, v = x W_q^T, x W_k^T, x W_v^T; the rows' k
+    and v are written into the sequence's cache at positions pos[b] + i
+    (rounded to bf16 for a bf16 model, as the cache stores them); o =
+    attn_decode(q, cache); h_out = h + o W_o^T.  With ``operands="bf16"`` and
+    a bf16 model, x and o are rounded to bf16 as the projections take them.
+    ``cache`` = {"k", "v"}: float64 [B, L, H], updated in place.
+    """
+    rnd = operands == "bf16" and dtype == "bf16"
+    x = rmsnorm(h, 1.0, eps)
+    x_op = round_bf16(x) if rnd else x
+    q = x_op @ to_f64(attn["w_q"], dtype).T
+    k = x_op @ to_f64(attn["w_k"], dtype).T
+    v = x_op @ to_f64(attn["w_v"], dtype).T
+    if dtype == "bf16":
+        k, v = round_bf16(k), round_bf16(v)
+    B = len(pos)
+    for b in range(B):
+        for i in range(rows):
+            cache["k"][b, int(pos[b]) + i] = k[b * rows + i]
+            cache["v"][b, int(pos[b]) + i] = v[b * rows + i]
+    o = attn_decode(q, cache["k"], cache["v"], pos, rows, n_heads, "f64")
+    o_op = round_bf16(o) if rnd else o
+    return h + o_op @ to_f64(attn["w_o"], dtype).T
+
+
+def cached_greedy(tokens: np.ndarray, model: dict, attn: list, caches: list, pos: np.ndarray,
+                  n_heads: int, operands: str = "bf16") -> dict:
+    """Greedy tokens of the decoder with an attention sublayer before every
+    MoE sublayer (tokens int [B, rows], row i of sequence b at position
+    pos[b] + i; ``caches`` one {"k", "v"} per layer, updated in place)."""
+    shape = model["shape"]
+    dt = model["dtype"]
+    tokens = np.asarray(tokens, np.int64)
+    B, rows = tokens.shape
+    h = embed(tokens.reshape(-1), model["emb"], dt)
+    for layer, at, cache in zip(model["layers"], attn, caches):
+        h = attn_sublayer(h, at, cache, pos, rows, n_heads, dt, shape.eps, operands)
+        h = moe_layer(h, layer, dt, shape.top_k, shape.n_routed, shape.n_shared, shape.eps,
+                      operands)["h_out"]
+    head = lm_head(h, model["norm_f"], model["w_lm"], dt, shape.eps, operands)
+    return {"argmax": head["argmax"].reshape(B, rows), "gap": head["gap"].reshape(B, rows), "h": h}
+
+
+def cached_verify_step(last: np.ndarray, drafts: np.ndarray, model: dict, attn: list, caches: list,
+                       pos: np.ndarray, n_heads: int, operands: str = "bf16") -> dict:
+    """One verify pass with attention: (last, d_1..d_K) of sequence b at
+    positions pos[b] .. pos[b]+K, accept as ``mtp_verify``; the sequence's
+    position then advances by n_b + 1 (its last token and the n accepted
+    drafts stay in the cache; the rows past them are overwritten later)."""
+    last = np.asarray(last, np.int64).reshape(-1, 1)
+    tokens = np.concatenate([last, np.asarray(drafts, np.int64).reshape(last.shape[0], -1)], axis=1)
+    fwd = cached_greedy(tokens, model, attn, caches, pos, n_heads, operands)
+    n_acc, commit, clen, nxt = mtp_verify(tokens, fwd["argmax"])
+    return {"greedy": fwd["argmax"], "gap": fwd["gap"], "n_accept": n_acc, "commit": commit,
+            "commit_len": clen, "next_last": nxt, "pos": np.asarray(pos) + n_acc + 1}
+
+
+def cached_rollout(last: np.ndarray, model: dict, attn: list, caches: list, pos: np.ndarray,
+                   n_heads: int, n_tokens: int, operands: str = "bf16") -> np.ndarray:
+    """Plain greedy decoding with attention: one row per sequence per step."""
+    cur = np.asarray(last, np.int64).reshape(-1)
+    pos = np.asarray(pos).copy()
+    out = np.empty((len(cur), n_tokens), np.int64)
+    for s in range(n_tokens):
+        cur = cached_greedy(cur[:, None], model, attn, caches, pos, n_heads, operands)["argmax"][:, 0]
+        out[:, s] = cur
+        pos = pos + 1
     return out
 
 

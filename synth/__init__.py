@@ -39,12 +39,14 @@ __all__ = [
     "model_weights", "hidden_states", "initial_tokens", "prompt_tokens", "draft_tokens",
     "zipf_bias", "f32_to_bf16_bits", "splitmix64", "counter_uniform",
     "counter_randint", "weight_bytes", "draft_weights", "draft_states", "attention_inputs",
+    "attention_weights",
 ]
 
 # tensor codes in the spawn key
 _ROUTER, _GATE, _UP, _DOWN, _LM, _EMB, _HIDDEN, _ZIPF = 0, 1, 2, 3, 4, 5, 6, 7
 _DPROJ, _DGATE, _DUP, _DDOWN, _DSTATE = 8, 9, 10, 11, 12
 _AQ, _AK, _AV = 13, 14, 15
+_WQ, _WK, _WV, _WO = 16, 17, 18, 19
 _DRAFT_LAYER = 1000  # layer field of the draft block's streams
 _ATTN_LAYER = 2000   # layer field of the attention inputs' streams
 _ROW_CHUNK = 4096  # rows per stream for the vocabulary-sized tensors
@@ -297,6 +299,22 @@ def weight_bytes(w: dict) -> int:
         if k in w:
             n += w[k].nbytes
     return n
+
+
+def attention_weights(shape: ModelShape, seed: int = 0) -> list:
+    """Per decoder layer, the attention sublayer's projections W_q, W_k, W_v,
+    W_o, each [H, H] ~ N(0, weight_std^2) (bf16 bit patterns for a bf16
+    model), on streams of their own."""
+    bf16 = shape.dtype == "bf16"
+    H = shape.hidden
+    out = []
+    for layer in range(shape.n_layers):
+        d = {key: _empty((H, H), bf16) for key in ("w_q", "w_k", "w_v", "w_o")}
+        jobs = [(d[key], seed, (shape.model_id, layer, code, 0), shape.weight_std, bf16)
+                for key, code in (("w_q", _WQ), ("w_k", _WK), ("w_v", _WV), ("w_o", _WO))]
+        _fill(jobs)
+        out.append(d)
+    return out
 
 
 def attention_inputs(batch: int, rows: int, hidden: int, max_len: int, prefix: Tuple[int, int],
