@@ -6,9 +6,11 @@
 // attention with scale 1/sqrt(head width) and no positional rotation: row i
 // of sequence b, at position pos[b] + i, sees positions 0 .. pos[b] + i.
 //
-// One workgroup per (sequence, head) with kAttnWaves wavefronts that split the
-// visible positions (those of the sequence's last row) into equal contiguous
-// ranges.  A wave walks its range in chunks of 64: lane l scores position
+// One workgroup per (sequence, head) with kAttnWaves wavefronts; wave w takes
+// the 64-position chunks w, w + kAttnWaves, ... of the positions the
+// sequence's last row can see, so a row's visible chunks, the order a wave
+// takes them in and the merge order do not depend on the number of rows in
+// the pass (chunks a row cannot see leave its state unchanged).  Per chunk: lane l scores position
 // c0 + l against every verify row's query (staged in LDS, rows masked
 // causally), each row's chunk maximum updates that row's running maximum of
 // an online softmax, and the values are accumulated position by position in
@@ -92,8 +94,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
 
   const int p0 = min(max(pos[b], 0), max_len - rows);  // row r sees positions 0 .. p0 + r
   const int n_all = p0 + rows;
-  const int lo = static_cast<int>(static_cast<long long>(wave) * n_all / kAttnWaves);
-  const int hi = static_cast<int>(static_cast<long long>(wave + 1) * n_all / kAttnWaves);
+  const int hi = n_all;
   const WT* kb = kc + static_cast<long long>(b) * max_len * H + col0;
   const WT* vb = vc + static_cast<long long>(b) * max_len * H + col0;
   const int vg = lane / kLpk;           // this lane's position group
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
     for (int e = 0; e < kEpl; ++e) o[r][e] = 0.f;
   }
 
-  for (int c0 = lo; c0 < hi; c0 += kWave) {
+  for (int c0 = wave * kWave; c0 < hi; c0 += kAttnWaves * kWave) {
     const int j = c0 + lane;
     float s[R];
 #pragma unroll

@@ -53,3 +53,4 @@ def test_attn_decode_rows_do_not_depend_on_the_batch(ops):
         one = host(ops.attn_decode(q[b * rows:(b + 1) * rows].contiguous(), kc[b:b + 1].contiguous(),
                                    vc[b:b + 1].contiguous(), pos[b:b + 1].contiguous(), rows, heads))
         np.testing.assert_array_equal(one.view(np.uint32), full[b * rows:(b + 1) * rows].view(np.uint32))
+
