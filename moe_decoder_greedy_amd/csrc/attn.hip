@@ -65,6 +65,10 @@ template <typename WT, int D, int R>
 __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
     const float* __restrict__ q, const WT* __restrict__ kc, const WT* __restrict__ vc,
     const int32_t* __restrict__ pos, int rows, int max_len, int H, float scale, float* __restrict__ out) {
+  // Every fused multiply-add below is written out and no other is formed, so
+  // the instantiations for different row counts round identically (the
+  // compiler may otherwise fuse a*b + c*d either way round).
+#pragma clang fp contract(off)
   // value walk: a value row is read as D / kEpl 16-byte pieces (kLpk lanes);
   // the kNg lane groups of a wave take every kNg-th position of a chunk
   constexpr int kEpl = 16 / static_cast<int>(sizeof(WT));  // elements per 16-byte load
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s[r] += q_s[r][c + e] * kv[e];
+          for (int e = 0; e < 8; ++e) s[r] = fmaf(q_s[r][c + e], kv[e], s[r]);
       }
     }
 #pragma unroll
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
       // positions than the last one); keep its state unchanged
       const float corr = m_new == -INFINITY ? 1.f : expf(m_run[r] - m_new);
       const float pv = vis ? expf(sv - m_new) : 0.f;
-      l_run[r] = l_run[r] * corr + wave_sum(pv);
+      l_run[r] = fmaf(l_run[r], corr, wave_sum(pv));
 #pragma unroll
       for (int e = 0; e < kEpl; ++e) o[r][e] *= corr;
       m_run[r] = m_new;
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
       for (int r = 0; r < R; ++r) {
         const float pj = p_s[wave][r][jj];
 #pragma unroll
-        for (int e = 0; e < kEpl; ++e) o[r][e] += pj * vv[e];
+        for (int e = 0; e < kEpl; ++e) o[r][e] = fmaf(pj, vv[e], o[r][e]);
       }
     }
     __builtin_amdgcn_wave_barrier();  // p_s is rewritten by the next chunk
@@ -202,8 +206,8 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
       const float f = m_s[w][r] == -INFINITY ? 0.f : expf(m_s[w][r] - M);
-      L += l_s[w][r] * f;
-      O += o_s[w][r][c] * f;
+      L = fmaf(l_s[w][r], f, L);
+      O = fmaf(o_s[w][r][c], f, O);
     }
     out[(static_cast<long long>(b) * rows + r) * H + col0 + c] = O / L;
   }

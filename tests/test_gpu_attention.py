@@ -54,3 +54,17 @@ def test_attn_decode_rows_do_not_depend_on_the_batch(ops):
                                    vc[b:b + 1].contiguous(), pos[b:b + 1].contiguous(), rows, heads))
         np.testing.assert_array_equal(one.view(np.uint32), full[b * rows:(b + 1) * rows].view(np.uint32))
 
+
+
+def test_attn_row_is_the_same_in_a_one_row_pass(ops):
+    """Row i of a 4-row pass is the same bits as a one-row pass at position
+    pos[b] + i: greedy decoding and a verify pass see the same attention."""
+    B, rows, H, heads, L = 3, 4, 1280, 10, 900
+    a = synth.attention_inputs(B, rows, H, L, (100, 880), seed=31)
+    kc, vc = _dev_cache(a)
+    q, pos = dev_f32(a["q"]), dev_i32(a["pos"])
+    full = host(ops.attn_decode(q, kc, vc, pos, rows, heads)).reshape(B, rows, H)
+    for i in range(rows):
+        qi = q.view(B, rows, H)[:, i].contiguous()
+        one = host(ops.attn_decode(qi, kc, vc, (pos + i).contiguous(), 1, heads))
+        np.testing.assert_array_equal(one.view(np.uint32), np.ascontiguousarray(full[:, i]).view(np.uint32))
