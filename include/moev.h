@@ -389,6 +389,51 @@ moev_status moev_attn_decode(const float* q, const void* k_cache, const void* v_
                              int B, int rows, int max_len, int H, int n_heads, int dt, float* out,
                              void* stream);
 
+/*
+ * moev_verify_step_attn -- the verify pass of moev_verify_step through a
+ * decoder whose layers each run a causal attention sublayer before the MoE
+ * sublayer (the main model checks all K drafts in one pass, "The speed comes
+ * from three layers working together" on kg.zhiyong.dev; the pages do not
+ * describe the attention, so it is plain pre-norm multi-head attention, unit
+ * norm gain, no positional rotation).  Per layer, for the rows of sequence b
+ * at positions pos[b] .. pos[b]+K:
+ *   x = RMSNorm(h);  [q | k | v] = x [W_q; W_k; W_v]^T
+ *   k, v rounded to dt into the caches at those positions
+ *   h += W_o attn(q, caches)   (moev_attn_decode), then the MoE sublayer.
+ * After the head and the prefix acceptance, pos[b] += commit_len[b]: the
+ * sequence's last token and its accepted drafts stay in the cache, and the
+ * rows written for rejected drafts are overwritten by the next pass.
+ *   attn->layers[l].w_qkv  dt [3H, H] fragment-packed (W_q, W_k, W_v stacked)
+ *   attn->layers[l].w_o    dt [H, H] fragment-packed
+ *   attn->layers[l].k_cache, v_cache  dt [B, max_len, H] device, updated
+ *   pos      int32 [B] device, read then advanced; the caller keeps
+ *            pos[b] + K + 1 <= max_len (larger values are clamped on the
+ *            device, which keeps every access in bounds but overwrites the
+ *            cache's last rows)
+ *   greedy, n_accept, commit, commit_len, next_last: as moev_verify_step
+ *   ws       workspace of moev_verify_step_attn_workspace_size() bytes
+ * Needs B*(K+1) <= 512, K + 1 <= 16, H / n_heads in {64, 128, 256} and
+ * max_len >= K + 1.  K = 0 is plain greedy decoding of one token per
+ * sequence.  Nothing allocates or synchronises.
+ */
+typedef struct moev_attn_layer {
+  const void* w_qkv;
+  const void* w_o;
+  void* k_cache;
+  void* v_cache;
+} moev_attn_layer;
+
+typedef struct moev_attn {
+  int n_heads, max_len;
+  const moev_attn_layer* layers; /* host array of n_layers entries */
+} moev_attn;
+
+size_t moev_verify_step_attn_workspace_size(const moev_model* m, const moev_attn* a, int B, int K);
+moev_status moev_verify_step_attn(const moev_model* m, const moev_attn* a, const int32_t* tokens,
+                                  int B, int K, int32_t* pos, int32_t* greedy, int32_t* n_accept,
+                                  int32_t* commit, int32_t* commit_len, int32_t* next_last,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

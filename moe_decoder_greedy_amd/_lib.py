@@ -39,6 +39,14 @@ class DraftWeights(ctypes.Structure):
 
 STAGES = {"route": 0, "permute": 1, "gate_up": 2, "down": 3, "combine": 4, "head": 5}
 
+class AttnLayer(ctypes.Structure):
+    _fields_ = [("w_qkv", c_void_p), ("w_o", c_void_p), ("k_cache", c_void_p), ("v_cache", c_void_p)]
+
+
+class Attn(ctypes.Structure):
+    _fields_ = [("n_heads", c_int), ("max_len", c_int), ("layers", ctypes.POINTER(AttnLayer))]
+
+
 # name -> (restype, argtypes); mirrors include/moev.h
 SIGNATURES = {
     "moev_status_string": (ctypes.c_char_p, [c_int]),
@@ -79,6 +87,11 @@ SIGNATURES = {
     "moev_spec_step": (c_int, [ctypes.POINTER(Model), ctypes.POINTER(DraftWeights), c_void_p, c_int, c_int,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                c_size_t, c_void_p]),
+    "moev_verify_step_attn_workspace_size": (c_size_t, [ctypes.POINTER(Model), ctypes.POINTER(Attn), c_int,
+                                                         c_int]),
+    "moev_verify_step_attn": (c_int, [ctypes.POINTER(Model), ctypes.POINTER(Attn), c_void_p, c_int, c_int,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]),
     "moev_attn_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                  c_int, c_int, c_void_p, c_void_p]),
     "moev_prefill_workspace_size": (c_size_t, [ctypes.POINTER(Model), c_int, c_int]),

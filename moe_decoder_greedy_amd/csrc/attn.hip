@@ -240,6 +240,16 @@ void launch_attn_t(const float* q, const void* kc, const void* vc, const int32_t
 }
 
 }  // namespace
+
+void launch_attn_decode(const float* q, const void* k_cache, const void* v_cache, const int32_t* pos,
+                        int B, int rows, int max_len, int H, int n_heads, int dt, float* out,
+                        hipStream_t s) {
+  if (dt == MOEV_BF16)
+    launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, out, s);
+  else
+    launch_attn_t<float>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, out, s);
+}
+
 }  // namespace moev
 
 extern "C" moev_status moev_attn_decode(const float* q, const void* k_cache, const void* v_cache,
@@ -261,9 +271,6 @@ extern "C" moev_status moev_attn_decode(const float* q, const void* k_cache, con
   MOEV_CHECK(need_ptr(q, "q") && need_ptr(k_cache, "k_cache") && need_ptr(v_cache, "v_cache") &&
                  need_ptr(pos, "pos", 4) && need_ptr(out, "out"),
              MOEV_ERR_INVALID_ARG);
-  if (dt == MOEV_BF16)
-    launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, out, as_stream(stream));
-  else
-    launch_attn_t<float>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, out, as_stream(stream));
+  launch_attn_decode(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, dt, out, as_stream(stream));
   return launch_status("moev_attn_decode");
 }

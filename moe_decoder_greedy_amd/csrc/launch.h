@@ -105,6 +105,11 @@ void launch_norm_cast(const float* h, const float* y, int S, const void* gamma, 
 void launch_verify(const int32_t* tokens, const int32_t* greedy, int B, int K, int32_t* n_accept,
                    int32_t* commit, int32_t* commit_len, int32_t* next_last, hipStream_t s);
 
+// Decode attention (moev_attn_decode's kernel, arguments already checked).
+void launch_attn_decode(const float* q, const void* k_cache, const void* v_cache, const int32_t* pos,
+                        int B, int rows, int max_len, int H, int n_heads, int dt, float* out,
+                        hipStream_t s);
+
 size_t grouped_ffn_ws_bytes(int T, int I, int k, int ns, int dt);
 size_t lmhead_ws_bytes(int T, int H, int V, int dt);
 

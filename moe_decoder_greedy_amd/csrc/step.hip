@@ -129,11 +129,96 @@ extern "C" size_t moev_verify_step_workspace_size(const moev_model* m, int B, in
 namespace moev {
 namespace {
 
+// The attention sublayer's device buffers and weights for one pass (see
+// moev_verify_step_attn); rows = K + 1 verify rows per sequence.
+struct AttnHook {
+  const moev_attn* a;
+  int B, rows;
+  const int32_t* pos;
+  int32_t* list;   // [T] = 0 .. T-1: every row in the one group of the dense GEMMs
+  int32_t* count;  // [1] = T
+  float* qkv;      // [T, 3H]
+  float* q;        // [T, H]
+  float* o;        // [T, H] attention output
+  float* ao;       // [T, H] its W_o projection, folded into the router's residual add
+};
+
+constexpr int kAttnRowThreads = 256;
+
+// list[t] = t, count[0] = T: the dense projections run on the expert-list
+// GEMM as one group holding every row.
+__global__ void dense_list_kernel(int32_t* list, int32_t* count, int T) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < T) list[t] = t;
+  if (t == 0) count[0] = T;
+}
+
+// Row t = b*rows + i of [q | k | v]: q to its own fp32 buffer, k and v rounded
+// to the cache type at position p0 + i of sequence b's caches, p0 = pos[b]
+// clamped as the attention kernel clamps it.
+template <typename WT>
+__global__ __launch_bounds__(kAttnRowThreads) void kv_scatter_kernel(
+    const float* __restrict__ qkv, const int32_t* __restrict__ pos, int rows, int max_len, int H,
+    float* __restrict__ q, WT* __restrict__ kc, WT* __restrict__ vc) {
+  const int t = blockIdx.x;
+  const int b = t / rows, i = t - b * rows;
+  const int p = min(max(pos[b], 0), max_len - rows) + i;
+  const float* src = qkv + static_cast<long long>(t) * 3 * H;
+  const long long dst = (static_cast<long long>(b) * max_len + p) * H;
+  for (int c = threadIdx.x; c < H; c += kAttnRowThreads) {
+    q[static_cast<long long>(t) * H + c] = src[c];
+    kc[dst + c] = from_f32<WT>(src[H + c]);
+    vc[dst + c] = from_f32<WT>(src[2 * H + c]);
+  }
+}
+
+// fp32 -> the GEMM operand type, n elements
+template <typename WT>
+__global__ __launch_bounds__(kAttnRowThreads) void cast_kernel(const float* __restrict__ x, long long n,
+                                                               WT* __restrict__ y) {
+  const long long i = static_cast<long long>(blockIdx.x) * kAttnRowThreads + threadIdx.x;
+  if (i < n) y[i] = from_f32<WT>(x[i]);
+}
+
+__global__ void pos_advance_kernel(int32_t* pos, const int32_t* commit_len, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) pos[b] += commit_len[b];
+}
+
+// The attention sublayer of layer l on the residual stream h (to which the
+// previous layer's expert slots y_prev are added first).  Leaves its output
+// projection in hook.ao for the router to add.
+void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h, const float* y_prev,
+                       int S, void* x, hipStream_t s) {
+  const moev_attn_layer& al = at.a->layers[l];
+  const int H = m->hidden, dt = m->dtype, T = at.B * at.rows;
+  launch_norm_cast(h, y_prev, S, nullptr, m->eps, T, H, dt, x, h, s);
+  launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_qkv, T, 3 * H, H, 0, 0, 1, dt, at.qkv, s, true);
+  if (dt == MOEV_BF16)
+    kv_scatter_kernel<u16><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, at.q,
+                                                         static_cast<u16*>(al.k_cache),
+                                                         static_cast<u16*>(al.v_cache));
+  else
+    kv_scatter_kernel<float><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, at.q,
+                                                           static_cast<float*>(al.k_cache),
+                                                           static_cast<float*>(al.v_cache));
+  launch_attn_decode(at.q, al.k_cache, al.v_cache, at.pos, at.B, at.rows, at.a->max_len, H,
+                     at.a->n_heads, dt, at.o, s);
+  const long long n = static_cast<long long>(T) * H;
+  const unsigned nb = static_cast<unsigned>((n + kAttnRowThreads - 1) / kAttnRowThreads);
+  if (dt == MOEV_BF16)
+    cast_kernel<u16><<<nb, kAttnRowThreads, 0, s>>>(at.o, n, static_cast<u16*>(x));
+  else
+    cast_kernel<float><<<nb, kAttnRowThreads, 0, s>>>(at.o, n, static_cast<float*>(x));
+  launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_o, T, H, H, 0, 0, 1, dt, at.ao, s, true);
+}
+
 // Embedding and the decoder layers for T rows.  On return h holds the residual
 // stream before the last layer's expert outputs, y those outputs: the caller
 // folds the last combine into whatever reads h next.
 void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLayout& L,
-                unsigned char* base, const moev_step_probe* probe, hipStream_t s) {
+                unsigned char* base, const moev_step_probe* probe, hipStream_t s,
+                const AttnHook* at = nullptr) {
   float* h = reinterpret_cast<float*>(base + L.h);
   void* x = base + L.x;
   int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
@@ -165,9 +250,17 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
   for (int l = 0; l < m->n_layers; ++l) {
     const moev_layer_weights& lw = m->layers[l];
     const float* y_prev = l > 0 ? y : nullptr;
+    int s_prev = S;
+    if (at != nullptr) {
+      // attention first: the previous layer's slots go into h there, and the
+      // router adds the attention's output projection as a single slot
+      run_attn_sublayer(m, *at, l, h, y_prev, S, x, s);
+      y_prev = at->ao;
+      s_prev = 1;
+    }
     int32_t* cnt = counts + static_cast<size_t>(l) * G;
     mark(MOEV_STAGE_ROUTE, l, false);
-    launch_route_fused(h, y_prev, S, h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, dt, x,
+    launch_route_fused(h, y_prev, s_prev, h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, dt, x,
                        idx, w, s, lists ? cnt : nullptr, lists ? sorted : nullptr, S);
     mark(MOEV_STAGE_ROUTE, l, true);
     mark(MOEV_STAGE_PERMUTE, l, false);
@@ -191,7 +284,7 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
 moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, int32_t* greedy,
                      int32_t* n_accept, int32_t* commit, int32_t* commit_len, int32_t* next_last,
                      void* ws, size_t ws_bytes, const moev_step_probe* probe, void* stream,
-                     float* h_final = nullptr) {
+                     float* h_final = nullptr, const AttnHook* at = nullptr) {
   if (moev_status st = validate_model(m, B, K)) return st;
   if (B == 0) return MOEV_OK;
   MOEV_CHECK(need_ptr(tokens, "tokens", 4) && need_ptr(greedy, "greedy", 4) &&
@@ -211,7 +304,7 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
 
   unsigned char* base = static_cast<unsigned char*>(ws);
   const hipStream_t s = as_stream(stream);
-  run_layers(m, tokens, T, L, base, probe, s);
+  run_layers(m, tokens, T, L, base, probe, s, at);
   const int S = m->top_k + m->n_shared;
   float* h = reinterpret_cast<float*>(base + L.h);
   float* y = reinterpret_cast<float*>(base + L.y);
@@ -379,4 +472,98 @@ extern "C" moev_status moev_spec_step(const moev_model* m, const moev_draft_weig
   run_draft(*m, *d, hf, n_accept, K + 1, next_last, B, K, next_tokens, K + 1, 1, next_tokens,
             nullptr, base + S.draft, as_stream(stream));
   return launch_status("moev_spec_step");
+}
+
+namespace moev {
+namespace {
+
+// Attention step workspace: the verify step's, then the dense-GEMM row list
+// and the attention sublayer's buffers.
+struct AttnLayout {
+  size_t list, count, qkv, q, o, ao, total;
+};
+
+AttnLayout attn_layout(const moev_model& m, int B, int K) {
+  const int T = B * (K + 1);
+  const size_t rowf = static_cast<size_t>(T) * m.hidden * 4;
+  AttnLayout A{};
+  size_t o = layout(m, T).total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes, 256);
+    return at;
+  };
+  A.list = take(static_cast<size_t>(T) * 4);
+  A.count = take(4);
+  A.qkv = take(3 * rowf);
+  A.q = take(rowf);
+  A.o = take(rowf);
+  A.ao = take(rowf);
+  A.total = o;
+  return A;
+}
+
+moev_status validate_attn(const moev_model* m, const moev_attn* a, int B, int K) {
+  MOEV_REQUIRE(a != nullptr, MOEV_ERR_INVALID_ARG, "attention weights must not be NULL");
+  MOEV_REQUIRE(K + 1 <= 16, MOEV_ERR_UNSUPPORTED, "K=%d: attention takes at most 16 rows per sequence", K);
+  MOEV_REQUIRE(static_cast<long long>(B) * (K + 1) <= kListMaxTokens, MOEV_ERR_UNSUPPORTED,
+               "B*(K+1)=%lld rows exceeds %d", static_cast<long long>(B) * (K + 1), kListMaxTokens);
+  MOEV_REQUIRE(a->n_heads >= 1 && m->hidden % a->n_heads == 0, MOEV_ERR_UNSUPPORTED,
+               "hidden size %d must be a multiple of n_heads=%d", m->hidden, a->n_heads);
+  const int D = m->hidden / a->n_heads;
+  MOEV_REQUIRE(D == 64 || D == 128 || D == 256, MOEV_ERR_UNSUPPORTED, "head width %d must be 64, 128 or 256",
+               D);
+  MOEV_REQUIRE(a->max_len >= K + 1, MOEV_ERR_INVALID_ARG, "max_len=%d must be >= K+1=%d", a->max_len, K + 1);
+  MOEV_REQUIRE(m->n_layers == 0 || a->layers != nullptr, MOEV_ERR_INVALID_ARG,
+               "attention layers must not be NULL");
+  for (int l = 0; l < m->n_layers; ++l) {
+    const moev_attn_layer& al = a->layers[l];
+    if (!(need_ptr(al.w_qkv, "attn.w_qkv") && need_ptr(al.w_o, "attn.w_o") &&
+          need_ptr(al.k_cache, "attn.k_cache") && need_ptr(al.v_cache, "attn.v_cache"))) {
+      set_error("attention layer %d: %s", l, moev_last_error());
+      return MOEV_ERR_INVALID_ARG;
+    }
+  }
+  return MOEV_OK;
+}
+
+}  // namespace
+}  // namespace moev
+
+extern "C" size_t moev_verify_step_attn_workspace_size(const moev_model* m, const moev_attn* a, int B,
+                                                       int K) {
+  if (m == nullptr || a == nullptr || B < 0 || K < 0) return 0;
+  return moev::attn_layout(*m, B, K).total;
+}
+
+extern "C" moev_status moev_verify_step_attn(const moev_model* m, const moev_attn* a, const int32_t* tokens,
+                                             int B, int K, int32_t* pos, int32_t* greedy, int32_t* n_accept,
+                                             int32_t* commit, int32_t* commit_len, int32_t* next_last,
+                                             void* ws, size_t ws_bytes, void* stream) {
+  using namespace moev;
+  clear_error();
+  if (moev_status st = validate_model(m, B, K)) return st;
+  if (moev_status st = validate_attn(m, a, B, K)) return st;
+  if (B == 0) return MOEV_OK;
+  MOEV_CHECK(need_ptr(pos, "pos", 4) && need_ptr(commit_len, "commit_len", 4) &&
+                 need_ptr(next_last, "next_last", 4),
+             MOEV_ERR_INVALID_ARG);
+  const AttnLayout A = attn_layout(*m, B, K);
+  MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE,
+               "workspace must be non-NULL and 16-byte aligned");
+  MOEV_REQUIRE(ws_bytes >= A.total, MOEV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes,
+               A.total);
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  const hipStream_t s = as_stream(stream);
+  const int T = B * (K + 1);
+  const AttnHook at{a, B, K + 1, pos,
+                    reinterpret_cast<int32_t*>(base + A.list), reinterpret_cast<int32_t*>(base + A.count),
+                    reinterpret_cast<float*>(base + A.qkv), reinterpret_cast<float*>(base + A.q),
+                    reinterpret_cast<float*>(base + A.o), reinterpret_cast<float*>(base + A.ao)};
+  dense_list_kernel<<<(T + 255) / 256, 256, 0, s>>>(at.list, at.count, T);
+  if (moev_status st = run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last, ws,
+                                ws_bytes, nullptr, stream, nullptr, &at))
+    return st;
+  pos_advance_kernel<<<(B + 255) / 256, 256, 0, s>>>(pos, commit_len, B);
+  return launch_status("moev_verify_step_attn");
 }

@@ -207,6 +207,49 @@ class DeviceModel:
             ws.numel(), stream_handle(stream)))
         return out
 
+    # ------------------------------------------------------ attention sublayer
+    def attach_attention(self, attn: list, n_heads: int, batch: int, max_len: int) -> None:
+        """Upload per-layer attention projections (as ``synth.attention_weights``:
+        W_q, W_k, W_v, W_o [H, H]; the first three are stacked into one packed
+        [3H, H] matrix) and allocate zeroed key/value caches [batch, max_len, H]
+        per layer in the model dtype."""
+        dt = self.dtype
+        H = self.shape.hidden
+        cdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        self.attn = []
+        for a in attn:
+            qkv = np.concatenate([a["w_q"], a["w_k"], a["w_v"]], axis=0)
+            self.attn.append({"w_qkv": pack_weights(to_device(qkv, dt, self.device)),
+                              "w_o": pack_weights(to_device(a["w_o"], dt, self.device)),
+                              "k": torch.zeros((batch, max_len, H), dtype=cdt, device=self.device),
+                              "v": torch.zeros((batch, max_len, H), dtype=cdt, device=self.device)})
+        self._c_attn_layers = (_lib.AttnLayer * max(len(self.attn), 1))()
+        for i, A in enumerate(self.attn):
+            self._c_attn_layers[i] = _lib.AttnLayer(ptr(A["w_qkv"]), ptr(A["w_o"]), ptr(A["k"]), ptr(A["v"]))
+        self._c_attn = _lib.Attn(n_heads, max_len, self._c_attn_layers)
+        self.attn_batch = batch
+
+    @property
+    def c_attn(self):
+        return ctypes.byref(self._c_attn)
+
+    def verify_step_attn(self, tokens: torch.Tensor, pos: torch.Tensor, out: Optional[dict] = None,
+                         stream=None) -> dict:
+        """One verify pass with attention (``moev_verify_step_attn``): tokens
+        int32 [B, K+1] at positions pos[b] .. pos[b]+K of the caches; ``pos``
+        (int32 [B] on the GPU) advances by commit_len."""
+        B, K1 = tokens.shape
+        K = K1 - 1
+        assert B == self.attn_batch, "the caches were allocated for another batch"
+        out = self.alloc_outputs(B, K) if out is None else out
+        ws = self._ws_named(("attn", B, K),
+                            lib().moev_verify_step_attn_workspace_size(self.c_model, self.c_attn, B, K))
+        check("moev_verify_step_attn", lib().moev_verify_step_attn(
+            self.c_model, self.c_attn, ptr(tokens), B, K, ptr(pos), ptr(out["greedy"]), ptr(out["n_accept"]),
+            ptr(out["commit"]), ptr(out["commit_len"]), ptr(out["next_last"]), ptr(ws), ws.numel(),
+            stream_handle(stream)))
+        return out
+
     def greedy(self, tokens: torch.Tensor) -> torch.Tensor:
         """Greedy successor of every token (a K = 0 step)."""
         return self.verify_step(tokens.reshape(-1, 1).to(torch.int32).contiguous())["greedy"].reshape(-1)

@@ -512,18 +512,23 @@ def cached_greedy(tokens: np.ndarray, model: dict, attn: list, caches: list, pos
                   n_heads: int, operands: str = "bf16") -> dict:
     """Greedy tokens of the decoder with an attention sublayer before every
     MoE sublayer (tokens int [B, rows], row i of sequence b at position
-    pos[b] + i; ``caches`` one {"k", "v"} per layer, updated in place)."""
+    pos[b] + i; ``caches`` one {"k", "v"} per layer, updated in place).
+    Also returns each row's head gap and its smallest router gap over the
+    layers (the near-tie margins of the greedy token)."""
     shape = model["shape"]
     dt = model["dtype"]
     tokens = np.asarray(tokens, np.int64)
     B, rows = tokens.shape
     h = embed(tokens.reshape(-1), model["emb"], dt)
+    min_rgap = np.full(B * rows, np.inf)
     for layer, at, cache in zip(model["layers"], attn, caches):
         h = attn_sublayer(h, at, cache, pos, rows, n_heads, dt, shape.eps, operands)
-        h = moe_layer(h, layer, dt, shape.top_k, shape.n_routed, shape.n_shared, shape.eps,
-                      operands)["h_out"]
+        st = moe_layer(h, layer, dt, shape.top_k, shape.n_routed, shape.n_shared, shape.eps, operands)
+        min_rgap = np.minimum(min_rgap, st["gap"])
+        h = st["h_out"]
     head = lm_head(h, model["norm_f"], model["w_lm"], dt, shape.eps, operands)
-    return {"argmax": head["argmax"].reshape(B, rows), "gap": head["gap"].reshape(B, rows), "h": h}
+    return {"argmax": head["argmax"].reshape(B, rows), "gap": head["gap"].reshape(B, rows), "h": h,
+            "router_gap": min_rgap.reshape(B, rows)}
 
 
 def cached_verify_step(last: np.ndarray, drafts: np.ndarray, model: dict, attn: list, caches: list,
@@ -536,8 +541,9 @@ def cached_verify_step(last: np.ndarray, drafts: np.ndarray, model: dict, attn: 
     tokens = np.concatenate([last, np.asarray(drafts, np.int64).reshape(last.shape[0], -1)], axis=1)
     fwd = cached_greedy(tokens, model, attn, caches, pos, n_heads, operands)
     n_acc, commit, clen, nxt = mtp_verify(tokens, fwd["argmax"])
-    return {"greedy": fwd["argmax"], "gap": fwd["gap"], "n_accept": n_acc, "commit": commit,
-            "commit_len": clen, "next_last": nxt, "pos": np.asarray(pos) + n_acc + 1}
+    return {"greedy": fwd["argmax"], "gap": fwd["gap"], "router_gap": fwd["router_gap"],
+            "n_accept": n_acc, "commit": commit, "commit_len": clen, "next_last": nxt,
+            "pos": np.asarray(pos) + n_acc + 1}
 
 
 def cached_rollout(last: np.ndarray, model: dict, attn: list, caches: list, pos: np.ndarray,

@@ -187,3 +187,31 @@ def test_attn_decode_validation(lib):
     assert call(B=0, q=None, k=None, v=None, pos=None, out=None) == OK
     assert call(q=None) == INVALID and "q" in _err(lib)
     assert call(pos=FAKE + 2) == INVALID and "aligned" in _err(lib)
+
+
+def test_verify_step_attn_validation(lib):
+    layers = (_lib.LayerWeights * 1)(_lib.LayerWeights(None, FAKE, None, FAKE, FAKE, FAKE))
+    m = _lib.Model(1280, 64, 896, 6, 2, 129280, 1, BF16, 1e-6, FAKE, None, FAKE, layers)
+    al = (_lib.AttnLayer * 1)(_lib.AttnLayer(FAKE, FAKE, FAKE, None))
+    a = _lib.Attn(10, 2400, al)
+    ws = lib.moev_verify_step_attn_workspace_size(ctypes.byref(m), ctypes.byref(a), 32, 3)
+    assert ws > lib.moev_verify_step_workspace_size(ctypes.byref(m), 32, 3)
+    assert lib.moev_verify_step_attn_workspace_size(ctypes.byref(m), None, 32, 3) == 0
+
+    def step(attn=ctypes.byref(a), B=32, K=3, pos=FAKE, n=ws):
+        return lib.moev_verify_step_attn(ctypes.byref(m), attn, FAKE, B, K, pos, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, n, None)
+
+    assert step() == INVALID and "attention layer 0" in _err(lib) and "v_cache" in _err(lib)
+    assert step(attn=None) == INVALID
+    assert step(K=16) == UNSUPPORTED and "16 rows" in _err(lib)
+    assert step(B=200, K=3) == UNSUPPORTED and "exceeds 512" in _err(lib)
+    a.n_heads = 16                                    # 80-wide heads
+    assert step() == UNSUPPORTED and "head width" in _err(lib)
+    a.n_heads, a.max_len = 10, 3
+    assert step() == INVALID and "max_len" in _err(lib)
+    a.max_len = 2400
+    al[0].v_cache = FAKE
+    assert step(pos=None) == INVALID and "pos" in _err(lib)
+    assert step(n=ws - 1) == WORKSPACE
+    assert step(B=0) == OK

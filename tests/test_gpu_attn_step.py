@@ -1,0 +1,165 @@
+"""Verify steps with an attention sublayer in every layer
+(moev_verify_step_attn): parity with the oracle's cached decoder, and
+losslessness against the GPU's own one-row greedy rollout over the same
+caches."""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import dev_i32, host, need_gpu, report
+
+pytestmark = pytest.mark.gpu
+
+HEAD_GAP, ROUTE_GAP = 1e-2, 1e-3
+
+# two bf16 layers with the decoder's 128-wide heads
+ATTN_BF16 = synth.ModelShape("attn_bf16", hidden=256, n_routed=16, inter=128, top_k=4, n_shared=2,
+                             vocab=2048, n_layers=2, dtype="bf16", model_id=5)
+
+
+@pytest.fixture(scope="module")
+def model_mod():
+    need_gpu()
+    from moe_decoder_greedy_amd import model
+    return model
+
+
+def _prefix_caches(shape, B, rows, L, prefix, seed):
+    """Per layer a key and a value cache [B, L, H] with seeded values at every
+    position (those at and past pos[b] are overwritten before they are read),
+    and the per-sequence prefix lengths pos."""
+    out = []
+    for layer in range(shape.n_layers):
+        a = synth.attention_inputs(B, rows, shape.hidden, L, prefix, seed=seed + layer,
+                                   bf16=shape.dtype == "bf16")
+        out.append(a)
+    return out, out[0]["pos"].astype(np.int64)
+
+
+def _oracle_caches(raw, dt):
+    return [{"k": oracle.to_f64(a["k_cache"], dt), "v": oracle.to_f64(a["v_cache"], dt)} for a in raw]
+
+
+def _load_caches(dm, raw):
+    for A, a in zip(dm.attn, raw):
+        for key, src in (("k", a["k_cache"]), ("v", a["v_cache"])):
+            t = torch.from_numpy(src.view(np.int16)).view(torch.bfloat16) if src.dtype == np.uint16 \
+                else torch.from_numpy(src)
+            A[key].copy_(t.to(A[key].device))
+
+
+def _gpu_cache(A, key):
+    t = A[key]
+    return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy().astype(np.float64)
+
+
+def test_attn_step_tiny_matches_oracle(model_mod):
+    """The tiny fp32 model, 3 sequences, K = 3, four passes: unflagged greedy
+    tokens equal the oracle's, acceptance follows them, every cache row the
+    passes wrote matches the oracle's, and pos advances by commit_len."""
+    shape, heads = synth.TINY, 2
+    w = synth.model_weights(shape)
+    attn = synth.attention_weights(shape)
+    B, K, L = 3, 3, 48
+    raw, pos = _prefix_caches(shape, B, K + 1, L, (0, 20), seed=41)
+    dm = model_mod.DeviceModel(w)
+    dm.attach_attention(attn, heads, B, L)
+    _load_caches(dm, raw)
+    caches = _oracle_caches(raw, shape.dtype)
+    pos_d = dev_i32(pos.astype(np.int32))
+    rng = np.random.default_rng(9)
+    for step in range(4):
+        tokens = rng.integers(0, shape.vocab, size=(B, K + 1)).astype(np.int64)
+        if step % 2 == 1:   # the first draft right, so acceptance varies
+            probe = oracle.cached_greedy(tokens[:, :1], w, attn, copy.deepcopy(caches), pos, heads, "exact")
+            tokens[:, 1] = probe["argmax"][:, 0]
+        ref = oracle.cached_greedy(tokens, w, attn, caches, pos, heads, "exact")
+        out = dm.verify_step_attn(dev_i32(tokens.astype(np.int32)), pos_d)
+        gg = host(out["greedy"])
+        flagged = (ref["gap"] < HEAD_GAP) | (ref["router_gap"] < ROUTE_GAP)
+        report("attn_step_tiny", step=step, pos=pos.tolist(), flagged=int(flagged.sum()))
+        np.testing.assert_array_equal(gg[~flagged], ref["argmax"][~flagged])
+        n, c, l, nx = oracle.mtp_verify(tokens, gg)
+        np.testing.assert_array_equal(host(out["n_accept"]), n)
+        np.testing.assert_array_equal(host(out["commit"]), c)
+        np.testing.assert_array_equal(host(out["next_last"]), nx)
+        for A, cache in zip(dm.attn, caches):
+            for key in ("k", "v"):
+                got = _gpu_cache(A, key)
+                for b in range(B):
+                    rows = slice(int(pos[b]), int(pos[b]) + K + 1)
+                    np.testing.assert_allclose(got[b, rows], cache[key][b, rows], rtol=1e-4, atol=1e-5)
+        pos = pos + l
+        np.testing.assert_array_equal(host(pos_d), pos)
+
+
+def _rollout(dm, last, pos0, n):
+    """n greedy tokens per sequence, one row per pass (K = 0)."""
+    cur = torch.from_numpy(last.astype(np.int32)).cuda().reshape(-1, 1)
+    pos = dev_i32(pos0.astype(np.int32))
+    seq = []
+    for _ in range(n):
+        out = dm.verify_step_attn(cur, pos)
+        cur = out["next_last"].reshape(-1, 1).clone()
+        seq.append(host(cur)[:, 0])
+    return np.stack(seq, axis=1)
+
+
+@pytest.mark.parametrize("K", [1, 3])
+def test_attn_step_is_lossless(model_mod, K):
+    """Speculative passes with drafts right with probability 0.7 commit exactly
+    the tokens of one-row greedy decoding from the same caches, bit for bit,
+    although every pass writes cache rows for drafts that are then rejected.
+    The first pass's unflagged greedy tokens also equal the oracle's (bf16
+    operands)."""
+    shape, heads = ATTN_BF16, 2
+    w = synth.model_weights(shape)
+    attn = synth.attention_weights(shape)
+    B, steps = 8, 10
+    L = 120 + steps * (K + 1) + K + 2
+    raw, pos0 = _prefix_caches(shape, B, K + 1, L, (0, 120), seed=51)
+    dm = model_mod.DeviceModel(w)
+    dm.attach_attention(attn, heads, B, L)
+    last0 = synth.initial_tokens(B, shape.vocab).astype(np.int64)
+    _load_caches(dm, raw)
+    ref = _rollout(dm, last0, pos0, steps * (K + 1) + 1)
+
+    _load_caches(dm, raw)
+    rng = np.random.default_rng(K)
+    pos_d = dev_i32(pos0.astype(np.int32))
+    last = last0.copy()
+    done = np.zeros(B, np.int64)
+    commits = [[] for _ in range(B)]
+    for step in range(steps):
+        drafts = np.empty((B, K), np.int64)
+        for b in range(B):
+            for j in range(K):
+                right = ref[b, done[b] + j]
+                drafts[b, j] = right if rng.random() < 0.7 else rng.integers(0, shape.vocab)
+        tokens = np.concatenate([last[:, None], drafts], axis=1)
+        if step == 0:
+            orc = oracle.cached_greedy(tokens, w, attn, _oracle_caches(raw, shape.dtype), pos0, heads, "bf16")
+        out = dm.verify_step_attn(dev_i32(tokens.astype(np.int32)), pos_d)
+        if step == 0:
+            flagged = (orc["gap"] < HEAD_GAP) | (orc["router_gap"] < ROUTE_GAP)
+            gg = host(out["greedy"])
+            report("attn_step_bf16", flagged=int(flagged.sum()), mismatches=int((gg != orc["argmax"]).sum()))
+            np.testing.assert_array_equal(gg[~flagged], orc["argmax"][~flagged])
+        clen = host(out["commit_len"])
+        cm = host(out["commit"])
+        for b in range(B):
+            commits[b].extend(cm[b, :clen[b]].tolist())
+        done += clen
+        last = host(out["next_last"]).astype(np.int64)
+    np.testing.assert_array_equal(host(pos_d), pos0 + done)
+    accepted = 0
+    for b in range(B):
+        n = len(commits[b])
+        accepted += n
+        np.testing.assert_array_equal(np.array(commits[b]), ref[b, :n])
+    report("attn_step_lossless", K=K, committed=accepted, tau=accepted / (B * steps))
+    assert accepted > B * steps   # some drafts were accepted
