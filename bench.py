@@ -33,7 +33,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="verify_step_b32k3",
                     help="verify_step_b32k{3,2,1,0} | zipf_verify_b{1,8,32,128}k{1,3} | decode_layer_t128 | "
-                         "prefill_layer_t9760 | prefill_model_t9760 | kselect_b32 | spec_loop_b32k3 | attn_decode_b32k3")
+                         "prefill_layer_t9760 | prefill_model_t9760 | kselect_b32 | spec_loop_b32k3 | attn_decode_b32k3 | "
+                         "verify_attn_b32k3")
     ap.add_argument("--launch", choices=("auto", "eager", "graph"), default="auto")
     ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -526,6 +527,104 @@ def run_attn(args, torch, np):
     }
 
 
+def run_verify_attn(args, torch, np):
+    """The verify step with an attention sublayer in every layer
+    (moev_verify_step_attn): the 12-layer decoder, 32 sequences x (1 + K=3)
+    rows, 10 heads of 128, every sequence's cache holding 1220-2300 positions
+    (the same seeded prefix in every layer).  Drafts are seeded random tokens:
+    the pass does the same work whatever is accepted, and pos advances by
+    commit_len each step.  The roofline is the attention kernel's (the largest
+    per-step kernel here), timed alone on layer 0's caches at the final
+    positions."""
+    import synth
+    from moe_decoder_greedy_amd import model as mdl
+    from moe_decoder_greedy_amd import ops
+
+    shape = synth.DECODER
+    B, K, heads, rows = 32, 3, 10, 4
+    H, V = shape.hidden, shape.vocab
+    n_steps = args.warmup + args.steps
+    L = 2300 + rows * n_steps + 8
+    t0 = time.perf_counter()
+    weights = synth.model_weights(shape)
+    attn = synth.attention_weights(shape)
+    a = synth.attention_inputs(B, rows, H, L, (1220, 2300), seed=7)
+    log(f"weights and caches generated in {time.perf_counter() - t0:.1f} s")
+    dm = mdl.DeviceModel(weights)
+    dm.attach_attention(attn, heads, B, L)
+    kc = torch.from_numpy(a["k_cache"].view(np.int16)).cuda().view(torch.bfloat16)
+    vc = torch.from_numpy(a["v_cache"].view(np.int16)).cuda().view(torch.bfloat16)
+    for A in dm.attn:
+        A["k"].copy_(kc)
+        A["v"].copy_(vc)
+    del kc, vc
+    pos0 = a["pos"].astype(np.int32)
+    pos_d = torch.from_numpy(pos0.copy()).cuda()
+    rng = np.random.default_rng(11)
+    toks = rng.integers(0, V, size=(n_steps, B, K + 1)).astype(np.int32)
+    toks_d = torch.from_numpy(toks).cuda()
+    outs = dm.alloc_outputs(B, K)
+    for s in range(args.warmup):
+        dm.verify_step_attn(toks_d[s], pos_d, out=outs)
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    for s in range(args.warmup, n_steps):
+        dm.verify_step_attn(toks_d[s], pos_d, out=outs)
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - ta) / args.steps
+    pos_end = pos_d.cpu().numpy()
+    log(f"step with attention: {t * 1e3:.3f} ms, pos advanced by {int((pos_end - pos0).sum())} over "
+        f"{n_steps} steps")
+
+    # the attention kernel alone, on layer 0's caches at the final positions
+    q = torch.randn((B * rows, H), generator=torch.Generator(device="cuda").manual_seed(3), device="cuda")
+    o = torch.empty((B * rows, H), dtype=torch.float32, device="cuda")
+    A0 = dm.attn[0]
+    for _ in range(5):
+        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, heads, out=o)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n_att = 50
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(n_att):
+        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, heads, out=o)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_att = ev[0].elapsed_time(ev[1]) * 1e-3 / n_att
+    visible = int((np.minimum(pos_end.astype(np.int64), L - rows) + rows).sum())
+    nbytes = visible * H * 2 * 2 + 2 * B * rows * H * 4
+    gbs = nbytes / t_att / 1e9
+    log(f"attention alone: {t_att * 1e6:.1f} us, {nbytes / 1e6:.1f} MB, {gbs:.0f} GB/s; "
+        f"x{shape.n_layers} = {t_att * shape.n_layers * 1e3:.3f} ms of the step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        caches = [{"k": oracle.to_f64(a["k_cache"][:1], "bf16"), "v": oracle.to_f64(a["v_cache"][:1], "bf16")}
+                  for _ in range(shape.n_layers)]
+        t0 = time.perf_counter()
+        oracle.cached_verify_step(toks[0, :1, 0], toks[0, :1, 1:], weights, attn, caches, pos0[:1].astype(np.int64),
+                                  heads, "bf16")
+        dt_cpu = time.perf_counter() - t0
+        cpu = {"value": round(rows / dt_cpu, 2), "unit": "verified tokens/s", "cores": torch.get_num_threads(),
+               "kind": "oracle", "sample": f"one sequence's pass (1 of {B}; {rows} rows, prefix {int(pos0[0])}), "
+                                           "float64 numpy"}
+    T = B * rows
+    return {
+        "metric": "verified tokens/s, verify step with attention (32 seq x (1+K=3), 1220-2300 cached positions)",
+        "value": round(T / t, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded weights, caches and draft tokens)",
+        "config": {"workload": "verify_attn_b32k3", "batch": B, "drafts": K, "layers": shape.n_layers,
+                   "hidden": H, "heads": heads, "max_len": L, "prefix": [1220, 2300]},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_decode_kernel<bf16, 128> (one layer's attention)", "bytes_per_launch": nbytes,
+                     "avg_launch_us": round(t_att * 1e6, 2)},
+        "cpu_baseline": cpu,
+    }
+
+
 def run_verify(args, torch, np):
     import synth
     from moe_decoder_greedy_amd import model as mdl
@@ -799,6 +898,8 @@ def main():
         result = run_spec(args, torch, np)
     elif args.workload == "attn_decode_b32k3":
         result = run_attn(args, torch, np)
+    elif args.workload == "verify_attn_b32k3":
+        result = run_verify_attn(args, torch, np)
     elif args.workload == "prefill_model_t9760":
         result = run_prefill_model(args, torch, np)
     elif args.workload.endswith(("_t128", "_t9760")):

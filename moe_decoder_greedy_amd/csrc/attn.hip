@@ -61,10 +61,12 @@ template <typename WT, int N> __device__ __forceinline__ void ldn(const WT* p, f
 
 constexpr int kAttnWaves = 8;  // wavefronts per workgroup (key-range split)
 
-template <typename WT, int D, int R>
+// OT: output type (fp32, or the cache type when the output feeds a GEMM
+// directly; rounded once at the store)
+template <typename WT, int D, int R, typename OT>
 __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
     const float* __restrict__ q, const WT* __restrict__ kc, const WT* __restrict__ vc,
-    const int32_t* __restrict__ pos, int rows, int max_len, int H, float scale, float* __restrict__ out) {
+    const int32_t* __restrict__ pos, int rows, int max_len, int H, float scale, OT* __restrict__ out) {
   // Every fused multiply-add below is written out and no other is formed, so
   // the instantiations for different row counts round identically (the
   // compiler may otherwise fuse a*b + c*d either way round).
@@ -209,24 +211,28 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
       L = fmaf(l_s[w][r], f, L);
       O = fmaf(o_s[w][r][c], f, O);
     }
-    out[(static_cast<long long>(b) * rows + r) * H + col0 + c] = O / L;
+    out[(static_cast<long long>(b) * rows + r) * H + col0 + c] = from_f32<OT>(O / L);
   }
 }
 
-template <typename WT, int D>
+template <typename WT, int D, typename OT>
 void launch_attn_d(const float* q, const WT* k, const WT* v, const int32_t* pos, int B, int rows, int max_len,
-                   int H, int n_heads, float scale, float* out, hipStream_t s) {
+                   int H, int n_heads, float scale, OT* out, hipStream_t s) {
   const dim3 grid(B, n_heads);
   const dim3 block(kWave * kAttnWaves);
-  if (rows <= 1) attn_decode_kernel<WT, D, 1><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
-  else if (rows <= 4) attn_decode_kernel<WT, D, 4><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
-  else if (rows <= 8) attn_decode_kernel<WT, D, 8><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
-  else attn_decode_kernel<WT, D, 16><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
+  if (rows <= 1)
+    attn_decode_kernel<WT, D, 1, OT><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
+  else if (rows <= 4)
+    attn_decode_kernel<WT, D, 4, OT><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
+  else if (rows <= 8)
+    attn_decode_kernel<WT, D, 8, OT><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
+  else
+    attn_decode_kernel<WT, D, 16, OT><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
 }
 
-template <typename WT>
+template <typename WT, typename OT>
 void launch_attn_t(const float* q, const void* kc, const void* vc, const int32_t* pos, int B, int rows,
-                   int max_len, int H, int n_heads, float* out, hipStream_t s) {
+                   int max_len, int H, int n_heads, OT* out, hipStream_t s) {
   const int D = H / n_heads;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const WT* k = static_cast<const WT*>(kc);
@@ -242,12 +248,16 @@ void launch_attn_t(const float* q, const void* kc, const void* vc, const int32_t
 }  // namespace
 
 void launch_attn_decode(const float* q, const void* k_cache, const void* v_cache, const int32_t* pos,
-                        int B, int rows, int max_len, int H, int n_heads, int dt, float* out,
+                        int B, int rows, int max_len, int H, int n_heads, int dt, void* out, bool out_dt,
                         hipStream_t s) {
-  if (dt == MOEV_BF16)
-    launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, out, s);
-  else
-    launch_attn_t<float>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, out, s);
+  if (dt == MOEV_BF16) {
+    if (out_dt)
+      launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, static_cast<u16*>(out), s);
+    else
+      launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, static_cast<float*>(out), s);
+  } else {
+    launch_attn_t<float>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, static_cast<float*>(out), s);
+  }
 }
 
 }  // namespace moev
@@ -271,6 +281,6 @@ extern "C" moev_status moev_attn_decode(const float* q, const void* k_cache, con
   MOEV_CHECK(need_ptr(q, "q") && need_ptr(k_cache, "k_cache") && need_ptr(v_cache, "v_cache") &&
                  need_ptr(pos, "pos", 4) && need_ptr(out, "out"),
              MOEV_ERR_INVALID_ARG);
-  launch_attn_decode(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, dt, out, as_stream(stream));
+  launch_attn_decode(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, dt, out, false, as_stream(stream));
   return launch_status("moev_attn_decode");
 }

@@ -139,7 +139,6 @@ struct AttnHook {
   int32_t* count;  // [1] = T
   float* qkv;      // [T, 3H]
   float* q;        // [T, H]
-  float* o;        // [T, H] attention output
   float* ao;       // [T, H] its W_o projection, folded into the router's residual add
 };
 
@@ -172,14 +171,6 @@ __global__ __launch_bounds__(kAttnRowThreads) void kv_scatter_kernel(
   }
 }
 
-// fp32 -> the GEMM operand type, n elements
-template <typename WT>
-__global__ __launch_bounds__(kAttnRowThreads) void cast_kernel(const float* __restrict__ x, long long n,
-                                                               WT* __restrict__ y) {
-  const long long i = static_cast<long long>(blockIdx.x) * kAttnRowThreads + threadIdx.x;
-  if (i < n) y[i] = from_f32<WT>(x[i]);
-}
-
 __global__ void pos_advance_kernel(int32_t* pos, const int32_t* commit_len, int B) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) pos[b] += commit_len[b];
@@ -202,14 +193,9 @@ void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h,
     kv_scatter_kernel<float><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, at.q,
                                                            static_cast<float*>(al.k_cache),
                                                            static_cast<float*>(al.v_cache));
+  // the attention output goes straight into x in the operand type
   launch_attn_decode(at.q, al.k_cache, al.v_cache, at.pos, at.B, at.rows, at.a->max_len, H,
-                     at.a->n_heads, dt, at.o, s);
-  const long long n = static_cast<long long>(T) * H;
-  const unsigned nb = static_cast<unsigned>((n + kAttnRowThreads - 1) / kAttnRowThreads);
-  if (dt == MOEV_BF16)
-    cast_kernel<u16><<<nb, kAttnRowThreads, 0, s>>>(at.o, n, static_cast<u16*>(x));
-  else
-    cast_kernel<float><<<nb, kAttnRowThreads, 0, s>>>(at.o, n, static_cast<float*>(x));
+                     at.a->n_heads, dt, x, true, s);
   launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_o, T, H, H, 0, 0, 1, dt, at.ao, s, true);
 }
 
@@ -480,7 +466,7 @@ namespace {
 // Attention step workspace: the verify step's, then the dense-GEMM row list
 // and the attention sublayer's buffers.
 struct AttnLayout {
-  size_t list, count, qkv, q, o, ao, total;
+  size_t list, count, qkv, q, ao, total;
 };
 
 AttnLayout attn_layout(const moev_model& m, int B, int K) {
@@ -497,7 +483,6 @@ AttnLayout attn_layout(const moev_model& m, int B, int K) {
   A.count = take(4);
   A.qkv = take(3 * rowf);
   A.q = take(rowf);
-  A.o = take(rowf);
   A.ao = take(rowf);
   A.total = o;
   return A;
@@ -559,7 +544,7 @@ extern "C" moev_status moev_verify_step_attn(const moev_model* m, const moev_att
   const AttnHook at{a, B, K + 1, pos,
                     reinterpret_cast<int32_t*>(base + A.list), reinterpret_cast<int32_t*>(base + A.count),
                     reinterpret_cast<float*>(base + A.qkv), reinterpret_cast<float*>(base + A.q),
-                    reinterpret_cast<float*>(base + A.o), reinterpret_cast<float*>(base + A.ao)};
+                    reinterpret_cast<float*>(base + A.ao)};
   dense_list_kernel<<<(T + 255) / 256, 256, 0, s>>>(at.list, at.count, T);
   if (moev_status st = run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last, ws,
                                 ws_bytes, nullptr, stream, nullptr, &at))
