@@ -473,6 +473,13 @@ def run_spec(args, torch, np):
     }
 
 
+def head_major(torch, bits, heads):
+    """bf16 bit patterns [B, L, H] -> the kernels' head-major [B, heads, L, D] cache on the GPU."""
+    B, L, H = bits.shape
+    t = torch.from_numpy(bits.view("int16")).cuda().view(torch.bfloat16)
+    return t.view(B, L, heads, H // heads).permute(0, 2, 1, 3).contiguous()
+
+
 def run_attn(args, torch, np):
     """Decode attention of a verify pass (moev_attn_decode): 32 sequences x
     (1 + K=3) rows at the decoder's width (10 heads of 128) against cached
@@ -483,18 +490,17 @@ def run_attn(args, torch, np):
     from moe_decoder_greedy_amd import ops
     B, rows, H, heads, L = 32, 4, 1280, 10, 2400
     a = synth.attention_inputs(B, rows, H, L, (1220, 2300), seed=7)
-    kc = torch.from_numpy(a["k_cache"].view(np.int16)).cuda().view(torch.bfloat16)
-    vc = torch.from_numpy(a["v_cache"].view(np.int16)).cuda().view(torch.bfloat16)
+    kc, vc = (head_major(torch, a[key], heads) for key in ("k_cache", "v_cache"))
     q = torch.from_numpy(a["q"]).cuda()
     pos = torch.from_numpy(a["pos"]).cuda()
     out = torch.empty((B * rows, H), dtype=torch.float32, device="cuda")
     for _ in range(args.warmup):
-        ops.attn_decode(q, kc, vc, pos, rows, heads, out=out)
+        ops.attn_decode(q, kc, vc, pos, rows, out=out)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev[0].record()
     for _ in range(args.steps):
-        ops.attn_decode(q, kc, vc, pos, rows, heads, out=out)
+        ops.attn_decode(q, kc, vc, pos, rows, out=out)
     ev[1].record()
     torch.cuda.synchronize()
     t = ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
@@ -552,8 +558,7 @@ def run_verify_attn(args, torch, np):
     log(f"weights and caches generated in {time.perf_counter() - t0:.1f} s")
     dm = mdl.DeviceModel(weights)
     dm.attach_attention(attn, heads, B, L)
-    kc = torch.from_numpy(a["k_cache"].view(np.int16)).cuda().view(torch.bfloat16)
-    vc = torch.from_numpy(a["v_cache"].view(np.int16)).cuda().view(torch.bfloat16)
+    kc, vc = (head_major(torch, a[key], heads) for key in ("k_cache", "v_cache"))
     for A in dm.attn:
         A["k"].copy_(kc)
         A["v"].copy_(vc)
@@ -581,13 +586,13 @@ def run_verify_attn(args, torch, np):
     o = torch.empty((B * rows, H), dtype=torch.float32, device="cuda")
     A0 = dm.attn[0]
     for _ in range(5):
-        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, heads, out=o)
+        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, out=o)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     n_att = 50
     torch.cuda.synchronize()
     ev[0].record()
     for _ in range(n_att):
-        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, heads, out=o)
+        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, out=o)
     ev[1].record()
     torch.cuda.synchronize()
     t_att = ev[0].elapsed_time(ev[1]) * 1e-3 / n_att

@@ -376,9 +376,10 @@ moev_status moev_spec_step(const moev_model* m, const moev_draft_weights* d,
  * (columns h*D .. (h+1)*D - 1, D = H / n_heads):
  *   out = sum_j softmax_j(q . k_j / sqrt(D)) v_j
  *   q        fp32 [B*rows, H] device (row b*rows + i)
- *   k_cache, v_cache  dt [B, max_len, H] device: the prefix at positions
- *            0 .. pos[b]-1 and the verify rows' own keys and values at
- *            pos[b] .. pos[b]+rows-1 (caller-owned; not modified)
+ *   k_cache, v_cache  dt [B, n_heads, max_len, D] device, head-major: the
+ *            prefix at positions 0 .. pos[b]-1 and the verify rows' own keys
+ *            and values at pos[b] .. pos[b]+rows-1 (caller-owned; not
+ *            modified)
  *   pos      int32 [B] device; clamped on the device so that at most max_len
  *            positions are read
  *   out      fp32 [B*rows, H] device (written)
@@ -405,7 +406,8 @@ moev_status moev_attn_decode(const float* q, const void* k_cache, const void* v_
  * rows written for rejected drafts are overwritten by the next pass.
  *   attn->layers[l].w_qkv  dt [3H, H] fragment-packed (W_q, W_k, W_v stacked)
  *   attn->layers[l].w_o    dt [H, H] fragment-packed
- *   attn->layers[l].k_cache, v_cache  dt [B, max_len, H] device, updated
+ *   attn->layers[l].k_cache, v_cache  dt [B, n_heads, max_len, H/n_heads]
+ *            device (head-major, as moev_attn_decode reads them), updated
  *   pos      int32 [B] device, read then advanced; the caller keeps
  *            pos[b] + K + 1 <= max_len (larger values are clamped on the
  *            device, which keeps every access in bounds but overwrites the

@@ -6,6 +6,8 @@
 // attention with scale 1/sqrt(head width) and no positional rotation: row i
 // of sequence b, at position pos[b] + i, sees positions 0 .. pos[b] + i.
 //
+// The caches are head-major, [B, n_heads, max_len, D]: a (sequence, head)'s
+// keys and values are each one contiguous block, read front to back.
 // One workgroup per (sequence, head) with kAttnWaves wavefronts; wave w takes
 // the 64-position chunks w, w + kAttnWaves, ... of the positions the
 // sequence's last row can see, so a row's visible chunks, the order a wave
@@ -101,8 +103,11 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
   const int p0 = min(max(pos[b], 0), max_len - rows);  // row r sees positions 0 .. p0 + r
   const int n_all = p0 + rows;
   const int hi = n_all;
-  const WT* kb = kc + static_cast<long long>(b) * max_len * H + col0;
-  const WT* vb = vc + static_cast<long long>(b) * max_len * H + col0;
+  // head-major caches: this (sequence, head)'s rows are one contiguous
+  // [max_len, D] block
+  const long long blk = (static_cast<long long>(b) * gridDim.y + h) * max_len * D;
+  const WT* kb = kc + blk;
+  const WT* vb = vc + blk;
   const int vg = lane / kLpk;           // this lane's position group
   const int vc0 = (lane % kLpk) * kEpl;  // and its columns vc0 .. vc0 + kEpl - 1
   float m_run[R], l_run[R], o[R][kEpl];
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = 0.f;
     if (j < hi) {
-      const WT* kr = kb + static_cast<long long>(j) * H;
+      const WT* kr = kb + static_cast<long long>(j) * D;
 #pragma unroll
       for (int c = 0; c < D; c += 8) {
         float kv[8];
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
       const int jj = it * kNg + vg;
       const int jr = c0 + jj < hi ? c0 + jj : c0;
       float vv[kEpl];
-      ldn<WT, kEpl>(vb + static_cast<long long>(jr) * H + vc0, vv);
+      ldn<WT, kEpl>(vb + static_cast<long long>(jr) * D + vc0, vv);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float pj = p_s[wave][r][jj];

@@ -153,21 +153,24 @@ __global__ void dense_list_kernel(int32_t* list, int32_t* count, int T) {
 }
 
 // Row t = b*rows + i of [q | k | v]: q to its own fp32 buffer, k and v rounded
-// to the cache type at position p0 + i of sequence b's caches, p0 = pos[b]
-// clamped as the attention kernel clamps it.
+// to the cache type at position p0 + i of sequence b's head-major caches
+// [B, n_heads, max_len, D], p0 = pos[b] clamped as the attention kernel
+// clamps it.
 template <typename WT>
 __global__ __launch_bounds__(kAttnRowThreads) void kv_scatter_kernel(
-    const float* __restrict__ qkv, const int32_t* __restrict__ pos, int rows, int max_len, int H,
+    const float* __restrict__ qkv, const int32_t* __restrict__ pos, int rows, int max_len, int H, int D,
     float* __restrict__ q, WT* __restrict__ kc, WT* __restrict__ vc) {
   const int t = blockIdx.x;
   const int b = t / rows, i = t - b * rows;
   const int p = min(max(pos[b], 0), max_len - rows) + i;
   const float* src = qkv + static_cast<long long>(t) * 3 * H;
-  const long long dst = (static_cast<long long>(b) * max_len + p) * H;
+  const int n_heads = H / D;
   for (int c = threadIdx.x; c < H; c += kAttnRowThreads) {
+    const int hd = c / D, d = c - hd * D;
+    const long long dst = ((static_cast<long long>(b) * n_heads + hd) * max_len + p) * D + d;
     q[static_cast<long long>(t) * H + c] = src[c];
-    kc[dst + c] = from_f32<WT>(src[H + c]);
-    vc[dst + c] = from_f32<WT>(src[2 * H + c]);
+    kc[dst] = from_f32<WT>(src[H + c]);
+    vc[dst] = from_f32<WT>(src[2 * H + c]);
   }
 }
 
@@ -185,12 +188,13 @@ void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h,
   const int H = m->hidden, dt = m->dtype, T = at.B * at.rows;
   launch_norm_cast(h, y_prev, S, nullptr, m->eps, T, H, dt, x, h, s);
   launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_qkv, T, 3 * H, H, 0, 0, 1, dt, at.qkv, s, true);
+  const int D = H / at.a->n_heads;
   if (dt == MOEV_BF16)
-    kv_scatter_kernel<u16><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, at.q,
+    kv_scatter_kernel<u16><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, D, at.q,
                                                          static_cast<u16*>(al.k_cache),
                                                          static_cast<u16*>(al.v_cache));
   else
-    kv_scatter_kernel<float><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, at.q,
+    kv_scatter_kernel<float><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, D, at.q,
                                                            static_cast<float*>(al.k_cache),
                                                            static_cast<float*>(al.v_cache));
   // the attention output goes straight into x in the operand type

@@ -211,18 +211,19 @@ class DeviceModel:
     def attach_attention(self, attn: list, n_heads: int, batch: int, max_len: int) -> None:
         """Upload per-layer attention projections (as ``synth.attention_weights``:
         W_q, W_k, W_v, W_o [H, H]; the first three are stacked into one packed
-        [3H, H] matrix) and allocate zeroed key/value caches [batch, max_len, H]
-        per layer in the model dtype."""
+        [3H, H] matrix) and allocate zeroed key/value caches per layer in the
+        model dtype, head-major: [batch, n_heads, max_len, H / n_heads]."""
         dt = self.dtype
         H = self.shape.hidden
+        D = H // n_heads
         cdt = torch.bfloat16 if dt == "bf16" else torch.float32
         self.attn = []
         for a in attn:
             qkv = np.concatenate([a["w_q"], a["w_k"], a["w_v"]], axis=0)
             self.attn.append({"w_qkv": pack_weights(to_device(qkv, dt, self.device)),
                               "w_o": pack_weights(to_device(a["w_o"], dt, self.device)),
-                              "k": torch.zeros((batch, max_len, H), dtype=cdt, device=self.device),
-                              "v": torch.zeros((batch, max_len, H), dtype=cdt, device=self.device)})
+                              "k": torch.zeros((batch, n_heads, max_len, D), dtype=cdt, device=self.device),
+                              "v": torch.zeros((batch, n_heads, max_len, D), dtype=cdt, device=self.device)})
         self._c_attn_layers = (_lib.AttnLayer * max(len(self.attn), 1))()
         for i, A in enumerate(self.attn):
             self._c_attn_layers[i] = _lib.AttnLayer(ptr(A["w_qkv"]), ptr(A["w_o"]), ptr(A["k"]), ptr(A["v"]))

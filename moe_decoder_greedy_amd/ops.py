@@ -183,11 +183,14 @@ def lmhead_argmax(h: torch.Tensor, norm_f: Optional[torch.Tensor], eps: float, w
 
 
 def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, pos: torch.Tensor,
-                rows: int, n_heads: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                rows: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Causal decode attention of each sequence's ``rows`` verify rows (q fp32
-    [B*rows, H]) over its cache (k_cache, v_cache [B, max_len, H], bf16 or fp32);
-    ``pos`` int32 [B] = cached positions before each sequence's first row."""
-    B, L, H = k_cache.shape
+    [B*rows, H]) over its head-major cache (k_cache, v_cache [B, n_heads,
+    max_len, D], bf16 or fp32; H = n_heads * D); ``pos`` int32 [B] = cached
+    positions before each sequence's first row."""
+    B, n_heads, L, D = k_cache.shape
+    H = n_heads * D
+    assert tuple(v_cache.shape) == tuple(k_cache.shape) and q.shape[-1] == H
     out = _empty((B * rows, H), torch.float32, q) if out is None else out
     check("moev_attn_decode", lib().moev_attn_decode(ptr(q), ptr(k_cache), ptr(v_cache), ptr(pos), B, rows, L,
                                                      H, n_heads, dtype_code(k_cache), ptr(out),

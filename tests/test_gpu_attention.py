@@ -18,11 +18,15 @@ def ops():
     return _ops
 
 
-def _dev_cache(a):
-    if a["dtype"] == "bf16":
-        return tuple(torch.from_numpy(a[key].view(np.int16)).cuda().view(torch.bfloat16)
-                     for key in ("k_cache", "v_cache"))
-    return tuple(torch.from_numpy(a[key]).cuda() for key in ("k_cache", "v_cache"))
+def _dev_cache(a, heads):
+    """The oracle's [B, L, H] caches as the kernel's head-major [B, heads, L, D]."""
+    out = []
+    for key in ("k_cache", "v_cache"):
+        c = a[key]
+        B, L, H = c.shape
+        t = torch.from_numpy(c.view(np.int16)).view(torch.bfloat16) if a["dtype"] == "bf16" else torch.from_numpy(c)
+        out.append(t.view(B, L, heads, H // heads).permute(0, 2, 1, 3).contiguous().cuda())
+    return tuple(out)
 
 
 @pytest.mark.parametrize("B,rows,H,heads,L,prefix,bf16", [
@@ -34,8 +38,8 @@ def _dev_cache(a):
 def test_attn_decode_matches_oracle(ops, B, rows, H, heads, L, prefix, bf16):
     a = synth.attention_inputs(B, rows, H, L, prefix, seed=11 + B, bf16=bf16)
     report("attn_decode", B=B, rows=rows, H=H, heads=heads, L=L, pos=a["pos"].tolist())
-    kc, vc = _dev_cache(a)
-    out = host(ops.attn_decode(dev_f32(a["q"]), kc, vc, dev_i32(a["pos"]), rows, heads))
+    kc, vc = _dev_cache(a, heads)
+    out = host(ops.attn_decode(dev_f32(a["q"]), kc, vc, dev_i32(a["pos"]), rows))
     want = oracle.attn_decode(a["q"], a["k_cache"], a["v_cache"], a["pos"], rows, heads, a["dtype"])
     err = max_abs(out, want)
     report("attn_decode", err=err, scale=float(np.abs(want).max()))
@@ -46,12 +50,12 @@ def test_attn_decode_rows_do_not_depend_on_the_batch(ops):
     """A sequence's outputs are the same bits alone and in a batch."""
     B, rows, H, heads, L = 6, 4, 1280, 10, 600
     a = synth.attention_inputs(B, rows, H, L, (100, 590), seed=21)
-    kc, vc = _dev_cache(a)
+    kc, vc = _dev_cache(a, heads)
     q, pos = dev_f32(a["q"]), dev_i32(a["pos"])
-    full = host(ops.attn_decode(q, kc, vc, pos, rows, heads))
+    full = host(ops.attn_decode(q, kc, vc, pos, rows))
     for b in (0, 3, 5):
         one = host(ops.attn_decode(q[b * rows:(b + 1) * rows].contiguous(), kc[b:b + 1].contiguous(),
-                                   vc[b:b + 1].contiguous(), pos[b:b + 1].contiguous(), rows, heads))
+                                   vc[b:b + 1].contiguous(), pos[b:b + 1].contiguous(), rows))
         np.testing.assert_array_equal(one.view(np.uint32), full[b * rows:(b + 1) * rows].view(np.uint32))
 
 
@@ -61,10 +65,10 @@ def test_attn_row_is_the_same_in_a_one_row_pass(ops):
     pos[b] + i: greedy decoding and a verify pass see the same attention."""
     B, rows, H, heads, L = 3, 4, 1280, 10, 900
     a = synth.attention_inputs(B, rows, H, L, (100, 880), seed=31)
-    kc, vc = _dev_cache(a)
+    kc, vc = _dev_cache(a, heads)
     q, pos = dev_f32(a["q"]), dev_i32(a["pos"])
-    full = host(ops.attn_decode(q, kc, vc, pos, rows, heads)).reshape(B, rows, H)
+    full = host(ops.attn_decode(q, kc, vc, pos, rows)).reshape(B, rows, H)
     for i in range(rows):
         qi = q.view(B, rows, H)[:, i].contiguous()
-        one = host(ops.attn_decode(qi, kc, vc, (pos + i).contiguous(), 1, heads))
+        one = host(ops.attn_decode(qi, kc, vc, (pos + i).contiguous(), 1))
         np.testing.assert_array_equal(one.view(np.uint32), np.ascontiguousarray(full[:, i]).view(np.uint32))

@@ -45,15 +45,21 @@ def _oracle_caches(raw, dt):
 
 
 def _load_caches(dm, raw):
+    """The oracle's [B, L, H] caches into the device model's head-major
+    [B, heads, L, D] ones."""
     for A, a in zip(dm.attn, raw):
         for key, src in (("k", a["k_cache"]), ("v", a["v_cache"])):
             t = torch.from_numpy(src.view(np.int16)).view(torch.bfloat16) if src.dtype == np.uint16 \
                 else torch.from_numpy(src)
-            A[key].copy_(t.to(A[key].device))
+            B, heads, L, D = A[key].shape
+            A[key].copy_(t.view(B, L, heads, D).permute(0, 2, 1, 3).contiguous().to(A[key].device))
 
 
 def _gpu_cache(A, key):
+    """A device cache back in the oracle's [B, L, H] layout, float64."""
     t = A[key]
+    B, heads, L, D = t.shape
+    t = t.permute(0, 2, 1, 3).reshape(B, L, heads * D)
     return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy().astype(np.float64)
 
 
