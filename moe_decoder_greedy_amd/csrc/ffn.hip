@@ -459,7 +459,9 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
              static_cast<long long>(tile) * nkb * kFrag + lane * 8;
   }
 
-  for (int m0 = 0; m0 < M; m0 += MT) {
+  // token passes: workgroup z of gridDim.z takes passes z, z + gridDim.z, ...
+  // (a token's arithmetic does not depend on which workgroup runs its pass)
+  for (int m0 = static_cast<int>(blockIdx.z) * MT; m0 < M; m0 += static_cast<int>(gridDim.z) * MT) {
     const int mp = min(MT, M - m0);
     // the branches are uniform across the workgroup
     if (mp <= 16) {
@@ -1305,7 +1307,8 @@ void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t*
 
 void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* counts,
                            const float* topk_w, const void* w_down, int T, int H, int I, int E,
-                           int k, int ns, int dt, float* y_slots, hipStream_t s, bool split_k) {
+                           int k, int ns, int dt, float* y_slots, hipStream_t s, bool split_k,
+                           int pass_split) {
   GemmArgs dn = ffn_args(list, nullptr, T, H, I, k, ns);
   dn.counts = counts;
   dn.w0 = w_down;
@@ -1316,7 +1319,8 @@ void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* 
   dn.topk_w = topk_w;
   dn.out = y_slots;
   if (split_k) {
-    const dim3 grid(H / (16 * kRtDown), E + ns);
+    const int z = max(1, min(pass_split, (T + 31) / 32));
+    const dim3 grid(H / (16 * kRtDown), E + ns, z);
     if (dt == MOEV_BF16)
       stream_gemm<u16, kDown, kRtDown, 32, kWavesFfn, kWavesFfn><<<grid, kWavesFfn * 64, 0, s>>>(dn);
     else

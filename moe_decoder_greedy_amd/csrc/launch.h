@@ -69,10 +69,12 @@ void run_draft(const moev_model& m, const moev_draft_weights& d, const float* z_
 void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t* counts,
                               const void* w_gate, const void* w_up, int T, int H, int I, int E,
                               int k, int ns, int dt, void* act, hipStream_t s, bool split_k = false);
+// pass_split (split_k only): the 32-token passes are spread over this many
+// workgroups per row tile (grid z), for dense projections of a whole batch.
 void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* counts,
                            const float* topk_w, const void* w_down, int T, int H, int I, int E,
                            int k, int ns, int dt, float* y_slots, hipStream_t s,
-                           bool split_k = false);
+                           bool split_k = false, int pass_split = 1);
 void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
                     hipStream_t s);
 // out[i] = h[t] + the sum of y's S slots of row t (y may be NULL), t = the

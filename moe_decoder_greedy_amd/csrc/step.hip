@@ -187,7 +187,10 @@ void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h,
   const moev_attn_layer& al = at.a->layers[l];
   const int H = m->hidden, dt = m->dtype, T = at.B * at.rows;
   launch_norm_cast(h, y_prev, S, nullptr, m->eps, T, H, dt, x, h, s);
-  launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_qkv, T, 3 * H, H, 0, 0, 1, dt, at.qkv, s, true);
+  // dense projections: every 32-token pass of a row tile in its own workgroup
+  const int passes = (T + 31) / 32;
+  launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_qkv, T, 3 * H, H, 0, 0, 1, dt, at.qkv, s, true,
+                        passes);
   const int D = H / at.a->n_heads;
   if (dt == MOEV_BF16)
     kv_scatter_kernel<u16><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, D, at.q,
@@ -200,7 +203,7 @@ void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h,
   // the attention output goes straight into x in the operand type
   launch_attn_decode(at.q, al.k_cache, al.v_cache, at.pos, at.B, at.rows, at.a->max_len, H,
                      at.a->n_heads, dt, x, true, s);
-  launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_o, T, H, H, 0, 0, 1, dt, at.ao, s, true);
+  launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_o, T, H, H, 0, 0, 1, dt, at.ao, s, true, passes);
 }
 
 // Embedding and the decoder layers for T rows.  On return h holds the residual
