@@ -494,13 +494,14 @@ def run_attn(args, torch, np):
     q = torch.from_numpy(a["q"]).cuda()
     pos = torch.from_numpy(a["pos"]).cuda()
     out = torch.empty((B * rows, H), dtype=torch.float32, device="cuda")
+    ws = ops.attn_decode_workspace(B, rows, H, heads, q.device)
     for _ in range(args.warmup):
-        ops.attn_decode(q, kc, vc, pos, rows, out=out)
+        ops.attn_decode(q, kc, vc, pos, rows, out=out, ws=ws)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev[0].record()
     for _ in range(args.steps):
-        ops.attn_decode(q, kc, vc, pos, rows, out=out)
+        ops.attn_decode(q, kc, vc, pos, rows, out=out, ws=ws)
     ev[1].record()
     torch.cuda.synchronize()
     t = ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
@@ -527,7 +528,7 @@ def run_attn(args, torch, np):
                    "max_len": L, "visible_positions": visible},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attn_decode_kernel<bf16, 128> (moev_attn_decode)", "bytes_per_launch": nbytes,
+                     "kernel": "attn_decode_kernel<bf16, 128> + attn_merge_kernel (moev_attn_decode)", "bytes_per_launch": nbytes,
                      "avg_launch_us": round(t * 1e6, 2)},
         "cpu_baseline": cpu,
     }
@@ -585,14 +586,15 @@ def run_verify_attn(args, torch, np):
     q = torch.randn((B * rows, H), generator=torch.Generator(device="cuda").manual_seed(3), device="cuda")
     o = torch.empty((B * rows, H), dtype=torch.float32, device="cuda")
     A0 = dm.attn[0]
+    ws = ops.attn_decode_workspace(B, rows, H, heads, q.device)
     for _ in range(5):
-        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, out=o)
+        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, out=o, ws=ws)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     n_att = 50
     torch.cuda.synchronize()
     ev[0].record()
     for _ in range(n_att):
-        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, out=o)
+        ops.attn_decode(q, A0["k"], A0["v"], pos_d, rows, out=o, ws=ws)
     ev[1].record()
     torch.cuda.synchronize()
     t_att = ev[0].elapsed_time(ev[1]) * 1e-3 / n_att
@@ -624,7 +626,7 @@ def run_verify_attn(args, torch, np):
                    "hidden": H, "heads": heads, "max_len": L, "prefix": [1220, 2300]},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attn_decode_kernel<bf16, 128> (one layer's attention)", "bytes_per_launch": nbytes,
+                     "kernel": "attn_decode_kernel<bf16, 128> + attn_merge_kernel (one layer's attention)", "bytes_per_launch": nbytes,
                      "avg_launch_us": round(t_att * 1e6, 2)},
         "cpu_baseline": cpu,
     }

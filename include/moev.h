@@ -383,12 +383,16 @@ moev_status moev_spec_step(const moev_model* m, const moev_draft_weights* d,
  *   pos      int32 [B] device; clamped on the device so that at most max_len
  *            positions are read
  *   out      fp32 [B*rows, H] device (written)
+ *   ws       workspace of moev_attn_decode_workspace_size() bytes, 16-byte
+ *            aligned (each (sequence, head) runs as several workgroups over
+ *            fixed position chunks whose softmax states are merged in order)
  * 1 <= rows <= 16; D in {64, 128, 256}.  B = 0 is a no-op.  Nothing
  * allocates or synchronises.
  */
+size_t moev_attn_decode_workspace_size(int B, int rows, int H, int n_heads);
 moev_status moev_attn_decode(const float* q, const void* k_cache, const void* v_cache, const int32_t* pos,
                              int B, int rows, int max_len, int H, int n_heads, int dt, float* out,
-                             void* stream);
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moev_verify_step_attn -- the verify pass of moev_verify_step through a

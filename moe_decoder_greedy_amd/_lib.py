@@ -92,8 +92,9 @@ SIGNATURES = {
     "moev_verify_step_attn": (c_int, [ctypes.POINTER(Model), ctypes.POINTER(Attn), c_void_p, c_int, c_int,
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_size_t, c_void_p]),
+    "moev_attn_decode_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
     "moev_attn_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
-                                 c_int, c_int, c_void_p, c_void_p]),
+                                 c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moev_prefill_workspace_size": (c_size_t, [ctypes.POINTER(Model), c_int, c_int]),
     "moev_prefill": (c_int, [ctypes.POINTER(Model), c_void_p, c_int, c_int, c_void_p, c_void_p,
                              c_void_p, c_size_t, c_void_p]),

@@ -8,11 +8,16 @@
 //
 // The caches are head-major, [B, n_heads, max_len, D]: a (sequence, head)'s
 // keys and values are each one contiguous block, read front to back.
-// One workgroup per (sequence, head) with kAttnWaves wavefronts; wave w takes
-// the 64-position chunks w, w + kAttnWaves, ... of the positions the
-// sequence's last row can see, so a row's visible chunks, the order a wave
-// takes them in and the merge order do not depend on the number of rows in
-// the pass (chunks a row cannot see leave its state unchanged).  Per chunk: lane l scores position
+// kAttnSplits workgroups per (sequence, head), each of kAttnWaves wavefronts:
+// 64-position chunk c of the positions the sequence's last row can see goes
+// to split (c / kAttnWaves) mod kAttnSplits and, there, to wave
+// c mod kAttnWaves.  A row's visible chunks, the order a wave takes them in
+// and both merge orders (waves in a split, then splits) therefore do not
+// depend on the number of rows in the pass (chunks a row cannot see leave its
+// state unchanged).  Each split writes its unnormalised softmax state
+// (maximum, sum, weighted values) to a workspace; attn_merge_kernel combines
+// the splits.  Splitting shortens each workgroup's chain of dependent chunk
+// loads, which bounds the kernel, and spreads the work over more CUs.  Per chunk: lane l scores position
 // c0 + l against every verify row's query (staged in LDS, rows masked
 // causally), each row's chunk maximum updates that row's running maximum of
 // an online softmax, and the values are accumulated position by position in
@@ -61,14 +66,15 @@ template <typename WT, int N> __device__ __forceinline__ void ldn(const WT* p, f
   }
 }
 
-constexpr int kAttnWaves = 8;  // wavefronts per workgroup (key-range split)
+constexpr int kAttnWaves = 8;   // wavefronts per workgroup
+constexpr int kAttnSplits = 4;  // workgroups per (sequence, head)
 
-// OT: output type (fp32, or the cache type when the output feeds a GEMM
-// directly; rounded once at the store)
-template <typename WT, int D, int R, typename OT>
+// part: the splits' states, [B, n_heads, kAttnSplits, rows, D] weighted
+// values, then [B, n_heads, kAttnSplits, rows, 2] (maximum, sum)
+template <typename WT, int D, int R>
 __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
     const float* __restrict__ q, const WT* __restrict__ kc, const WT* __restrict__ vc,
-    const int32_t* __restrict__ pos, int rows, int max_len, int H, float scale, OT* __restrict__ out) {
+    const int32_t* __restrict__ pos, int rows, int max_len, int H, float scale, float* __restrict__ part) {
   // Every fused multiply-add below is written out and no other is formed, so
   // the instantiations for different row counts round identically (the
   // compiler may otherwise fuse a*b + c*d either way round).
@@ -119,7 +125,8 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
     for (int e = 0; e < kEpl; ++e) o[r][e] = 0.f;
   }
 
-  for (int c0 = wave * kWave; c0 < hi; c0 += kAttnWaves * kWave) {
+  const int split = blockIdx.z;
+  for (int c0 = (split * kAttnWaves + wave) * kWave; c0 < hi; c0 += kAttnSplits * kAttnWaves * kWave) {
     const int j = c0 + lane;
     float s[R];
 #pragma unroll
@@ -204,6 +211,11 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
     }
   }
   __syncthreads();
+  // this split's state, unnormalised (maximum -inf, sum 0 when the split
+  // holds nothing the row can see)
+  const long long slot = (static_cast<long long>(b) * gridDim.y + h) * kAttnSplits + split;
+  float* po = part + slot * rows * D;
+  float* pml = part + static_cast<long long>(gridDim.x) * gridDim.y * kAttnSplits * rows * D + slot * rows * 2;
   for (int i = threadIdx.x; i < rows * D; i += blockDim.x) {
     const int r = i / D, c = i - r * D;
     float M = -INFINITY;
@@ -216,60 +228,104 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
       L = fmaf(l_s[w][r], f, L);
       O = fmaf(o_s[w][r][c], f, O);
     }
-    out[(static_cast<long long>(b) * rows + r) * H + col0 + c] = from_f32<OT>(O / L);
+    po[r * D + c] = O;
+    if (c == 0) {
+      pml[2 * r] = M;
+      pml[2 * r + 1] = L;
+    }
   }
 }
 
-template <typename WT, int D, typename OT>
-void launch_attn_d(const float* q, const WT* k, const WT* v, const int32_t* pos, int B, int rows, int max_len,
-                   int H, int n_heads, float scale, OT* out, hipStream_t s) {
-  const dim3 grid(B, n_heads);
-  const dim3 block(kWave * kAttnWaves);
-  if (rows <= 1)
-    attn_decode_kernel<WT, D, 1, OT><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
-  else if (rows <= 4)
-    attn_decode_kernel<WT, D, 4, OT><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
-  else if (rows <= 8)
-    attn_decode_kernel<WT, D, 8, OT><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
-  else
-    attn_decode_kernel<WT, D, 16, OT><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, out);
+// out = the splits' states merged in split order, normalised; one workgroup
+// per (sequence, head).  OT: fp32, or the cache type when the output feeds
+// the output projection directly (rounded once at the store).
+template <typename OT>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part, int rows, int H,
+                                                         int D, OT* __restrict__ out) {
+#pragma clang fp contract(off)
+  const int b = blockIdx.x, h = blockIdx.y;
+  const long long slot0 = (static_cast<long long>(b) * gridDim.y + h) * kAttnSplits;
+  const float* po = part + slot0 * rows * D;
+  const float* pml = part + static_cast<long long>(gridDim.x) * gridDim.y * kAttnSplits * rows * D + slot0 * rows * 2;
+  for (int i = threadIdx.x; i < rows * D; i += 256) {
+    const int r = i / D, c = i - r * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kAttnSplits; ++sp) M = fmaxf(M, pml[(sp * rows + r) * 2]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kAttnSplits; ++sp) {
+      const float m = pml[(sp * rows + r) * 2];
+      const float f = m == -INFINITY ? 0.f : expf(m - M);
+      L = fmaf(pml[(sp * rows + r) * 2 + 1], f, L);
+      O = fmaf(po[(static_cast<long long>(sp) * rows + r) * D + c], f, O);
+    }
+    out[(static_cast<long long>(b) * rows + r) * H + h * D + c] = from_f32<OT>(O / L);
+  }
 }
 
-template <typename WT, typename OT>
+template <typename WT, int D>
+void launch_attn_d(const float* q, const WT* k, const WT* v, const int32_t* pos, int B, int rows, int max_len,
+                   int H, int n_heads, float scale, float* part, hipStream_t s) {
+  const dim3 grid(B, n_heads, kAttnSplits);
+  const dim3 block(kWave * kAttnWaves);
+  if (rows <= 1)
+    attn_decode_kernel<WT, D, 1><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part);
+  else if (rows <= 4)
+    attn_decode_kernel<WT, D, 4><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part);
+  else if (rows <= 8)
+    attn_decode_kernel<WT, D, 8><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part);
+  else
+    attn_decode_kernel<WT, D, 16><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part);
+}
+
+template <typename WT>
 void launch_attn_t(const float* q, const void* kc, const void* vc, const int32_t* pos, int B, int rows,
-                   int max_len, int H, int n_heads, OT* out, hipStream_t s) {
+                   int max_len, int H, int n_heads, float* part, hipStream_t s) {
   const int D = H / n_heads;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const WT* k = static_cast<const WT*>(kc);
   const WT* v = static_cast<const WT*>(vc);
   switch (D) {
-    case 64: launch_attn_d<WT, 64>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, out, s); break;
-    case 128: launch_attn_d<WT, 128>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, out, s); break;
-    case 256: launch_attn_d<WT, 256>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, out, s); break;
+    case 64: launch_attn_d<WT, 64>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, part, s); break;
+    case 128: launch_attn_d<WT, 128>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, part, s); break;
+    case 256: launch_attn_d<WT, 256>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, part, s); break;
     default: break;  // validated
   }
 }
 
 }  // namespace
 
+size_t attn_ws_bytes(int B, int rows, int H, int n_heads) {
+  return static_cast<size_t>(B) * kAttnSplits * rows * (H + 2 * n_heads) * sizeof(float);
+}
+
 void launch_attn_decode(const float* q, const void* k_cache, const void* v_cache, const int32_t* pos,
                         int B, int rows, int max_len, int H, int n_heads, int dt, void* out, bool out_dt,
-                        hipStream_t s) {
-  if (dt == MOEV_BF16) {
-    if (out_dt)
-      launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, static_cast<u16*>(out), s);
-    else
-      launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, static_cast<float*>(out), s);
-  } else {
-    launch_attn_t<float>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, static_cast<float*>(out), s);
-  }
+                        float* part, hipStream_t s) {
+  if (dt == MOEV_BF16)
+    launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, part, s);
+  else
+    launch_attn_t<float>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, part, s);
+  const dim3 grid(B, n_heads);
+  const int D = H / n_heads;
+  if (out_dt && dt == MOEV_BF16)
+    attn_merge_kernel<u16><<<grid, 256, 0, s>>>(part, rows, H, D, static_cast<u16*>(out));
+  else
+    attn_merge_kernel<float><<<grid, 256, 0, s>>>(part, rows, H, D, static_cast<float*>(out));
 }
 
 }  // namespace moev
 
+extern "C" size_t moev_attn_decode_workspace_size(int B, int rows, int H, int n_heads) {
+  if (B < 0 || rows < 1 || n_heads < 1 || H < 1) return 0;
+  return moev::attn_ws_bytes(B, rows, H, n_heads);
+}
+
 extern "C" moev_status moev_attn_decode(const float* q, const void* k_cache, const void* v_cache,
                                         const int32_t* pos, int B, int rows, int max_len, int H,
-                                        int n_heads, int dt, float* out, void* stream) {
+                                        int n_heads, int dt, float* out, void* ws, size_t ws_bytes,
+                                        void* stream) {
   using namespace moev;
   clear_error();
   MOEV_CHECK(check_dtype(dt), MOEV_ERR_UNSUPPORTED);
@@ -286,6 +342,10 @@ extern "C" moev_status moev_attn_decode(const float* q, const void* k_cache, con
   MOEV_CHECK(need_ptr(q, "q") && need_ptr(k_cache, "k_cache") && need_ptr(v_cache, "v_cache") &&
                  need_ptr(pos, "pos", 4) && need_ptr(out, "out"),
              MOEV_ERR_INVALID_ARG);
-  launch_attn_decode(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, dt, out, false, as_stream(stream));
+  const size_t need = attn_ws_bytes(B, rows, H, n_heads);
+  MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE, "workspace must be non-NULL and 16-byte aligned");
+  MOEV_REQUIRE(ws_bytes >= need, MOEV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  launch_attn_decode(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, dt, out, false,
+                     static_cast<float*>(ws), as_stream(stream));
   return launch_status("moev_attn_decode");
 }

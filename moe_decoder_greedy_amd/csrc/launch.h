@@ -107,11 +107,13 @@ void launch_norm_cast(const float* h, const float* y, int S, const void* gamma, 
 void launch_verify(const int32_t* tokens, const int32_t* greedy, int B, int K, int32_t* n_accept,
                    int32_t* commit, int32_t* commit_len, int32_t* next_last, hipStream_t s);
 
-// Decode attention (moev_attn_decode's kernel, arguments already checked).
-// out: fp32, or dt when out_dt (the operand of the output projection).
+// Decode attention (moev_attn_decode's kernels, arguments already checked).
+// out: fp32, or dt when out_dt (the operand of the output projection); part:
+// attn_ws_bytes() of fp32 workspace for the splits' states.
+size_t attn_ws_bytes(int B, int rows, int H, int n_heads);
 void launch_attn_decode(const float* q, const void* k_cache, const void* v_cache, const int32_t* pos,
                         int B, int rows, int max_len, int H, int n_heads, int dt, void* out, bool out_dt,
-                        hipStream_t s);
+                        float* part, hipStream_t s);
 
 size_t grouped_ffn_ws_bytes(int T, int I, int k, int ns, int dt);
 size_t lmhead_ws_bytes(int T, int H, int V, int dt);

@@ -140,6 +140,7 @@ struct AttnHook {
   float* qkv;      // [T, 3H]
   float* q;        // [T, H]
   float* ao;       // [T, H] its W_o projection, folded into the router's residual add
+  float* part;     // attention's per-split softmax states
 };
 
 constexpr int kAttnRowThreads = 256;
@@ -202,7 +203,7 @@ void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h,
                                                            static_cast<float*>(al.v_cache));
   // the attention output goes straight into x in the operand type
   launch_attn_decode(at.q, al.k_cache, al.v_cache, at.pos, at.B, at.rows, at.a->max_len, H,
-                     at.a->n_heads, dt, x, true, s);
+                     at.a->n_heads, dt, x, true, at.part, s);
   launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_o, T, H, H, 0, 0, 1, dt, at.ao, s, true, passes);
 }
 
@@ -473,10 +474,10 @@ namespace {
 // Attention step workspace: the verify step's, then the dense-GEMM row list
 // and the attention sublayer's buffers.
 struct AttnLayout {
-  size_t list, count, qkv, q, ao, total;
+  size_t list, count, qkv, q, ao, part, total;
 };
 
-AttnLayout attn_layout(const moev_model& m, int B, int K) {
+AttnLayout attn_layout(const moev_model& m, const moev_attn& a, int B, int K) {
   const int T = B * (K + 1);
   const size_t rowf = static_cast<size_t>(T) * m.hidden * 4;
   AttnLayout A{};
@@ -491,6 +492,7 @@ AttnLayout attn_layout(const moev_model& m, int B, int K) {
   A.qkv = take(3 * rowf);
   A.q = take(rowf);
   A.ao = take(rowf);
+  A.part = take(a.n_heads >= 1 ? attn_ws_bytes(B, K + 1, m.hidden, a.n_heads) : 0);
   A.total = o;
   return A;
 }
@@ -525,7 +527,7 @@ moev_status validate_attn(const moev_model* m, const moev_attn* a, int B, int K)
 extern "C" size_t moev_verify_step_attn_workspace_size(const moev_model* m, const moev_attn* a, int B,
                                                        int K) {
   if (m == nullptr || a == nullptr || B < 0 || K < 0) return 0;
-  return moev::attn_layout(*m, B, K).total;
+  return moev::attn_layout(*m, *a, B, K).total;
 }
 
 extern "C" moev_status moev_verify_step_attn(const moev_model* m, const moev_attn* a, const int32_t* tokens,
@@ -540,7 +542,7 @@ extern "C" moev_status moev_verify_step_attn(const moev_model* m, const moev_att
   MOEV_CHECK(need_ptr(pos, "pos", 4) && need_ptr(commit_len, "commit_len", 4) &&
                  need_ptr(next_last, "next_last", 4),
              MOEV_ERR_INVALID_ARG);
-  const AttnLayout A = attn_layout(*m, B, K);
+  const AttnLayout A = attn_layout(*m, *a, B, K);
   MOEV_REQUIRE(ws != nullptr && aligned16(ws), MOEV_ERR_WORKSPACE,
                "workspace must be non-NULL and 16-byte aligned");
   MOEV_REQUIRE(ws_bytes >= A.total, MOEV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes,
@@ -551,7 +553,7 @@ extern "C" moev_status moev_verify_step_attn(const moev_model* m, const moev_att
   const AttnHook at{a, B, K + 1, pos,
                     reinterpret_cast<int32_t*>(base + A.list), reinterpret_cast<int32_t*>(base + A.count),
                     reinterpret_cast<float*>(base + A.qkv), reinterpret_cast<float*>(base + A.q),
-                    reinterpret_cast<float*>(base + A.ao)};
+                    reinterpret_cast<float*>(base + A.ao), reinterpret_cast<float*>(base + A.part)};
   dense_list_kernel<<<(T + 255) / 256, 256, 0, s>>>(at.list, at.count, T);
   if (moev_status st = run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last, ws,
                                 ws_bytes, nullptr, stream, nullptr, &at))

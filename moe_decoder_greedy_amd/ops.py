@@ -182,8 +182,14 @@ def lmhead_argmax(h: torch.Tensor, norm_f: Optional[torch.Tensor], eps: float, w
     return argmax_out, mx, logits
 
 
+def attn_decode_workspace(B: int, rows: int, H: int, n_heads: int, device) -> torch.Tensor:
+    n = lib().moev_attn_decode_workspace_size(B, rows, H, n_heads)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
 def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, pos: torch.Tensor,
-                rows: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                rows: int, out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
     """Causal decode attention of each sequence's ``rows`` verify rows (q fp32
     [B*rows, H]) over its head-major cache (k_cache, v_cache [B, n_heads,
     max_len, D], bf16 or fp32; H = n_heads * D); ``pos`` int32 [B] = cached
@@ -192,9 +198,10 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, p
     H = n_heads * D
     assert tuple(v_cache.shape) == tuple(k_cache.shape) and q.shape[-1] == H
     out = _empty((B * rows, H), torch.float32, q) if out is None else out
+    ws = attn_decode_workspace(B, rows, H, n_heads, q.device) if ws is None else ws
     check("moev_attn_decode", lib().moev_attn_decode(ptr(q), ptr(k_cache), ptr(v_cache), ptr(pos), B, rows, L,
-                                                     H, n_heads, dtype_code(k_cache), ptr(out),
-                                                     stream_handle(stream)))
+                                                     H, n_heads, dtype_code(k_cache), ptr(out), ptr(ws),
+                                                     ws.numel(), stream_handle(stream)))
     return out
 
 

@@ -173,8 +173,12 @@ def test_draft_and_spec_step_validation(lib):
 def test_attn_decode_validation(lib):
     s = None
 
-    def call(q=FAKE, k=FAKE, v=FAKE, pos=FAKE, B=2, rows=4, L=64, H=1280, heads=10, dt=BF16, out=FAKE):
-        return lib.moev_attn_decode(q, k, v, pos, B, rows, L, H, heads, dt, out, s)
+    need = lib.moev_attn_decode_workspace_size(2, 4, 1280, 10)
+    assert need == 2 * 4 * 4 * (1280 + 2 * 10) * 4   # 4 splits x (weighted values + max, sum) per row
+
+    def call(q=FAKE, k=FAKE, v=FAKE, pos=FAKE, B=2, rows=4, L=64, H=1280, heads=10, dt=BF16, out=FAKE,
+             ws=FAKE, n=need):
+        return lib.moev_attn_decode(q, k, v, pos, B, rows, L, H, heads, dt, out, ws, n, s)
 
     assert call(rows=0) == UNSUPPORTED and "rows" in _err(lib)
     assert call(rows=17) == UNSUPPORTED
@@ -187,6 +191,8 @@ def test_attn_decode_validation(lib):
     assert call(B=0, q=None, k=None, v=None, pos=None, out=None) == OK
     assert call(q=None) == INVALID and "q" in _err(lib)
     assert call(pos=FAKE + 2) == INVALID and "aligned" in _err(lib)
+    assert call(ws=None) == WORKSPACE
+    assert call(n=need - 1) == WORKSPACE and "needs" in _err(lib)
 
 
 def test_verify_step_attn_validation(lib):
