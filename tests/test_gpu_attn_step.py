@@ -169,3 +169,38 @@ def test_attn_step_is_lossless(model_mod, K):
         np.testing.assert_array_equal(np.array(commits[b]), ref[b, :n])
     report("attn_step_lossless", K=K, committed=accepted, tau=accepted / (B * steps))
     assert accepted > B * steps   # some drafts were accepted
+
+
+def test_attn_step_decoder_sampled(model_mod):
+    """The benchmark's shape: the 12-layer decoder with its 129280-token head,
+    10 heads of 128, B = 32, K = 3, every layer's caches holding the same
+    seeded prefix (100-300 positions).  Every greedy token of 3 sequences (12
+    of 128 rows) is recomputed by the oracle from the same caches (bf16
+    operands); unflagged ones must match, and acceptance follows the GPU's
+    tokens."""
+    shape, heads = synth.DECODER, 10
+    report("attn_step_decoder", msg="generating the 12-layer decoder and its attention weights")
+    w = synth.model_weights(shape)
+    attn = synth.attention_weights(shape)
+    B, K, L = 32, 3, 320
+    a = synth.attention_inputs(B, K + 1, shape.hidden, L, (100, 300), seed=61)
+    dm = model_mod.DeviceModel(w)
+    dm.attach_attention(attn, heads, B, L)
+    _load_caches(dm, [a] * shape.n_layers)
+    pos = a["pos"].astype(np.int64)
+    rng = np.random.default_rng(12)
+    tokens = rng.integers(0, shape.vocab, size=(B, K + 1)).astype(np.int64)
+    out = dm.verify_step_attn(dev_i32(tokens.astype(np.int32)), dev_i32(pos.astype(np.int32)))
+    gg = host(out["greedy"])
+    sample = [0, 17, 31]
+    sub = {key: a[key][sample] for key in ("k_cache", "v_cache")}
+    caches = [{"k": oracle.to_f64(sub["k_cache"], "bf16"), "v": oracle.to_f64(sub["v_cache"], "bf16")}
+              for _ in range(shape.n_layers)]
+    ref = oracle.cached_greedy(tokens[sample], w, attn, caches, pos[sample], heads, "bf16")
+    flagged = (ref["gap"] < HEAD_GAP) | (ref["router_gap"] < ROUTE_GAP)
+    got = gg[sample]
+    report("attn_step_decoder", flagged=int(flagged.sum()), mismatches=int((got != ref["argmax"]).sum()))
+    np.testing.assert_array_equal(got[~flagged], ref["argmax"][~flagged])
+    n, c, l, nx = oracle.mtp_verify(tokens, gg)
+    np.testing.assert_array_equal(host(out["commit"]), c)
+    np.testing.assert_array_equal(host(out["next_last"]), nx)
