@@ -1318,6 +1318,18 @@ void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* 
   dn.x = act;
   dn.topk_w = topk_w;
   dn.out = y_slots;
+  // dense projections of a whole batch (pass_split > 1): two 16-row tiles per
+  // workgroup halve the operand rows' L2 re-reads; the K order of every output
+  // is unchanged
+  if (split_k && pass_split > 1 && H % 32 == 0) {
+    const int z = max(1, min(pass_split, (T + 31) / 32));
+    const dim3 grid(H / 32, E + ns, z);
+    if (dt == MOEV_BF16)
+      stream_gemm<u16, kDown, 2, 32, kWavesFfn, kWavesFfn><<<grid, kWavesFfn * 64, 0, s>>>(dn);
+    else
+      stream_gemm<float, kDown, 2, 32, kWavesFfn, kWavesFfn><<<grid, kWavesFfn * 64, 0, s>>>(dn);
+    return;
+  }
   if (split_k) {
     const int z = max(1, min(pass_split, (T + 31) / 32));
     const dim3 grid(H / (16 * kRtDown), E + ns, z);

@@ -70,7 +70,8 @@ void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t*
                               const void* w_gate, const void* w_up, int T, int H, int I, int E,
                               int k, int ns, int dt, void* act, hipStream_t s, bool split_k = false);
 // pass_split (split_k only): the 32-token passes are spread over this many
-// workgroups per row tile (grid z), for dense projections of a whole batch.
+// workgroups per row tile (grid z), for dense projections of a whole batch;
+// with pass_split > 1 a workgroup takes two 16-row tiles (H % 32 == 0).
 void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* counts,
                            const float* topk_w, const void* w_down, int T, int H, int I, int E,
                            int k, int ns, int dt, float* y_slots, hipStream_t s,
