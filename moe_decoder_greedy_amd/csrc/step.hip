@@ -7,7 +7,9 @@
 // The verification itself follows "The speed comes from three layers working
 // together" (Jina-OCR-v1 explainer, kg.zhiyong.dev): the K drafted tokens are
 // checked by the main decoder in one pass, here as T = B*(K+1) rows of one
-// batch.
+// batch.  moev_verify_step_attn runs the same step with an attention sublayer
+// before every MoE sublayer (per-sequence key/value caches, positions
+// advanced by the accepted length on the device).
 #include "launch.h"
 
 namespace moev {
@@ -139,7 +141,7 @@ struct AttnHook {
   int32_t* count;  // [1] = T
   float* qkv;      // [T, 3H]
   float* q;        // [T, H]
-  float* ao;       // [T, H] its W_o projection, folded into the router's residual add
+  float* ao;       // [T, H] the attention output's W_o projection, added to h by the router
   float* part;     // attention's per-split softmax states
 };
 
