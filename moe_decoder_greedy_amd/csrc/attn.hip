@@ -67,7 +67,7 @@ template <typename WT, int N> __device__ __forceinline__ void ldn(const WT* p, f
 }
 
 constexpr int kAttnWaves = 4;   // wavefronts per workgroup
-constexpr int kAttnSplits = 8;  // workgroups per (sequence, head)
+constexpr int kAttnSplits = 3;  // workgroups per (sequence, head)
 
 // part: the splits' states, [B, n_heads, kAttnSplits, rows, D] weighted
 // values, then [B, n_heads, kAttnSplits, rows, 2] (maximum, sum)

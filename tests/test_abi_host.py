@@ -174,7 +174,7 @@ def test_attn_decode_validation(lib):
     s = None
 
     need = lib.moev_attn_decode_workspace_size(2, 4, 1280, 10)
-    assert need == 2 * 4 * 8 * (1280 + 2 * 10) * 4   # 8 splits x (weighted values + max, sum) per row
+    assert need == 2 * 4 * 3 * (1280 + 2 * 10) * 4   # 3 splits x (weighted values + max, sum) per row
 
     def call(q=FAKE, k=FAKE, v=FAKE, pos=FAKE, B=2, rows=4, L=64, H=1280, heads=10, dt=BF16, out=FAKE,
              ws=FAKE, n=need):
