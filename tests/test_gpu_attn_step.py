@@ -204,3 +204,58 @@ def test_attn_step_decoder_sampled(model_mod):
     n, c, l, nx = oracle.mtp_verify(tokens, gg)
     np.testing.assert_array_equal(host(out["commit"]), c)
     np.testing.assert_array_equal(host(out["next_last"]), nx)
+
+
+def test_attn_step_graph_replays(model_mod):
+    """Three consecutive passes captured as one HIP graph (cache writes,
+    attention workspace and the position advance inside it), replayed three
+    times from the same restored caches and positions, with eager passes in
+    between: every replay reproduces the eager outputs, positions and caches
+    bit for bit."""
+    shape, heads = ATTN_BF16, 2
+    w = synth.model_weights(shape)
+    attn = synth.attention_weights(shape)
+    B, K, n_steps = 8, 3, 3
+    L = 120 + n_steps * (K + 1) + 8
+    raw, pos0 = _prefix_caches(shape, B, K + 1, L, (0, 120), seed=71)
+    dm = model_mod.DeviceModel(w)
+    dm.attach_attention(attn, heads, B, L)
+    rng = np.random.default_rng(5)
+    toks = [dev_i32(rng.integers(0, shape.vocab, size=(B, K + 1))) for _ in range(n_steps)]
+    pos_d = dev_i32(pos0.astype(np.int32))
+
+    def restore():
+        _load_caches(dm, raw)
+        pos_d.copy_(dev_i32(pos0.astype(np.int32)))
+        torch.cuda.synchronize()
+
+    restore()
+    eager = [{k: host(v) for k, v in dm.verify_step_attn(t, pos_d).items()} for t in toks]
+    eager_pos = host(pos_d)
+    eager_k = [_gpu_cache(A, "k") for A in dm.attn]
+    outs = [dm.alloc_outputs(B, K) for _ in range(n_steps)]
+    restore()
+    dm.verify_step_attn(toks[0], pos_d, out=outs[0])   # workspace and code objects ready
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t, o in zip(toks, outs):
+            dm.verify_step_attn(t, pos_d, out=o)
+    other = dev_i32(rng.integers(0, shape.vocab, size=(B, K + 1)))
+    for r in range(3):
+        restore()
+        for o in outs:
+            for v in o.values():
+                v.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for s in range(n_steps):
+            for k in ("greedy", "n_accept", "commit", "commit_len", "next_last"):
+                np.testing.assert_array_equal(host(outs[s][k]), eager[s][k], err_msg=f"replay {r} step {s} {k}")
+        np.testing.assert_array_equal(host(pos_d), eager_pos)
+        for A, want in zip(dm.attn, eager_k):
+            np.testing.assert_array_equal(_gpu_cache(A, "k"), want)
+        dm.verify_step_attn(other, pos_d)                # eager work between replays
+        torch.cuda.synchronize()
+    report("attn_graph", B=B, K=K, steps=n_steps, replays=3)
