@@ -32,6 +32,8 @@ def test_zero_output_projection_is_the_moe_only_model(tiny):
     ref = oracle.model_greedy(tokens.reshape(-1), model, "exact")
     np.testing.assert_array_equal(got["argmax"].reshape(-1), ref["argmax"])
     np.testing.assert_array_equal(got["h"], ref["h"])
+    np.testing.assert_array_equal(got["router_gap"].reshape(-1), ref["router_gap"])
+    np.testing.assert_array_equal(got["gap"].reshape(-1), ref["gap"])
 
 
 def test_attention_makes_tokens_depend_on_the_prefix(tiny):
