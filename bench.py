@@ -82,6 +82,29 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def attn_source_digest() -> str:
+    """Digest of the sources the decode-attention kernels are built from."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for f in ("attn.hip", "common.h", "launch.h"):
+        with open(os.path.join(ROOT, "moe_decoder_greedy_amd", "csrc", f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+def stored_attn_traffic():
+    """HBM bytes per moev_attn_decode call at attn_decode_b32k3 from the committed
+    rocprofv3 PMC record, or None when absent or stale."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic_attn_decode_b32k3.json")) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != attn_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
 # ---------------------------------------------------------------------------
 # algorithmic work
 
@@ -527,7 +550,7 @@ def run_attn(args, torch, np):
         "config": {"workload": "attn_decode_b32k3", "batch": B, "rows": rows, "hidden": H, "heads": heads,
                    "max_len": L, "visible_positions": visible},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": stored_attn_traffic(),
                      "kernel": "attn_decode_kernel<bf16, 128> + attn_merge_kernel (moev_attn_decode)", "bytes_per_launch": nbytes,
                      "avg_launch_us": round(t * 1e6, 2)},
         "cpu_baseline": cpu,
