@@ -115,14 +115,16 @@ def gate_up_bytes(touched: int, T: int, P: int, H: int, I: int, es: int = 2) -> 
     return touched * 2 * I * H * es + T * H * es + P * I * es + 4 * P
 
 
-def layer_bytes(touched: int, T: int, P: int, H: int, I: int, E: int, es: int = 2) -> int:
-    """One MoE layer: router weights, all three matrices of each touched group,
-    the residual in and out, expert slots in and out, activations."""
-    return (E * H * es + touched * 3 * I * H * es + 2 * T * H * 4 + T * H * es
-            + 2 * P * I * es + 2 * P * H * 4)
+def layer_bytes(touched: int, T: int, H: int, I: int, E: int, es: int = 2) -> int:
+    """Algorithmic bytes of one MoE layer: the router weights, all three
+    matrices of each touched group once, and the residual stream in and out.
+    Implementation scratch (the bf16 operand copy, the SwiGLU activations,
+    the per-slot expert outputs) is not counted."""
+    return E * H * es + touched * 3 * I * H * es + 2 * T * H * 4
 
 
 def head_bytes(T: int, H: int, V: int, es: int = 2) -> int:
+    """The head's weights once, the residual rows in, the greedy tokens out."""
     return V * H * es + T * H * 4 + T * 4
 
 
@@ -138,11 +140,14 @@ def copy_probe(torch, mib: int):
     log(f"copy probe: {mib} MiB read + {mib} MiB written per copy, 3 copies")
 
 
-def cpu_baseline(wl, weights, tokens_np, budget_s):
+def cpu_baseline(wl, weights, tokens_np, budget_s, gpu_greedy=None):
     """The oracle as it stands, on this host's cores, over one verify step of
     the same batch: layers are timed one by one until the budget is spent and
     the per-layer mean is extrapolated to the full depth, plus the head and
-    the accept step."""
+    the accept step.  When every layer fit the budget, the same oracle pass
+    also gives the step's near-tie flags (a router gap below 1e-3 in any
+    layer, a head top-2 gap below 1e-2) and the GPU's greedy tokens are
+    compared with it: returned as a second dict (None otherwise)."""
     import numpy as np
     import oracle
     try:
@@ -156,11 +161,13 @@ def cpu_baseline(wl, weights, tokens_np, budget_s):
     t0 = time.perf_counter()
     h = oracle.embed(tokens_np.reshape(-1), weights["emb"], dt)
     layer_times = []
+    rgap = np.full(B * K1, np.inf)
     for layer in weights["layers"]:
         ts = time.perf_counter()
         st = oracle.moe_layer(h, layer, dt, shape.top_k, shape.n_routed, shape.n_shared, shape.eps, "bf16")
         h = st["h_out"]
         layer_times.append(time.perf_counter() - ts)
+        rgap = np.minimum(rgap, st["gap"])
         if time.perf_counter() - t0 > budget_s * 0.7:
             break
     ts = time.perf_counter()
@@ -170,11 +177,22 @@ def cpu_baseline(wl, weights, tokens_np, budget_s):
     n_l = len(layer_times)
     t_step = float(np.mean(layer_times)) * shape.n_layers + t_head
     T = B * K1
-    return {"value": T / t_step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    base = {"value": T / t_step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"one verify step of {B}x{K1} tokens (float64 numpy oracle): {n_l} of "
                        f"{shape.n_layers} layers timed, mean extrapolated to {shape.n_layers}, "
                        f"plus head and accept; oracle step {t_step:.2f} s"),
             "seconds_measured": round(time.perf_counter() - t0, 2)}
+    check = None
+    if n_l == shape.n_layers and gpu_greedy is not None:
+        rf, hf = rgap < 1e-3, head["gap"] < 1e-2
+        flagged = rf | hf
+        got = np.asarray(gpu_greedy).reshape(-1)
+        check = {"positions": int(T), "router_flagged": int(rf.sum()), "head_flagged": int(hf.sum()),
+                 "flagged": int(flagged.sum()),
+                 "mismatches_flagged": int((got[flagged] != head["argmax"][flagged]).sum()),
+                 "mismatches_unflagged": int((got[~flagged] != head["argmax"][~flagged]).sum()),
+                 "source": "oracle pass of the cpu_baseline leg over the first timed step (bf16 operands)"}
+    return base, check
 
 
 def cpu_baseline_prefill(weights, tokens_np, budget_s):
@@ -739,7 +757,9 @@ def run_verify(args, torch, np):
     # run on, right around the launches of one stage per pass, so the GPU is
     # never waiting on the host between the two events.
     # (the step driver folds each combine into the next router launch)
-    stages = ("route", "permute", "gate_up", "down", "head")
+    # decode-sized steps (T <= 512) fill expert lists in the router and
+    # launch no permute kernel, so that stage is only timed above
+    stages = ("route", "gate_up", "down", "head") if T <= 512 else ("route", "permute", "gate_up", "down", "head")
     dur_us = {}
     for st in stages:
         n_ev = 1 if st == "head" else shape.n_layers
@@ -775,10 +795,14 @@ def run_verify(args, torch, np):
     touched = (np.diff(offs.cpu().numpy(), axis=1) > 0).sum(axis=1)     # [layers]
     gu_bytes = float(np.mean([gate_up_bytes(int(t), T, P, H, I, es) for t in touched]))
     gu_flops = 4.0 * P * H * I
-    step_bytes = sum(layer_bytes(int(t), T, P, H, I, E, es) for t in touched) + head_bytes(T, H, V, es)
+    step_bytes = sum(layer_bytes(int(t), T, H, I, E, es) for t in touched) + head_bytes(T, H, V, es) + T * 4
     gu_gbs = gu_bytes / (dur_us["gate_up"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(wl.name),
+                "scope": "dominant kernel only (the gate/up GEMM); the whole step is step_roofline",
+                "traffic_source": "stored rocprofv3 FETCH_SIZE/WRITE_SIZE record "
+                                  f"profiles/{os.path.basename(traffic_file(wl.name))}, reported only while the "
+                                  "GEMM sources match its digest (null otherwise)",
                 "kernel": "stream_gemm<bf16, gate/up> (moe_ffn_gate_up)",
                 "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(dur_us["gate_up"], 2),
                 "mfma_frac": round(gu_flops / (dur_us["gate_up"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
@@ -796,13 +820,22 @@ def run_verify(args, torch, np):
         "ms_per_step_eager": round(t_eager * 1e3, 4),
         "ms_per_step_graph": None if t_graph is None else round(t_graph * 1e3, 4),
         "step_roofline": {"bound": "hbm", "bytes_per_step": int(step_bytes), "achieved": round(step_gbs, 1),
-                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                          "bytes": "algorithmic: router weights, every touched expert's three matrices once, "
+                                   "residual in and out per layer; head weights, its input rows and tokens"},
         "roofline": roofline,
         "kernel_avg_us": {n: round(v, 2) for n, v in dur_us.items()},
+        "kernel_avg_us_note": "HIP events recorded by the step driver around each stage's launches, averaged "
+                              "over layers; each event pair adds a few us, so the stages sum to more than "
+                              "ms_per_step; route includes the previous layer's combine, head its norm and "
+                              "the prefix accept",
     }
+    result["near_ties"] = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(wl, weights, inputs_d[args.warmup].cpu().numpy(), args.cpu_budget)
+        i0 = args.warmup
+        result["cpu_baseline"], result["near_ties"] = cpu_baseline(
+            wl, weights, inputs_d[i0].cpu().numpy(), args.cpu_budget, gpu_greedy=outs["greedy"][i0].cpu().numpy())
     else:
         result["cpu_baseline"] = None
     return result
@@ -872,7 +905,7 @@ def run_layer(args, torch, np):
     touched = (np.diff(offs.cpu().numpy(), axis=1) > 0).sum(axis=1)
     gu_bytes = float(np.mean([gate_up_bytes(int(t), T, P, H, I) for t in touched]))
     gu_flops = 4.0 * P * H * I
-    lb = float(np.mean([layer_bytes(int(t), T, P, H, I, E) for t in touched]))
+    lb = float(np.mean([layer_bytes(int(t), T, H, I, E) for t in touched]))
     lflops = 6.0 * P * H * I + 2.0 * T * E * H
     prefill = T > 1024
     traffic = stored_traffic(wl.name)

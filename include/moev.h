@@ -120,6 +120,13 @@ moev_status moe_route(const float* h, const void* norm_w, float eps, const void*
 
 /*
  * moe_permute -- group the (token, slot) pairs by expert.
+ * [P1] "The speed comes from three layers working together": each token
+ * goes to its top 6 of the 64 routed experts and to the two shared experts,
+ * so each expert's FFN runs over the subset of tokens that chose it.  The
+ * pages do not describe the dispatch; this call is the plain stable counting
+ * sort that lets each expert's GEMM read its tokens as one contiguous
+ * segment.  It returns no tile list: the grouped GEMMs derive their tile
+ * schedule on the device from group_offsets.
  * Pair p = t*S + slot.  Slot r < k belongs to routed expert topk_idx[t, r];
  * slot k+s to shared expert s (group E+s), which therefore holds every token.
  *   group_offsets int32 [G+1] (written): exclusive prefix sum of group sizes
@@ -168,7 +175,12 @@ moev_status moe_ffn_down(const void* act, const int32_t* sorted_src, const int32
                          int k, int ns, int dt, float* y_slots, void* stream);
 
 /*
- * moe_combine -- residual add of every slot's expert output:
+ * moe_combine -- residual add of every slot's expert output.
+ * [P1] "The speed comes from three layers working together": a token's MoE
+ * output is the mix of its chosen experts' outputs (weighted by the
+ * router's renormalised gates, already applied by moe_grouped_ffn) plus the
+ * always-on shared experts; in the pre-norm decoder it is added to the
+ * residual stream.  Summation order is fixed:
  *   h_out[t, :] = h_in[t, :] + sum_{slot = 0..S-1} y_slots[t, slot, :]
  * summed in slot order (routed by rank, then shared).  h_in NULL: no residual.
  * h_out may alias h_in.

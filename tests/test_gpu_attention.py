@@ -60,10 +60,13 @@ def test_attn_decode_rows_do_not_depend_on_the_batch(ops):
 
 
 
-def test_attn_row_is_the_same_in_a_one_row_pass(ops):
-    """Row i of a 4-row pass is the same bits as a one-row pass at position
-    pos[b] + i: greedy decoding and a verify pass see the same attention."""
-    B, rows, H, heads, L = 3, 4, 1280, 10, 900
+@pytest.mark.parametrize("rows", [2, 4, 5, 8, 16])
+def test_attn_row_is_the_same_in_a_one_row_pass(ops, rows):
+    """Row i of a multi-row pass is the same bits as a one-row pass at
+    position pos[b] + i: greedy decoding and a verify pass see the same
+    attention.  Row counts cover every instantiation a verify pass of up to
+    16 rows selects (2, 4, 8 and 16 rows; 5 runs the 8-row one part full)."""
+    B, H, heads, L = 3, 1280, 10, 900
     a = synth.attention_inputs(B, rows, H, L, (100, 880), seed=31)
     kc, vc = _dev_cache(a, heads)
     q, pos = dev_f32(a["q"]), dev_i32(a["pos"])

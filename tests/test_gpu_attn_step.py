@@ -115,17 +115,20 @@ def _rollout(dm, last, pos0, n):
     return np.stack(seq, axis=1)
 
 
-@pytest.mark.parametrize("K", [1, 3])
-def test_attn_step_is_lossless(model_mod, K):
+@pytest.mark.parametrize("B,K", [(8, 1), (8, 3), (32, 1), (32, 3)])
+def test_attn_step_is_lossless(model_mod, B, K):
     """Speculative passes with drafts right with probability 0.7 commit exactly
     the tokens of one-row greedy decoding from the same caches, bit for bit,
     although every pass writes cache rows for drafts that are then rejected.
     The first pass's unflagged greedy tokens also equal the oracle's (bf16
-    operands)."""
+    operands).  At B = 32 the verify passes (64 or 128 rows) run the dense
+    projections split over several 32-row passes with two row tiles per
+    workgroup, while the one-row rollout (32 rows) runs them as one pass of
+    one row tile: the commits show both give the same bits."""
     shape, heads = ATTN_BF16, 2
     w = synth.model_weights(shape)
     attn = synth.attention_weights(shape)
-    B, steps = 8, 10
+    steps = 10
     L = 120 + steps * (K + 1) + K + 2
     raw, pos0 = _prefix_caches(shape, B, K + 1, L, (0, 120), seed=51)
     dm = model_mod.DeviceModel(w)
@@ -171,13 +174,13 @@ def test_attn_step_is_lossless(model_mod, K):
     assert accepted > B * steps   # some drafts were accepted
 
 
-def test_attn_step_decoder_sampled(model_mod):
+def test_attn_step_decoder_all_rows(model_mod):
     """The benchmark's shape: the 12-layer decoder with its 129280-token head,
     10 heads of 128, B = 32, K = 3, every layer's caches holding the same
-    seeded prefix (100-300 positions).  Every greedy token of 3 sequences (12
-    of 128 rows) is recomputed by the oracle from the same caches (bf16
-    operands); unflagged ones must match, and acceptance follows the GPU's
-    tokens."""
+    seeded prefix (100-300 positions).  Every greedy token of all 32
+    sequences (128 rows) is recomputed by the oracle from the same caches
+    (bf16 operands); unflagged ones must match, and acceptance follows the
+    GPU's tokens."""
     shape, heads = synth.DECODER, 10
     report("attn_step_decoder", msg="generating the 12-layer decoder and its attention weights")
     w = synth.model_weights(shape)
@@ -192,7 +195,7 @@ def test_attn_step_decoder_sampled(model_mod):
     tokens = rng.integers(0, shape.vocab, size=(B, K + 1)).astype(np.int64)
     out = dm.verify_step_attn(dev_i32(tokens.astype(np.int32)), dev_i32(pos.astype(np.int32)))
     gg = host(out["greedy"])
-    sample = [0, 17, 31]
+    sample = list(range(B))
     sub = {key: a[key][sample] for key in ("k_cache", "v_cache")}
     caches = [{"k": oracle.to_f64(sub["k_cache"], "bf16"), "v": oracle.to_f64(sub["v_cache"], "bf16")}
               for _ in range(shape.n_layers)]

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from gpu_util import dev_i32, host, need_gpu, report
 
@@ -22,11 +23,22 @@ def model_mod():
     return model
 
 
-def _check_graph(dm, B, K, n_steps, seed, replays=3):
+def _check_graph(dm, B, K, n_steps, seed, replays=3, weights=None):
     V = dm.shape.vocab
     rng = np.random.default_rng(seed)
     toks = [dev_i32(rng.integers(0, V, size=(B, K + 1))) for _ in range(n_steps)]
     eager = [{k: host(v) for k, v in dm.verify_step(t).items()} for t in toks]
+    if weights is not None:
+        # the eager outputs the replays must reproduce are themselves the
+        # oracle's (fp32 model: exact operands), off near-ties
+        for t, e in zip(toks, eager):
+            tk = host(t)
+            ref = oracle.verify_step(tk[:, 0], tk[:, 1:], weights, operands="exact")
+            ok = (ref["gap"] >= 1e-2) & (ref["router_gap"] >= 1e-3)
+            np.testing.assert_array_equal(e["greedy"][ok], ref["greedy"][ok])
+            clear = ok.all(axis=1)
+            np.testing.assert_array_equal(e["commit"][clear], ref["commit"][clear])
+            np.testing.assert_array_equal(e["n_accept"][clear], ref["n_accept"][clear])
     outs = [dm.alloc_outputs(B, K) for _ in range(n_steps)]
     dm.verify_step(toks[0], out=outs[0])          # workspace and code objects ready
     torch.cuda.synchronize()
@@ -51,8 +63,11 @@ def _check_graph(dm, B, K, n_steps, seed, replays=3):
 
 
 def test_graph_tiny(model_mod):
-    dm = model_mod.DeviceModel(synth.model_weights(synth.TINY))
-    _check_graph(dm, B=4, K=3, n_steps=4, seed=1)
+    """Tiny fp32 model: replays equal the eager steps bit for bit, and those
+    equal the oracle's verify (greedy tokens off near-ties, commits)."""
+    w = synth.model_weights(synth.TINY)
+    dm = model_mod.DeviceModel(w)
+    _check_graph(dm, B=4, K=3, n_steps=4, seed=1, weights=w)
 
 
 @pytest.mark.parametrize("B,K", [(8, 3), (32, 3)])
