@@ -757,9 +757,9 @@ def run_verify(args, torch, np):
     # run on, right around the launches of one stage per pass, so the GPU is
     # never waiting on the host between the two events.
     # (the step driver folds each combine into the next router launch)
-    # decode-sized steps (T <= 512) fill expert lists in the router and
+    # decode-sized steps (T <= 256) fill expert lists in the router and
     # launch no permute kernel, so that stage is only timed above
-    stages = ("route", "gate_up", "down", "head") if T <= 512 else ("route", "permute", "gate_up", "down", "head")
+    stages = ("route", "gate_up", "down", "head") if T <= 256 else ("route", "permute", "gate_up", "down", "head")
     dur_us = {}
     for st in stages:
         n_ev = 1 if st == "head" else shape.n_layers
@@ -796,16 +796,19 @@ def run_verify(args, torch, np):
     gu_bytes = float(np.mean([gate_up_bytes(int(t), T, P, H, I, es) for t in touched]))
     gu_flops = 4.0 * P * H * I
     step_bytes = sum(layer_bytes(int(t), T, H, I, E, es) for t in touched) + head_bytes(T, H, V, es) + T * 4
-    gu_gbs = gu_bytes / (dur_us["gate_up"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(wl.name),
-                "scope": "dominant kernel only (the gate/up GEMM); the whole step is step_roofline",
+    dom_bytes, dom_us = gu_bytes, dur_us["gate_up"]
+    dom_name = ("stream_gemm<bf16, gate/up> (moe_ffn_gate_up)" if T <= 256 else
+                "tile_gemm<bf16, gate/up, 128> (moe_ffn_gate_up)")
+    dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(wl.name),
+                "scope": "dominant kernel only; the whole step is step_roofline",
                 "traffic_source": "stored rocprofv3 FETCH_SIZE/WRITE_SIZE record "
                                   f"profiles/{os.path.basename(traffic_file(wl.name))}, reported only while the "
                                   "GEMM sources match its digest (null otherwise)",
-                "kernel": "stream_gemm<bf16, gate/up> (moe_ffn_gate_up)",
-                "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(dur_us["gate_up"], 2),
-                "mfma_frac": round(gu_flops / (dur_us["gate_up"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                "kernel": dom_name,
+                "bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_us, 2),
+                "mfma_frac": round(gu_flops / (dom_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     step_gbs = step_bytes / t_step / 1e9
     result = {
         "metric": METRIC, "value": round(T / t_step, 1), "unit": "tokens/s", "n_gpus": 1,

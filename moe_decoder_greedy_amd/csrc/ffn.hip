@@ -35,37 +35,17 @@ namespace {
 
 enum Mode { kGateUp = 0, kDown = 1, kHead = 2 };
 
-#ifndef MOEV_KC
-#define MOEV_KC 64
-#endif
-#ifndef MOEV_KNB
-#define MOEV_KNB 3
-#endif
-#ifndef MOEV_KNBD
-#define MOEV_KNBD 3
-#endif
-constexpr int kKC = MOEV_KC;     // K elements per LDS chunk (multiple of 32)
-constexpr int kKB = kKC / 32;    // MFMA K blocks per chunk
-constexpr int kNB = MOEV_KNB;    // LDS path: weight ring depth in chunks
-constexpr int kNBD = MOEV_KNBD;  // direct path: ring depth in K blocks
-constexpr int kFrag = 512;       // elements of one packed 16x32 fragment
-#ifndef MOEV_RT_DOWN
-#define MOEV_RT_DOWN 1
-#endif
-#ifndef MOEV_RT_HEAD
-#define MOEV_RT_HEAD 2
-#endif
-#ifndef MOEV_WAVES_HEAD
-#define MOEV_WAVES_HEAD 8
-#endif
-constexpr int kRtDown = MOEV_RT_DOWN;        // 16-row tiles per wave, down projection
-constexpr int kRtHead = MOEV_RT_HEAD;        // 16-row tiles per wave, LM head
-constexpr int kWavesFfn = 4;                 // wavefronts per workgroup, expert GEMMs
-#ifndef MOEV_TILE_MIN_TOKENS
-#define MOEV_TILE_MIN_TOKENS 512
-#endif
-constexpr int kTileMinTokens = MOEV_TILE_MIN_TOKENS;  // larger batches use the tile schedule
-constexpr int kWavesHead = MOEV_WAVES_HEAD;  // wavefronts per workgroup, LM head
+constexpr int kKC = 64;              // K elements per LDS chunk (multiple of 32)
+constexpr int kKB = kKC / 32;        // MFMA K blocks per chunk
+constexpr int kNB = 3;               // LDS path: weight ring depth in chunks
+constexpr int kNBD = 4;              // direct path: ring depth in K blocks
+constexpr int kFrag = 512;           // elements of one packed 16x32 fragment
+constexpr int kRtDown = 1;           // 16-row tiles per wave, down projection
+constexpr int kRtHead = 2;           // 16-row tiles per wave, LM head
+constexpr int kWavesFfn = 4;         // wavefronts per workgroup, expert GEMMs
+constexpr int kTileMinTokens = 256;  // larger batches use the tile schedule
+constexpr int kWavesHead = 8;        // wavefronts per workgroup, LM head
+static_assert(kTileMinTokens == kListMaxTokens, "the step's list mode is the streaming schedule's range");
 
 // MT = tokens per pass (32, 64 or 128 = 2, 4 or 8 MFMA column tiles).  The
 // variant only changes how many accumulators and LDS rows a workgroup holds;
@@ -410,8 +390,11 @@ __device__ __forceinline__ void gemm_pass_lds(const GemmArgs& a, unsigned char* 
   epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
 }
 
+// One workgroup of the streaming schedule: row slab bx of group slot by,
+// token passes bz, bz + nz, ...  (G groups; the last a.n_first are
+// dispatched first).
 template <typename WT, int MODE, int RT, int MT, int W, int KS = 1>
-__global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
+__device__ __forceinline__ void stream_gemm_wg(const GemmArgs& a, int bx, int by, int bz, int G, int nz) {
   static_assert(KS == 1 || MT == 32, "split K runs direct passes of at most 32 tokens");
   using C = Cfg<WT, MT>;
   constexpr int NT = C::kTiles;
@@ -425,8 +408,7 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
   if (MODE == kHead) {
     M = a.T;
   } else {
-    const int G = gridDim.y;
-    g = static_cast<int>(blockIdx.y) < a.n_first ? G - a.n_first + blockIdx.y : blockIdx.y - a.n_first;
+    g = by < a.n_first ? G - a.n_first + by : by - a.n_first;
     if (a.counts != nullptr) {
       off = g * a.T;
       M = clampi(a.counts[g], 0, a.T);
@@ -450,8 +432,8 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
   const int wt = KS > 1 ? 0 : wave;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int rb = (MODE == kGateUp) ? blockIdx.x * (16 * kWaveTiles) + wt * 16
-                                     : blockIdx.x * (16 * RT * kWaveTiles) + wt * (16 * RT) + rt * 16;
+    const int rb = (MODE == kGateUp) ? bx * (16 * kWaveTiles) + wt * 16
+                                     : bx * (16 * RT * kWaveTiles) + wt * (16 * RT) + rt * 16;
     rowbase[rt] = rb;
     const int tile = min(rb / 16, ntiles - 1);
     const WT* base = (MODE == kGateUp && rt == 1) ? w1 : w0;
@@ -459,9 +441,9 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
              static_cast<long long>(tile) * nkb * kFrag + lane * 8;
   }
 
-  // token passes: workgroup z of gridDim.z takes passes z, z + gridDim.z, ...
-  // (a token's arithmetic does not depend on which workgroup runs its pass)
-  for (int m0 = static_cast<int>(blockIdx.z) * MT; m0 < M; m0 += static_cast<int>(gridDim.z) * MT) {
+  // token passes: workgroup z of nz takes passes z, z + nz, ... (a token's
+  // arithmetic does not depend on which workgroup runs its pass)
+  for (int m0 = bz * MT; m0 < M; m0 += nz * MT) {
     const int mp = min(MT, M - m0);
     // the branches are uniform across the workgroup
     if (mp <= 16) {
@@ -475,6 +457,11 @@ __global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
         gemm_pass_lds<WT, MODE, RT, MT, NT, W>(a, lds, off, m0, mp, wp, rowbase);
     }
   }
+}
+
+template <typename WT, int MODE, int RT, int MT, int W, int KS = 1>
+__global__ __launch_bounds__(W * 64) void stream_gemm(GemmArgs a) {
+  stream_gemm_wg<WT, MODE, RT, MT, W, KS>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.y, gridDim.z);
 }
 
 // ---------------------------------------------------------------------------
@@ -511,10 +498,7 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
 // same single fp32 chain over K blocks in order with the same MFMA as the
 // streaming schedule: results are bitwise identical.
 constexpr int kMaxGroups = 64 + 8;       // routed + shared experts
-#ifndef MOEV_TILE_BLOCK
-#define MOEV_TILE_BLOCK 4
-#endif
-constexpr int kTileBlock = MOEV_TILE_BLOCK;  // token tiles per ordering block
+constexpr int kTileBlock = 4;  // token tiles per ordering block
 constexpr int kXcds = 8;
 
 template <int MODE> constexpr int tile_cols() { return MODE == kGateUp ? 128 : 256; }  // output rows / 2 for gate/up
@@ -1002,10 +986,7 @@ void launch_tile(const GemmArgs& args, int n_ctiles, int G, int E, int k, int ns
 
 // LM head on the tile schedule: one group of T tokens, 256 vocabulary rows
 // per column tile, so the partial arg max blocks are the column tiles.
-#ifndef MOEV_HEAD_TILE_MIN_TOKENS
-#define MOEV_HEAD_TILE_MIN_TOKENS 32
-#endif
-constexpr int kHeadTileMinTokens = MOEV_HEAD_TILE_MIN_TOKENS;
+constexpr int kHeadTileMinTokens = 32;
 static_assert(tile_cols<kHead>() == 16 * kRtHead * kWavesHead, "head partial blocks");
 
 template <typename WT>

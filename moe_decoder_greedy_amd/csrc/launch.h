@@ -16,7 +16,9 @@ struct ExpertLists {
   int32_t* list;    // [G][T]
   int n_sets, E, G, k, S;
 };
-constexpr int kListMaxTokens = 512;  // list mode only on the streaming GEMM schedule
+// list mode only on the streaming GEMM schedule; above this many tokens the
+// tiled schedule is faster
+constexpr int kListMaxTokens = 256;
 
 // lists != NULL: also resets every count set (routed 0, shared T) and writes
 // the shared groups' lists.
@@ -117,6 +119,11 @@ void launch_attn_decode(const float* q, const void* k_cache, const void* v_cache
                         float* part, hipStream_t s);
 
 size_t grouped_ffn_ws_bytes(int T, int I, int k, int ns, int dt);
+// moe_grouped_ffn's argument checks (ws_bytes: the workspace's size)
+moev_status validate_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,
+                                 const float* topk_w, const void* w_gate, const void* w_up,
+                                 const void* w_down, int T, int H, int I, int E, int k, int ns,
+                                 int dt, const float* y_slots, const void* ws, size_t ws_bytes);
 size_t lmhead_ws_bytes(int T, int H, int V, int dt);
 
 }  // namespace moev

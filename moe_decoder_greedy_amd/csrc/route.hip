@@ -26,6 +26,7 @@
 // Every reduction has a fixed order, so a token's outputs do not depend on
 // which block or batch it lands in.
 #include "launch.h"
+#include "route_core.h"
 
 namespace moev {
 namespace {
@@ -34,25 +35,6 @@ constexpr int kRouteGroupMax = 4;    // tokens per logit pass
 constexpr int kRouteThreads = 1024;   // 16 wavefronts
 constexpr int kExpertsPerWave = 4;    // 16 waves x 4 = 64 experts
 constexpr int kMaxSlots = 16;         // k + ns limit of the fused combine
-
-template <typename WT> struct Vec4;
-template <> struct Vec4<u16> {
-  __device__ static float4 load(const u16* p) {
-    uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(bf16_to_f32(u.x & 0xFFFF), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFF),
-                       bf16_to_f32(u.y >> 16));
-  }
-  __device__ static void store(u16* p, float4 v) {
-    uint2 u;
-    u.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
-    u.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
-    *reinterpret_cast<uint2*>(p) = u;
-  }
-};
-template <> struct Vec4<float> {
-  __device__ static float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
-  __device__ static void store(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
-};
 
 template <typename WT>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
@@ -161,19 +143,7 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
         const float4* ys = reinterpret_cast<const float4*>(a.y + t * a.S * H + i);
         float4 acc;
         if constexpr (PRELOAD) {
-          float4 sv[kMaxSlots];
-#pragma unroll
-          for (int sl = 0; sl < kMaxSlots; ++sl)
-            if (sl < a.S) sv[sl] = ys[static_cast<size_t>(sl) * h4];
-          acc = sv[0];
-#pragma unroll
-          for (int sl = 1; sl < kMaxSlots; ++sl)
-            if (sl < a.S) {
-              acc.x += sv[sl].x;
-              acc.y += sv[sl].y;
-              acc.z += sv[sl].z;
-              acc.w += sv[sl].w;
-            }
+          v = add_slots<kMaxSlots>(v, ys, a.S, h4);
         } else {  // the same left-to-right sum, each slot added as it arrives
           acc = ys[0];
 #pragma unroll
@@ -185,8 +155,8 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
               acc.z += yv.z;
               acc.w += yv.w;
             }
+          v = make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
         }
-        v = make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
         *reinterpret_cast<float4*>(a.h_out + t * H + i) = v;
       }
       *reinterpret_cast<float4*>(xs + tt * H + i) = v;
@@ -194,9 +164,11 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
   }
   __syncthreads();
 
-  // phase 1: RMSNorm in place in LDS, wave w < TPB takes token t0 + w
+  // phase 1: RMSNorm in place in LDS, wave w < TPB takes token t0 + w; the
+  // logit row's entries past E are set to -inf (never ranked above a real one)
   if (wave < kRouteTPB) {
     const int t = t0 + wave;
+    if (lane >= E) lg[wave * 64 + lane] = -INFINITY;
     if (t < T) {
       float4 hv[NCH], gv[NCH];
 #pragma unroll
@@ -208,10 +180,8 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
       }
       float ss = 0.f;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        ss += hv[c].x * hv[c].x + hv[c].y * hv[c].y + hv[c].z * hv[c].z + hv[c].w * hv[c].w;
-      ss = lane63(wave_sum_lane63(ss));
-      const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + a.eps);
+      for (int c = 0; c < NCH; ++c) ss = sumsq_step(ss, hv[c]);
+      const float r = rms_scale(ss, H, a.eps);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int i = lane * 4 + c * 256;
@@ -253,7 +223,7 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
             const float4 x = *reinterpret_cast<const float4*>(xs + (t1 + tt) * H + i);
 #pragma unroll
             for (int u = 0; u < kExpertsPerWave; ++u)
-              acc[u][tt] += x.x * wv[u][cw].x + x.y * wv[u][cw].y + x.z * wv[u][cw].z + x.w * wv[u][cw].w;
+              acc[u][tt] = dot_step(acc[u][tt], x, wv[u][cw]);
           }
         }
       }
@@ -281,10 +251,9 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
     const int t = t0 + wave;
     if (t < T) {
       const float* row = lg + wave * 64;
-      const float v = lane < E ? row[lane] : -INFINITY;
+      const float v = row[lane];
       if (a.logits_out != nullptr && lane < E) a.logits_out[static_cast<size_t>(t) * E + lane] = v;
-      int rank = 0;
-      for (int j = 0; j < E; ++j) rank += better(row[j], j, v, lane) ? 1 : 0;
+      const int rank = logit_rank(row, v, lane);
       if (lane < E && rank < k) {
         sel_v[wave * 64 + rank] = v;
         sel_i[wave * 64 + rank] = lane;
@@ -293,12 +262,11 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       if (lane < k) {
-        const float top0 = sel_v[wave * 64];
-        float sum = 0.f;
-        for (int j = 0; j < k; ++j) sum += expf(sel_v[wave * 64 + j] - top0);
-        const int e = sel_i[wave * 64 + lane];
+        // the ranks are a permutation for finite logits; the clamp keeps the
+        // list append in bounds whatever the inputs
+        const int e = min(max(sel_i[wave * 64 + lane], 0), E - 1);
         a.topk_idx[static_cast<size_t>(t) * k + lane] = e;
-        a.topk_w[static_cast<size_t>(t) * k + lane] = expf(sel_v[wave * 64 + lane] - top0) / sum;
+        a.topk_w[static_cast<size_t>(t) * k + lane] = topk_weight(sel_v + wave * 64, k, lane);
         if (a.list != nullptr) {
           const int at = atomicAdd(a.counts + e, 1);
           a.list[static_cast<size_t>(e) * T + at] = t * a.S_pairs + lane;

@@ -1,0 +1,100 @@
+// Per-token arithmetic of the router ("The speed comes from three layers
+// working together", Jina-OCR-v1 explainer on kg.zhiyong.dev: top-6 of 64
+// routed experts).  Every block shape of the router kernel calls these, so a
+// token gets the same bits whichever instantiation routes it; every
+// multiply-add is written out, because a contraction left to the compiler
+// could be formed differently in different instantiations.
+#pragma once
+
+#include "common.h"
+
+namespace moev {
+
+template <typename WT> struct Vec4;
+template <> struct Vec4<u16> {
+  __device__ static float4 load(const u16* p) {
+    uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(bf16_to_f32(u.x & 0xFFFF), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFF),
+                       bf16_to_f32(u.y >> 16));
+  }
+  __device__ static uint2 pack(float4 v) {
+    uint2 u;
+    u.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+    u.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+    return u;
+  }
+  __device__ static void store(u16* p, float4 v) { *reinterpret_cast<uint2*>(p) = pack(v); }
+};
+template <> struct Vec4<float> {
+  __device__ static float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static void store(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+};
+
+// ss + v.x^2 + v.y^2 + v.z^2 + v.w^2, one fused multiply-add at a time
+__device__ __forceinline__ float sumsq_step(float ss, float4 v) {
+  ss = fmaf(v.x, v.x, ss);
+  ss = fmaf(v.y, v.y, ss);
+  ss = fmaf(v.z, v.z, ss);
+  return fmaf(v.w, v.w, ss);
+}
+
+// acc + x . w over four elements, one fused multiply-add at a time
+__device__ __forceinline__ float dot_step(float acc, float4 x, float4 w) {
+  acc = fmaf(x.x, w.x, acc);
+  acc = fmaf(x.y, w.y, acc);
+  acc = fmaf(x.z, w.z, acc);
+  return fmaf(x.w, w.w, acc);
+}
+
+// h + the S expert slots ys[0], ys[h4], ... added left to right (the order
+// the combine kernel uses); every slot load is issued before the sum
+template <int kMaxSlots>
+__device__ __forceinline__ float4 add_slots(float4 h, const float4* ys, int S, size_t h4) {
+  float4 sv[kMaxSlots];
+#pragma unroll
+  for (int sl = 0; sl < kMaxSlots; ++sl)
+    if (sl < S) sv[sl] = ys[static_cast<size_t>(sl) * h4];
+  float4 acc = sv[0];
+#pragma unroll
+  for (int sl = 1; sl < kMaxSlots; ++sl)
+    if (sl < S) {
+      acc.x += sv[sl].x;
+      acc.y += sv[sl].y;
+      acc.z += sv[sl].z;
+      acc.w += sv[sl].w;
+    }
+  return make_float4(h.x + acc.x, h.y + acc.y, h.z + acc.z, h.w + acc.w);
+}
+
+// RMSNorm scale from the wave's sum of squares (lane 63 holds the total)
+__device__ __forceinline__ float rms_scale(float ss_lanes, int H, float eps) {
+  const float ss = lane63(wave_sum_lane63(ss_lanes));
+  return 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
+}
+
+// Rank of this lane's logit v among the 64 entries of an LDS row (entries
+// past the expert count hold -inf): the number of entries that beat it
+// (larger, or equal with a lower index).
+__device__ __forceinline__ int logit_rank(const float* row, float v, int lane) {
+  int rank = 0;
+#pragma unroll
+  for (int j4 = 0; j4 < 16; ++j4) {
+    const float4 r = reinterpret_cast<const float4*>(row)[j4];
+    rank += better(r.x, 4 * j4 + 0, v, lane) ? 1 : 0;
+    rank += better(r.y, 4 * j4 + 1, v, lane) ? 1 : 0;
+    rank += better(r.z, 4 * j4 + 2, v, lane) ? 1 : 0;
+    rank += better(r.w, 4 * j4 + 3, v, lane) ? 1 : 0;
+  }
+  return rank;
+}
+
+// Renormalised softmax weight of the chosen logit sel[lane] over the k chosen
+// ones, rank order: exp(l_r - l_0) / sum_j exp(l_j - l_0)
+__device__ __forceinline__ float topk_weight(const float* sel, int k, int lane) {
+  const float top0 = sel[0];
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += expf(sel[j] - top0);
+  return expf(sel[lane] - top0) / sum;
+}
+
+}  // namespace moev

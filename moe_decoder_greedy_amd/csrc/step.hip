@@ -499,11 +499,14 @@ AttnLayout attn_layout(const moev_model& m, const moev_attn& a, int B, int K) {
   return A;
 }
 
+// rows of one pass with attention (the dense projections' single list)
+constexpr int kAttnMaxRows = 512;
+
 moev_status validate_attn(const moev_model* m, const moev_attn* a, int B, int K) {
   MOEV_REQUIRE(a != nullptr, MOEV_ERR_INVALID_ARG, "attention weights must not be NULL");
   MOEV_REQUIRE(K + 1 <= 16, MOEV_ERR_UNSUPPORTED, "K=%d: attention takes at most 16 rows per sequence", K);
-  MOEV_REQUIRE(static_cast<long long>(B) * (K + 1) <= kListMaxTokens, MOEV_ERR_UNSUPPORTED,
-               "B*(K+1)=%lld rows exceeds %d", static_cast<long long>(B) * (K + 1), kListMaxTokens);
+  MOEV_REQUIRE(static_cast<long long>(B) * (K + 1) <= kAttnMaxRows, MOEV_ERR_UNSUPPORTED,
+               "B*(K+1)=%lld rows exceeds %d", static_cast<long long>(B) * (K + 1), kAttnMaxRows);
   MOEV_REQUIRE(a->n_heads >= 1 && m->hidden % a->n_heads == 0, MOEV_ERR_UNSUPPORTED,
                "hidden size %d must be a multiple of n_heads=%d", m->hidden, a->n_heads);
   const int D = m->hidden / a->n_heads;
