@@ -160,6 +160,30 @@ moev_status moe_grouped_ffn(const void* x, const int32_t* sorted_src, const int3
                             float* y_slots, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_grouped_ffn_noalloc -- moe_grouped_ffn with no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The SwiGLU
+ * activations go to a scratch array of MOEV_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * that the library keeps in the memory of each GPU it runs on until the
+ * process ends; its device address is looked up (hipGetSymbolAddress) on the
+ * first call on each device, so make that first call outside graph capture.
+ * Nothing is allocated or freed by the call.  Arguments, results and every
+ * other check are those of moe_grouped_ffn.  A call whose activations,
+ * moe_grouped_ffn_workspace_size(T, I, k, ns, dt) bytes, exceed the scratch
+ * (for the decoder's I = 896, k + ns = 8, bf16: T > 1170) returns
+ * MOEV_ERR_WORKSPACE before any HIP call.  All calls on one GPU share the
+ * array: calls on one stream run in order and are safe, calls that overlap
+ * in time on one GPU (several streams, several host threads) race and give
+ * undefined results.  Nothing in the scratch needs to start at zero; it keeps
+ * the last call's activations.
+ */
+#define MOEV_NOALLOC_SCRATCH_BYTES (16u << 20)
+moev_status moe_grouped_ffn_noalloc(const void* x, const int32_t* sorted_src, const int32_t* group_offsets,
+                                    const float* topk_w, const void* w_gate, const void* w_up,
+                                    const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
+                                    float* y_slots, void* stream);
+
+/*
  * The two stages of moe_grouped_ffn as separate calls (same kernels).
  * moe_ffn_gate_up: act[j, :] = SiLU(w_gate[g] . x[t]) * (w_up[g] . x[t]),
  *   rounded to dt, for every row j of the sorted pair order (pair

@@ -118,6 +118,23 @@ def test_step_validation(lib):
                                 ws, None) == UNSUPPORTED
 
 
+def test_noalloc_grouped_ffn_rejects_oversize(lib):
+    """The allocation-free grouped FFN refuses, before any HIP call, a batch
+    whose activations do not fit its static scratch (16 MiB: the decoder's
+    I = 896 with k + ns = 8 in bf16 fits up to T = 1170), and passes its
+    other checks on to moe_grouped_ffn's (T = 0 is a no-op)."""
+    args = lambda T: (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, 1280, 896, 64, 6, 2, BF16, FAKE, None)
+    assert lib.moe_grouped_ffn_noalloc(*args(1171)) == WORKSPACE
+    assert "1171" in _err(lib) and "16777216" in _err(lib)
+    assert lib.moe_grouped_ffn_noalloc(*args(0)) == OK
+    bad = list(args(16))
+    bad[8] = 100                     # H not a multiple of 64
+    assert lib.moe_grouped_ffn_noalloc(*bad) == UNSUPPORTED
+    bad = list(args(16))
+    bad[14] = None                   # y_slots
+    assert lib.moe_grouped_ffn_noalloc(*bad) == INVALID
+
+
 def test_prefill_validation(lib):
     layers = (_lib.LayerWeights * 1)(_lib.LayerWeights(None, FAKE, None, FAKE, FAKE, None))
     m = _lib.Model(1280, 64, 896, 6, 2, 129280, 1, BF16, 1e-6, FAKE, None, FAKE, layers)
