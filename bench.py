@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="verify_step_b32k3",
                     help="verify_step_b32k{3,2,1,0} | zipf_verify_b{1,8,32,128}k{1,3} | decode_layer_t128 | "
-                         "prefill_layer_t9760 | prefill_model_t9760 | kselect_b32 | spec_loop_b32k3 | attn_decode_b32k3 | "
+                         "prefill_layer_t9760 | prefill_model_t9760 | kselect_b{32,1} | spec_loop_b32k3 | attn_decode_b32k3 | "
                          "verify_attn_b32k3")
     ap.add_argument("--launch", choices=("auto", "eager", "graph"), default="auto")
     ap.add_argument("--kernel-steps", type=int, default=8, help="steps of the per-kernel event pass")
@@ -320,13 +320,15 @@ def stage_inputs(dm, wl, n_steps, torch, np):
     return torch.from_numpy(inputs).cuda(), want_len
 
 
-def run_kselect(args, torch, np):
-    """Choice of K (drafts per step) at B = 32: for K = 0 (plain greedy), 1, 2
-    and 3 the same model runs a loop of verify steps captured as one HIP graph
+def run_kselect(args, torch, np, batch: int = 32):
+    """Choice of K (drafts per step) at B = 32 (kselect_b32) or B = 1
+    (kselect_b1, the pages' batch size): for K = 0 (plain greedy), 1, 2 and 3
+    the same model runs a loop of verify steps captured as one HIP graph
     (chunks of consecutive steps, each reading its own staged input, no host
     work inside a chunk). c(K) = step time / the K = 0 step time, tau(K) =
     committed tokens per sequence per step as measured, S(K) = tau / c: the
     decomposition the review of the pages gives for the speedup."""
+    import dataclasses
     import synth
     from moe_decoder_greedy_amd import model as mdl
     shape = synth.DECODER
@@ -336,7 +338,8 @@ def run_kselect(args, torch, np):
     chunk = max(1, min(args.graph_chunk, args.steps))
     rows, lossless = [], True
     for K in (0, 1, 2, 3):
-        wl = synth.WORKLOADS[f"verify_step_b32k{K}"]
+        wl = dataclasses.replace(synth.WORKLOADS[f"verify_step_b32k{K}"], batch=batch,
+                                 name=f"verify_step_b{batch}k{K}")
         B = wl.batch
         n_steps = args.warmup + args.steps
         inputs_d, want_len = stage_inputs(dm, wl, n_steps, torch, np)
@@ -375,11 +378,11 @@ def run_kselect(args, torch, np):
         r["S"] = round(r["tau"] / r["c"], 4)
     best = max(rows, key=lambda r: r["S"])
     return {
-        "metric": "speculative speedup S = tau / c at the best K (B=32, graph-captured step loop)",
+        "metric": f"speculative speedup S = tau / c at the best K (B={batch}, graph-captured step loop)",
         "value": best["S"], "unit": "x", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": best["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) bf16 weights, drafts at the first K of 0.830/0.663/0.636)",
-        "config": {"workload": "kselect_b32", "batch": 32, "layers": shape.n_layers, "vocab": shape.vocab,
+        "config": {"workload": f"kselect_b{batch}", "batch": batch, "layers": shape.n_layers, "vocab": shape.vocab,
                    "graph_steps_per_replay": chunk, "best_K": best["K"]},
         "per_K": rows, "lossless_commits": lossless, "roofline": None, "cpu_baseline": None,
     }
@@ -757,9 +760,9 @@ def run_verify(args, torch, np):
     # run on, right around the launches of one stage per pass, so the GPU is
     # never waiting on the host between the two events.
     # (the step driver folds each combine into the next router launch)
-    # decode-sized steps (T <= 256) fill expert lists in the router and
+    # decode-sized steps (T <= 128) fill expert lists in the router and
     # launch no permute kernel, so that stage is only timed above
-    stages = ("route", "gate_up", "down", "head") if T <= 256 else ("route", "permute", "gate_up", "down", "head")
+    stages = ("route", "gate_up", "down", "head") if T <= 128 else ("route", "permute", "gate_up", "down", "head")
     dur_us = {}
     for st in stages:
         n_ev = 1 if st == "head" else shape.n_layers
@@ -797,7 +800,7 @@ def run_verify(args, torch, np):
     gu_flops = 4.0 * P * H * I
     step_bytes = sum(layer_bytes(int(t), T, H, I, E, es) for t in touched) + head_bytes(T, H, V, es) + T * 4
     dom_bytes, dom_us = gu_bytes, dur_us["gate_up"]
-    dom_name = ("stream_gemm<bf16, gate/up> (moe_ffn_gate_up)" if T <= 256 else
+    dom_name = ("stream_gemm<bf16, gate/up> (moe_ffn_gate_up)" if T <= 128 else
                 "tile_gemm<bf16, gate/up, 128> (moe_ffn_gate_up)")
     dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -958,8 +961,8 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe_mib:
         copy_probe(torch, args.copy_probe_mib)
-    if args.workload == "kselect_b32":
-        result = run_kselect(args, torch, np)
+    if args.workload in ("kselect_b32", "kselect_b1"):
+        result = run_kselect(args, torch, np, batch=int(args.workload[len("kselect_b"):]))
     elif args.workload == "spec_loop_b32k3":
         result = run_spec(args, torch, np)
     elif args.workload == "attn_decode_b32k3":

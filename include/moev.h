@@ -448,10 +448,12 @@ moev_status moev_attn_decode(const float* q, const void* k_cache, const void* v_
  *   attn->layers[l].w_o    dt [H, H] fragment-packed
  *   attn->layers[l].k_cache, v_cache  dt [B, n_heads, max_len, H/n_heads]
  *            device (head-major, as moev_attn_decode reads them), updated
- *   pos      int32 [B] device, read then advanced; the caller keeps
- *            pos[b] + K + 1 <= max_len (larger values are clamped on the
- *            device, which keeps every access in bounds but overwrites the
- *            cache's last rows)
+ *   pos      int32 [B] device, read then advanced.  A sequence whose cache
+ *            has no room for the pass (pos[b] < 0 or pos[b] + K + 1 >
+ *            max_len) is left as it is: no cache row is written, pos[b]
+ *            stays, commit_len[b] = 0, n_accept[b] = -1, its commit row is
+ *            all -1 and next_last[b] = its input last token (its greedy
+ *            row is unspecified); the caller retires or resets it
  *   greedy, n_accept, commit, commit_len, next_last: as moev_verify_step
  *   ws       workspace of moev_verify_step_attn_workspace_size() bytes
  * Needs B*(K+1) <= 512, K + 1 <= 16, H / n_heads in {64, 128, 256} and

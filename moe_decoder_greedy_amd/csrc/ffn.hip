@@ -43,7 +43,7 @@ constexpr int kFrag = 512;           // elements of one packed 16x32 fragment
 constexpr int kRtDown = 1;           // 16-row tiles per wave, down projection
 constexpr int kRtHead = 2;           // 16-row tiles per wave, LM head
 constexpr int kWavesFfn = 4;         // wavefronts per workgroup, expert GEMMs
-constexpr int kTileMinTokens = 256;  // larger batches use the tile schedule
+constexpr int kTileMinTokens = 128;  // larger batches use the tile schedule
 constexpr int kWavesHead = 8;        // wavefronts per workgroup, LM head
 static_assert(kTileMinTokens == kListMaxTokens, "the step's list mode is the streaming schedule's range");
 
@@ -1151,6 +1151,14 @@ __global__ __launch_bounds__(64 * kVerifyFuseMaxRows) void argmax_verify_kernel(
   }
   __syncthreads();
   if (threadIdx.x == 0) {
+    if (v.pos != nullptr && (v.pos[b] < 0 || v.pos[b] > v.max_len - K1)) {
+      // no room in the sequence's cache: nothing accepted or committed
+      for (int j = 0; j < K1; ++j) v.commit[static_cast<long long>(b) * K1 + j] = -1;
+      v.n_accept[b] = -1;
+      if (v.commit_len) v.commit_len[b] = 0;
+      if (v.next_last) v.next_last[b] = tok_s[0];
+      return;
+    }
     const int n = accept_prefix(tok_s, gr_s, v.K, v.commit + static_cast<long long>(b) * K1);
     v.n_accept[b] = n;
     if (v.commit_len) v.commit_len[b] = n + 1;
@@ -1386,6 +1394,7 @@ void launch_lmhead(const float* h, const void* norm_f, float eps, const void* w_
   } else {
     launch_gemm<float, kHead, kRtHead, kWavesHead>(hd, dim3(nblk), s);
   }
+  // (the attention step's checks keep it on the fused path: K + 1 <= 16)
   if (vf != nullptr && vf->K + 1 <= kVerifyFuseMaxRows && out_stride == 1 && max_out == nullptr) {
     argmax_verify_kernel<<<vf->B, 64 * (vf->K + 1), 0, s>>>(pmax, pidx, nblk, argmax_out, *vf);
     return;

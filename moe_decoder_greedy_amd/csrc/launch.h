@@ -18,7 +18,7 @@ struct ExpertLists {
 };
 // list mode only on the streaming GEMM schedule; above this many tokens the
 // tiled schedule is faster
-constexpr int kListMaxTokens = 256;
+constexpr int kListMaxTokens = 128;
 
 // lists != NULL: also resets every count set (routed 0, shared T) and writes
 // the shared groups' lists.
@@ -94,6 +94,11 @@ struct VerifyFuse {
   int32_t* commit;
   int32_t* commit_len;
   int32_t* next_last;
+  // with attention: a sequence whose cache has no room for the pass
+  // (pos[b] < 0 or pos[b] + K + 1 > max_len) commits nothing (see
+  // moev_verify_step_attn); pos NULL without attention
+  const int32_t* pos = nullptr;
+  int max_len = 0;
 };
 // y_prev (optional): the last layer's expert slots, added to h before the norm.
 // h_out (optional): the combined residual h + sum of y_prev's slots, fp32;

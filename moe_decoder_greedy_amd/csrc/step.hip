@@ -156,16 +156,19 @@ __global__ void dense_list_kernel(int32_t* list, int32_t* count, int T) {
 }
 
 // Row t = b*rows + i of [q | k | v]: q to its own fp32 buffer, k and v rounded
-// to the cache type at position p0 + i of sequence b's head-major caches
-// [B, n_heads, max_len, D], p0 = pos[b] clamped as the attention kernel
-// clamps it.
+// to the cache type at position pos[b] + i of sequence b's head-major caches
+// [B, n_heads, max_len, D].  A sequence whose cache has no room for the pass
+// (pos[b] < 0 or pos[b] + rows > max_len) writes nothing: the step commits
+// nothing for it and leaves its position.
 template <typename WT>
 __global__ __launch_bounds__(kAttnRowThreads) void kv_scatter_kernel(
     const float* __restrict__ qkv, const int32_t* __restrict__ pos, int rows, int max_len, int H, int D,
     float* __restrict__ q, WT* __restrict__ kc, WT* __restrict__ vc) {
   const int t = blockIdx.x;
   const int b = t / rows, i = t - b * rows;
-  const int p = min(max(pos[b], 0), max_len - rows) + i;
+  const int p0 = pos[b];
+  if (p0 < 0 || p0 > max_len - rows) return;
+  const int p = p0 + i;
   const float* src = qkv + static_cast<long long>(t) * 3 * H;
   const int n_heads = H / D;
   for (int c = threadIdx.x; c < H; c += kAttnRowThreads) {
@@ -311,7 +314,11 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
   };
   const int H = m->hidden, dt = m->dtype;
   // the head's last kernel also applies the prefix acceptance
-  const VerifyFuse vf{tokens, B, K, n_accept, commit, commit_len, next_last};
+  VerifyFuse vf{tokens, B, K, n_accept, commit, commit_len, next_last};
+  if (at != nullptr) {
+    vf.pos = at->pos;
+    vf.max_len = at->a->max_len;
+  }
   mark(MOEV_STAGE_HEAD, 0, false);
   launch_lmhead(h, m->norm_f, m->eps, m->w_lm, T, H, m->vocab, dt, greedy, nullptr, nullptr,
                 head_ws, s, m->n_layers > 0 ? y : nullptr, S, h_final, 1, &vf);

@@ -262,3 +262,41 @@ def test_attn_step_graph_replays(model_mod):
         dm.verify_step_attn(other, pos_d)                # eager work between replays
         torch.cuda.synchronize()
     report("attn_graph", B=B, K=K, steps=n_steps, replays=3)
+
+
+def test_attn_step_leaves_a_full_cache_alone(model_mod):
+    """A sequence whose cache has no room for the pass (pos + K + 1 > max_len)
+    commits nothing: commit_len 0, n_accept -1, a commit row of -1, next_last
+    its own last token, its position and every row of its caches unchanged.
+    The other sequences of the pass, one of them filling its cache exactly,
+    match the oracle's cached decoder."""
+    shape, heads = synth.TINY, 2
+    w = synth.model_weights(shape)
+    attn = synth.attention_weights(shape)
+    B, K, L = 3, 3, 20
+    raw, _ = _prefix_caches(shape, B, K + 1, L, (0, 0), seed=81)
+    pos = np.array([0, L - (K + 1), L - K], np.int64)   # fits, fits exactly, one row short
+    dm = model_mod.DeviceModel(w)
+    dm.attach_attention(attn, heads, B, L)
+    _load_caches(dm, raw)
+    before = [{key: _gpu_cache(A, key) for key in ("k", "v")} for A in dm.attn]
+    tokens = np.random.default_rng(3).integers(0, shape.vocab, size=(B, K + 1)).astype(np.int64)
+    pos_d = dev_i32(pos.astype(np.int32))
+    out = dm.verify_step_attn(dev_i32(tokens.astype(np.int32)), pos_d)
+    torch.cuda.synchronize()
+    assert host(out["commit_len"])[2] == 0 and host(out["n_accept"])[2] == -1
+    np.testing.assert_array_equal(host(out["commit"])[2], np.full(K + 1, -1))
+    assert host(out["next_last"])[2] == tokens[2, 0]
+    np.testing.assert_array_equal(host(pos_d), pos + np.append(host(out["commit_len"])[:2], 0))
+    for A, b4 in zip(dm.attn, before):
+        for key in ("k", "v"):
+            np.testing.assert_array_equal(_gpu_cache(A, key)[2], b4[key][2])
+    caches = [{"k": c["k"][:2], "v": c["v"][:2]} for c in _oracle_caches(raw, shape.dtype)]
+    ref = oracle.cached_greedy(tokens[:2], w, attn, caches, pos[:2], heads, "exact")
+    flagged = (ref["gap"] < HEAD_GAP) | (ref["router_gap"] < ROUTE_GAP)
+    gg = host(out["greedy"])[:2]
+    np.testing.assert_array_equal(gg[~flagged], ref["argmax"][~flagged])
+    n, c, l, nx = oracle.mtp_verify(tokens[:2], gg)
+    np.testing.assert_array_equal(host(out["commit"])[:2], c)
+    np.testing.assert_array_equal(host(out["commit_len"])[:2], l)
+    report("attn_full_cache", pos=pos.tolist(), commit_len=host(out["commit_len"]).tolist())
