@@ -51,12 +51,6 @@ struct DraftInArgs {
   const void* norm_e;
   float eps;
   void* x2;                 // [2][B][H] operand rows of the projection
-  // expert-list tables of the two grouped GEMMs (written when lists_p != NULL)
-  int32_t* lists_p;         // [2][B]
-  int32_t* counts_p;        // [2]
-  int32_t* lists_f;         // [n][B]
-  int32_t* counts_f;        // [n]
-  int n;
 };
 
 // Block b: wave 0 normalises z's row, wave 1 the embedding row of the token.
@@ -66,15 +60,6 @@ __global__ __launch_bounds__(kDraftThreads) void draft_in_kernel(DraftInArgs a) 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int H = a.H;
-  if (a.lists_p != nullptr) {
-    // pair = b * slots + group, as the grouped GEMMs read them
-    if (threadIdx.x < 2) a.lists_p[threadIdx.x * a.B + b] = b * 2 + threadIdx.x;
-    for (int g = threadIdx.x; g < a.n; g += kDraftThreads) a.lists_f[g * a.B + b] = b * a.n + g;
-    if (b == 0) {
-      if (threadIdx.x < 2) a.counts_p[threadIdx.x] = a.B;
-      for (int g = threadIdx.x; g < a.n; g += kDraftThreads) a.counts_f[g] = a.B;
-    }
-  }
   const int raw = a.tok[static_cast<long long>(b) * a.tok_stride];
   if (a.tok_copy != nullptr && threadIdx.x == 0) a.tok_copy[static_cast<long long>(b) * a.copy_stride] = raw;
   const int t = raw < 0 ? 0 : (raw >= a.V ? a.V - 1 : raw);
@@ -116,7 +101,7 @@ __global__ __launch_bounds__(kDraftThreads) void draft_in_kernel(DraftInArgs a) 
 size_t esz(int dt) { return dt == MOEV_BF16 ? 2 : 4; }
 
 struct DraftLayout {
-  size_t x2, yp, zp, xf, act, yf, z[2], head, lists_p, counts_p, lists_f, counts_f, total;
+  size_t x2, yp, zp, xf, act, yf, z[2], head, total;
 };
 
 DraftLayout draft_layout(const moev_model& m, int n, int B) {
@@ -137,10 +122,6 @@ DraftLayout draft_layout(const moev_model& m, int n, int B) {
   L.z[0] = take(Bz * H * 4);
   L.z[1] = take(Bz * H * 4);
   L.head = take(lmhead_ws_bytes(B, m.hidden, m.vocab, m.dtype));
-  L.lists_p = take(2 * Bz * 4);
-  L.counts_p = take(2 * 4);
-  L.lists_f = take(static_cast<size_t>(n) * Bz * 4);
-  L.counts_f = take(static_cast<size_t>(n) * 4);
   L.total = o;
   return L;
 }
@@ -179,10 +160,6 @@ void run_draft(const moev_model& m, const moev_draft_weights& d, const float* z_
   void* act = ws + L.act;
   float* yf = reinterpret_cast<float*>(ws + L.yf);
   float* zb[2] = {reinterpret_cast<float*>(ws + L.z[0]), reinterpret_cast<float*>(ws + L.z[1])};
-  int32_t* lists_p = reinterpret_cast<int32_t*>(ws + L.lists_p);
-  int32_t* counts_p = reinterpret_cast<int32_t*>(ws + L.counts_p);
-  int32_t* lists_f = reinterpret_cast<int32_t*>(ws + L.lists_f);
-  int32_t* counts_f = reinterpret_cast<int32_t*>(ws + L.counts_f);
   for (int j = 0; j < K; ++j) {
     DraftInArgs a{};
     a.z = j == 0 ? z_src : zb[(j - 1) & 1];
@@ -200,19 +177,16 @@ void run_draft(const moev_model& m, const moev_draft_weights& d, const float* z_
     a.norm_e = d.norm_e;
     a.eps = m.eps;
     a.x2 = x2;
-    a.lists_p = j == 0 ? lists_p : nullptr;
-    a.counts_p = counts_p;
-    a.lists_f = lists_f;
-    a.counts_f = counts_f;
-    a.n = n;
     if (dt == MOEV_BF16) draft_in_kernel<u16><<<B, kDraftThreads, 0, s>>>(a);
     else draft_in_kernel<float><<<B, kDraftThreads, 0, s>>>(a);
-    // z' = W_p[:, :H] u_z + W_p[:, H:] u_e: two groups of K = H, weight 1
-    // (these GEMMs cover 2 or n groups only: split K fills the GPU)
-    launch_ffn_down_lists(x2, lists_p, counts_p, nullptr, d.w_proj, B, H, H, 0, 0, 2, dt, yp, s, true);
+    // z' = W_p[:, :H] u_z + W_p[:, H:] u_e: two groups of K = H, weight 1,
+    // each holding every row (pair b * 2 + group); the FFN's n slices
+    // likewise (pair b * n + slice).  These GEMMs cover 2 or n groups only:
+    // split K fills the GPU.
+    launch_ffn_down_sets(x2, nullptr, nullptr, d.w_proj, B, H, H, 0, 0, 2, dt, yp, s, true);
     launch_norm_cast(nullptr, yp, 2, d.norm_ffn, m.eps, B, H, dt, xf, zp, s);
-    launch_ffn_gate_up_lists(xf, lists_f, counts_f, d.w_gate, d.w_up, B, H, I, 0, 0, n, dt, act, s, true);
-    launch_ffn_down_lists(act, lists_f, counts_f, nullptr, d.w_down, B, H, I, 0, 0, n, dt, yf, s, true);
+    launch_ffn_gate_up_sets(xf, nullptr, d.w_gate, d.w_up, B, H, I, 0, 0, n, dt, act, s, true);
+    launch_ffn_down_sets(act, nullptr, nullptr, d.w_down, B, H, I, 0, 0, n, dt, yf, s, true);
     float* zj = (j == K - 1 && z_out != nullptr) ? z_out : zb[j & 1];
     launch_lmhead(zp, d.norm_out, m.eps, m.w_lm, B, H, m.vocab, dt, out + out_col0 + j, nullptr,
                   nullptr, ws + L.head, s, yf, n, zj, out_stride);

@@ -45,7 +45,7 @@ constexpr int kRtHead = 2;           // 16-row tiles per wave, LM head
 constexpr int kWavesFfn = 4;         // wavefronts per workgroup, expert GEMMs
 constexpr int kTileMinTokens = 128;  // larger batches use the tile schedule
 constexpr int kWavesHead = 8;        // wavefronts per workgroup, LM head
-static_assert(kTileMinTokens == kListMaxTokens, "the step's list mode is the streaming schedule's range");
+static_assert(kTileMinTokens == kSetMaxTokens, "the step's token-set mode is the streaming schedule's range");
 
 // MT = tokens per pass (32, 64 or 128 = 2, 4 or 8 MFMA column tiles).  The
 // variant only changes how many accumulators and LDS rows a workgroup holds;
@@ -68,8 +68,13 @@ struct GemmArgs {
   const void* x;            // operand rows
   const int32_t* offsets;   // [G+1] (gate/up, down)
   const int32_t* sorted_src;
-  const int32_t* counts;    // expert-list mode (streaming schedule only): group g
-                            // is sorted_src[g*T ..] with counts[g] pairs, act row g*T
+  // token-set mode (streaming schedule only, T <= 128): routed group g < E
+  // holds the tokens whose bit is set in masks[g*W ..], shared groups every
+  // token; group g's m-th token has act row g*T + m (see TokenSets)
+  bool sets;
+  int E, W;
+  const uint64_t* masks;    // [E][W]
+  const int2* pinfo;        // [T][E] (down): {bits of the pair's weight, slot}
 
   int S, k, P, T;           // slots, routed slots, pairs, tokens
   int n_first;              // the last n_first groups (the shared experts, which
@@ -104,12 +109,88 @@ template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// Position of the m-th set bit (m counted from 0) of the 128-bit set
+// {lo, hi}; m is below the set's population count.  Halving search on the
+// population counts of the lower halves.
+__device__ __forceinline__ int nth_set_bit(uint64_t lo, uint64_t hi, int m) {
+  const int c = __popcll(lo);
+  uint64_t w = m < c ? lo : hi;
+  int pos = m < c ? 0 : 64;
+  m = m < c ? m : m - c;
+#pragma unroll
+  for (int sh = 32; sh > 0; sh >>= 1) {
+    const int cl = __popcll(w & ((1ull << sh) - 1));
+    if (m >= cl) {
+      m -= cl;
+      w >>= sh;
+      pos += sh;
+    }
+  }
+  return pos;
+}
+
+// The tokens of one group of the token-set mode: a routed group's mask, or
+// every token (masked = false).
+struct TokenSel {
+  uint64_t lo = 0, hi = 0;
+  bool masked = false;
+  int g = 0;
+};
+
+__device__ __forceinline__ int set_token(const GemmArgs& a, const TokenSel& sel, int m) {
+  return sel.masked ? min(nth_set_bit(sel.lo, sel.hi, m), a.T - 1) : m;
+}
+
 // Row of the operand matrix that token row `row` of this pass reads.
 template <int MODE>
-__device__ __forceinline__ long long operand_row(const GemmArgs& a, int off, int m0, int row) {
-  if (MODE == kGateUp) return clampi(a.sorted_src[off + m0 + row], 0, a.P - 1) / a.S;
+__device__ __forceinline__ long long operand_row(const GemmArgs& a, const TokenSel& sel, int off, int m0,
+                                                 int row) {
+  if (MODE == kGateUp)
+    return a.sets ? set_token(a, sel, m0 + row) : clampi(a.sorted_src[off + m0 + row], 0, a.P - 1) / a.S;
   if (MODE == kDown) return off + m0 + row;
   return m0 + row;
+}
+
+// Down projection: output pair and router weight of token row m of a pass,
+// read when the pass starts so the epilogue does not wait for them.
+struct PairMeta {
+  int p = 0;
+  float wgt = 1.f;
+};
+
+__device__ __forceinline__ PairMeta pair_meta(const GemmArgs& a, const TokenSel& sel, int off, int m) {
+  PairMeta r;
+  int t, slot;
+  if (a.sets) {
+    t = set_token(a, sel, m);
+    if (sel.masked) {
+      const int2 pi = a.pinfo[static_cast<long long>(t) * a.E + sel.g];
+      slot = clampi(pi.y, 0, a.k - 1);
+      r.wgt = __int_as_float(pi.x);
+    } else {
+      slot = a.k + sel.g - a.E;
+    }
+    r.p = t * a.S + slot;
+  } else {
+    r.p = clampi(a.sorted_src[off + m], 0, a.P - 1);
+    t = r.p / a.S;
+    slot = r.p - t * a.S;
+    if (slot < a.k) r.wgt = a.topk_w[static_cast<long long>(t) * a.k + slot];
+  }
+  return r;
+}
+
+template <int MODE, int NTX>
+__device__ __forceinline__ void load_meta(const GemmArgs& a, const TokenSel& sel, int off, int m0, int mp,
+                                          PairMeta (&meta)[NTX]) {
+  if constexpr (MODE == kDown) {
+    const int r16 = threadIdx.x & 15;
+#pragma unroll
+    for (int j = 0; j < NTX; ++j) {
+      const int m = j * 16 + r16;
+      if (m < mp) meta[j] = pair_meta(a, sel, off, m0 + m);
+    }
+  }
 }
 
 // Epilogue of one pass: lane (r16, q) holds rows rowbase[rt] + 4q + v of
@@ -117,7 +198,7 @@ __device__ __forceinline__ long long operand_row(const GemmArgs& a, int off, int
 template <typename WT, int MODE, int RT, int MT, int NTX, int W>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, unsigned char* __restrict__ lds,
                                          const f32x4 (&acc)[RT][NTX], int off, int m0, int mp,
-                                         const int (&rowbase)[RT]) {
+                                         const int (&rowbase)[RT], const PairMeta (&meta)[NTX]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -143,10 +224,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, unsigned char* __res
     for (int j = 0; j < NTX; ++j) {
       const int m = j * 16 + r16;
       if (m < mp) {
-        const int p = clampi(a.sorted_src[off + m0 + m], 0, a.P - 1);
-        const int t = p / a.S;
-        const int slot = p - t * a.S;
-        const float wgt = slot < a.k ? a.topk_w[static_cast<long long>(t) * a.k + slot] : 1.0f;
+        const int p = meta[j].p;
+        const float wgt = meta[j].wgt;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           f32x4 o = acc[rt][j];
@@ -219,7 +298,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, unsigned char* __res
 // of KS = 1, so a caller uses one KS for all its sizes.
 template <typename WT, int MODE, int RT, int MT, int NTX, int W, int KS = 1>
 __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned char* __restrict__ lds,
-                                                 int off, int m0, int mp,
+                                                 const TokenSel& sel, int off, int m0, int mp,
                                                  const WT* const (&wp)[RT],
                                                  const int (&rowbase)[RT]) {
   static_assert(KS == 1 || (KS == W && MODE != kHead), "split K: one K range per wave, expert GEMMs");
@@ -235,8 +314,10 @@ __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned cha
 #pragma unroll
   for (int j = 0; j < NTX; ++j) {
     const int m = j * 16 + r16;
-    xp[j] = xsrc + operand_row<MODE>(a, off, m0, m < mp ? m : 0) * K + q * 8;
+    xp[j] = xsrc + operand_row<MODE>(a, sel, off, m0, m < mp ? m : 0) * K + q * 8;
   }
+  PairMeta meta[NTX];
+  load_meta<MODE, NTX>(a, sel, off, m0, mp, meta);
   f32x4 acc[RT][NTX];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -290,11 +371,11 @@ __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned cha
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[rt][j][v] += o[v];
           }
-      epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
+      epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase, meta);
     }
     __syncthreads();  // red is free for the next pass
   } else {
-    epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
+    epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase, meta);
   }
 }
 
@@ -304,7 +385,7 @@ __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned cha
 // dropped by the epilogue.
 template <typename WT, int MODE, int RT, int MT, int NTX, int W>
 __device__ __forceinline__ void gemm_pass_lds(const GemmArgs& a, unsigned char* __restrict__ lds,
-                                              int off, int m0, int mp,
+                                              const TokenSel& sel, int off, int m0, int mp,
                                               const WT* const (&wp)[RT], const int (&rowbase)[RT]) {
   using C = Cfg<WT, MT>;
   constexpr int kThreads = W * kWave;
@@ -325,9 +406,11 @@ __device__ __forceinline__ void gemm_pass_lds(const GemmArgs& a, unsigned char* 
     const int v = tid + s * kThreads;
     const int row = v / C::kVecPerRow;
     const int cv = v - row * C::kVecPerRow;
-    src[s] = (v < kVecs && row < mp) ? xsrc + operand_row<MODE>(a, off, m0, row) * K + cv * C::kEpv
+    src[s] = (v < kVecs && row < mp) ? xsrc + operand_row<MODE>(a, sel, off, m0, row) * K + cv * C::kEpv
                                      : nullptr;
   }
+  PairMeta meta[NTX];
+  load_meta<MODE, NTX>(a, sel, off, m0, mp, meta);
   uint4 stage[kStage];
 #pragma unroll
   for (int s = 0; s < kStage; ++s)
@@ -387,7 +470,7 @@ __device__ __forceinline__ void gemm_pass_lds(const GemmArgs& a, unsigned char* 
       }
     }
   }
-  epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase);
+  epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase, meta);
 }
 
 // One workgroup of the streaming schedule: row slab bx of group slot by,
@@ -405,13 +488,22 @@ __device__ __forceinline__ void stream_gemm_wg(const GemmArgs& a, int bx, int by
   const int lane = tid & 63;
 
   int g = 0, off = 0, M;
+  TokenSel sel;
   if (MODE == kHead) {
     M = a.T;
   } else {
     g = by < a.n_first ? G - a.n_first + by : by - a.n_first;
-    if (a.counts != nullptr) {
+    sel.g = g;
+    if (a.sets) {
       off = g * a.T;
-      M = clampi(a.counts[g], 0, a.T);
+      M = a.T;
+      if (g < a.E) {
+        const uint64_t* mk = a.masks + static_cast<long long>(g) * a.W;
+        sel.lo = mk[0];
+        sel.hi = a.W > 1 ? mk[1] : 0ull;
+        sel.masked = true;
+        M = min(__popcll(sel.lo) + __popcll(sel.hi), a.T);
+      }
     } else {
       off = clampi(a.offsets[g], 0, a.P);
       M = clampi(a.offsets[g + 1], off, a.P) - off;
@@ -447,14 +539,14 @@ __device__ __forceinline__ void stream_gemm_wg(const GemmArgs& a, int bx, int by
     const int mp = min(MT, M - m0);
     // the branches are uniform across the workgroup
     if (mp <= 16) {
-      gemm_pass_direct<WT, MODE, RT, MT, 1, W, KS>(a, lds, off, m0, mp, wp, rowbase);
+      gemm_pass_direct<WT, MODE, RT, MT, 1, W, KS>(a, lds, sel, off, m0, mp, wp, rowbase);
     } else if (mp <= 32) {
-      gemm_pass_direct<WT, MODE, RT, MT, 2, W, KS>(a, lds, off, m0, mp, wp, rowbase);
+      gemm_pass_direct<WT, MODE, RT, MT, 2, W, KS>(a, lds, sel, off, m0, mp, wp, rowbase);
     } else if constexpr (NT >= 4) {
       if (mp <= 64 || NT == 4)
-        gemm_pass_lds<WT, MODE, RT, MT, 4, W>(a, lds, off, m0, mp, wp, rowbase);
+        gemm_pass_lds<WT, MODE, RT, MT, 4, W>(a, lds, sel, off, m0, mp, wp, rowbase);
       else
-        gemm_pass_lds<WT, MODE, RT, MT, NT, W>(a, lds, off, m0, mp, wp, rowbase);
+        gemm_pass_lds<WT, MODE, RT, MT, NT, W>(a, lds, sel, off, m0, mp, wp, rowbase);
     }
   }
 }
@@ -701,13 +793,13 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
         const int r = lane >> 3;
         const int row = min(ii * 8 + r, mp - 1);
         const int c = (lane & 7) ^ r ^ (ii & 1);
-        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, off, m0, row) * K + c * 8;
+        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, TokenSel{}, off, m0, row) * K + c * 8;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < kXPtr; ++i) {
         const int row = min((wave * TC::kXPerWave + i) * 16 + r16, mp - 1);
-        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, off, m0, row) * K + q * 8;
+        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, TokenSel{}, off, m0, row) * K + q * 8;
       }
     }
   };
@@ -1267,11 +1359,20 @@ void launch_ffn_down(const void* act, const int32_t* sorted_src, const int32_t* 
     launch_gemm<float, kDown, kRtDown, kWavesFfn>(dn, grid, s);
 }
 
-void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t* counts,
-                              const void* w_gate, const void* w_up, int T, int H, int I, int E,
-                              int k, int ns, int dt, void* act, hipStream_t s, bool split_k) {
-  GemmArgs up = ffn_args(list, nullptr, T, H, I, k, ns);
-  up.counts = counts;
+GemmArgs set_args(const uint64_t* masks, const int2* pinfo, int T, int H, int I, int E, int k, int ns) {
+  GemmArgs a = ffn_args(nullptr, nullptr, T, H, I, k, ns);
+  a.sets = true;
+  a.E = E;
+  a.W = (T + 63) / 64;
+  a.masks = masks;
+  a.pinfo = pinfo;
+  return a;
+}
+
+void launch_ffn_gate_up_sets(const void* x, const uint64_t* masks, const void* w_gate,
+                             const void* w_up, int T, int H, int I, int E, int k, int ns, int dt,
+                             void* act, hipStream_t s, bool split_k) {
+  GemmArgs up = set_args(masks, nullptr, T, H, I, E, k, ns);
   up.w0 = w_gate;
   up.w1 = w_up;
   up.w_group = static_cast<long long>(I) * H;
@@ -1294,18 +1395,15 @@ void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t*
     launch_gemm<float, kGateUp, 2, kWavesFfn>(up, grid, s);
 }
 
-void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* counts,
-                           const float* topk_w, const void* w_down, int T, int H, int I, int E,
-                           int k, int ns, int dt, float* y_slots, hipStream_t s, bool split_k,
-                           int pass_split) {
-  GemmArgs dn = ffn_args(list, nullptr, T, H, I, k, ns);
-  dn.counts = counts;
+void launch_ffn_down_sets(const void* act, const uint64_t* masks, const int2* pinfo,
+                          const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
+                          float* y_slots, hipStream_t s, bool split_k, int pass_split) {
+  GemmArgs dn = set_args(masks, pinfo, T, H, I, E, k, ns);
   dn.w0 = w_down;
   dn.w_group = static_cast<long long>(H) * I;
   dn.N = H;
   dn.K = I;
   dn.x = act;
-  dn.topk_w = topk_w;
   dn.out = y_slots;
   // dense projections of a whole batch (pass_split > 1): two 16-row tiles per
   // workgroup halve the operand rows' L2 re-reads; the K order of every output

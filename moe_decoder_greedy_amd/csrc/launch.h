@@ -6,36 +6,40 @@
 
 namespace moev {
 
-// Expert lists (the whole-step driver's replacement for the sorted pair
-// order at decode sizes): group g's pairs are list[g*T .. g*T + counts[g]),
-// in any order (each token's expert output depends on its own row only).
-// Routed groups are filled by the router with one atomic per pair; shared
-// groups always hold every token in order.
-struct ExpertLists {
-  int32_t* counts;  // [n_sets][G]: one set per layer
-  int32_t* list;    // [G][T]
-  int n_sets, E, G, k, S;
+// Token sets (the whole-step driver's replacement for the sorted pair order
+// at decode sizes, T <= kSetMaxTokens): routed group g < E holds the tokens
+// whose bit is set in masks[g*W ..] (bit t % 64 of word t / 64, W =
+// ceil(T / 64)), in increasing token order, and pair (t, g) has pinfo[t*E +
+// g] = {bits of its renormalised router weight, its slot}.  The router sets
+// both with no returned value to wait for (an atomic OR and a store).
+// Groups g >= E (the shared experts, and every group of a dense projection,
+// E = 0) hold every token in order, slot k + g - E, weight 1.  Group g's m-th
+// token has act row g*T + m.
+struct TokenSets {
+  uint64_t* masks;  // [n_sets][E][W]: one set per layer
+  int2* pinfo;      // [T][E]
+  int n_sets, E, W;
 };
-// list mode only on the streaming GEMM schedule; above this many tokens the
-// tiled schedule is faster
-constexpr int kListMaxTokens = 128;
+// token-set mode only on the streaming GEMM schedule; above this many tokens
+// the tiled schedule is faster (and a set fits two 64-bit words)
+constexpr int kSetMaxTokens = 128;
+constexpr int set_words(int T) { return (T + 63) / 64; }
 
-// lists != NULL: also resets every count set (routed 0, shared T) and writes
-// the shared groups' lists.
+// sets != NULL: also clears every mask set.
 void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, int dt, float* h,
-                  hipStream_t s, const ExpertLists* lists = nullptr);
+                  hipStream_t s, const TokenSets* sets = nullptr);
 void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,
                   const float* bias, int T, int H, int E, int k, int dt, void* x_out,
                   int32_t* topk_idx, float* topk_w, float* logits_out, hipStream_t s);
 // Router with the previous layer's combine folded in (y_prev != NULL: h_out =
 // h + the sum of y_prev's S_prev slots, in slot order); h_out may equal h.
-// counts/list != NULL: each token's k pairs are also appended to the expert
-// lists (pair = t * S_pairs + slot).
+// masks != NULL: each token's k pairs also go into the token sets (masks of
+// this layer's set, pinfo; T <= kSetMaxTokens).
 void launch_route_fused(const float* h, const float* y_prev, int S_prev, float* h_out,
                         const void* norm_w, float eps, const void* w_router, const float* bias,
                         int T, int H, int E, int k, int dt, void* x_out, int32_t* topk_idx,
-                        float* topk_w, hipStream_t s, int32_t* counts = nullptr,
-                        int32_t* list = nullptr, int S_pairs = 0);
+                        float* topk_w, hipStream_t s, uint64_t* masks = nullptr,
+                        int2* pinfo = nullptr);
 void launch_permute(const int32_t* topk_idx, int T, int k, int E, int ns, int32_t* offsets,
                     int32_t* sorted_src, hipStream_t s);
 void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,
@@ -63,21 +67,20 @@ void run_draft(const moev_model& m, const moev_draft_weights& d, const float* z_
                int out_stride, int out_col0, int32_t* t0_copy, float* z_out, unsigned char* ws,
                hipStream_t s);
 
-// Expert GEMMs reading expert lists (T <= kListMaxTokens): act holds G*T rows.
-// split_k: each workgroup's waves split one row tile's K range (passes of at
-// most 32 tokens, every size): several times the workgroups for GEMMs over a
-// few groups, with rounding that differs from split_k = false, so a caller
-// keeps one setting.
-void launch_ffn_gate_up_lists(const void* x, const int32_t* list, const int32_t* counts,
-                              const void* w_gate, const void* w_up, int T, int H, int I, int E,
-                              int k, int ns, int dt, void* act, hipStream_t s, bool split_k = false);
+// Expert GEMMs over token sets (T <= kSetMaxTokens; masks and pinfo may be
+// NULL when E = 0): act holds G*T rows.  split_k: each workgroup's waves split
+// one row tile's K range (passes of at most 32 tokens, every size): several
+// times the workgroups for GEMMs over a few groups, with rounding that
+// differs from split_k = false, so a caller keeps one setting.
+void launch_ffn_gate_up_sets(const void* x, const uint64_t* masks, const void* w_gate,
+                             const void* w_up, int T, int H, int I, int E, int k, int ns, int dt,
+                             void* act, hipStream_t s, bool split_k = false);
 // pass_split (split_k only): the 32-token passes are spread over this many
 // workgroups per row tile (grid z), for dense projections of a whole batch;
 // with pass_split > 1 a workgroup takes two 16-row tiles (H % 32 == 0).
-void launch_ffn_down_lists(const void* act, const int32_t* list, const int32_t* counts,
-                           const float* topk_w, const void* w_down, int T, int H, int I, int E,
-                           int k, int ns, int dt, float* y_slots, hipStream_t s,
-                           bool split_k = false, int pass_split = 1);
+void launch_ffn_down_sets(const void* act, const uint64_t* masks, const int2* pinfo,
+                          const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
+                          float* y_slots, hipStream_t s, bool split_k = false, int pass_split = 1);
 void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
                     hipStream_t s);
 // out[i] = h[t] + the sum of y's S slots of row t (y may be NULL), t = the

@@ -7,12 +7,14 @@
 // softmax renormalised over the selected experts, i.e. exp(l_r - l_max) over
 // the sum of the k chosen exp(l_j - l_max).
 //
-// Layout of one block (1024 threads = 16 wavefronts, TPB = 1, 4 or 16
+// Layout of one block (1024 threads = 16 wavefronts, TPB = 1, 4 or 8
 // tokens: more blocks in flight for small batches, more tokens per fetch of
 // the router matrix for large ones):
-//   start    wave w fetches the router rows of experts 4w..4w+3 into
-//            registers (coalesced 8-byte bf16 loads, all in flight), so the
-//            weight fetch overlaps phase 1;
+//   phase 0  the block's residual rows (with the previous layer's expert
+//            slots added, when fused) into LDS; at decode sizes wave w also
+//            requests the router rows of experts 4w..4w+3 into registers
+//            right behind them (coalesced 8-byte bf16 loads, all in flight),
+//            so the weight fetch overlaps phases 0 and 1;
 //   phase 1  waves 0..TPB-1, one per token: sum of squares (per-lane strided
 //            partials, then a DPP reduction), x = h * rsqrt-scale * gamma into
 //            LDS (fp32) and to x_out (rounded to the operand type);
@@ -33,23 +35,19 @@ namespace {
 
 constexpr int kRouteGroupMax = 4;    // tokens per logit pass
 constexpr int kRouteThreads = 1024;   // 16 wavefronts
+constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kExpertsPerWave = 4;    // 16 waves x 4 = 64 experts
 constexpr int kMaxSlots = 16;         // k + ns limit of the fused combine
 
 template <typename WT>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
                                                     const WT* __restrict__ emb, int T, int H, int V,
-                                                    float* __restrict__ h, ExpertLists lists) {
+                                                    float* __restrict__ h, TokenSets sets) {
   const int t = blockIdx.x;
-  if (lists.list != nullptr) {
-    // block t writes token t's entry of every shared list; block 0 resets the
-    // count sets (routed 0, shared T)
-    const int ns = lists.G - lists.E;
-    if (threadIdx.x < ns)
-      lists.list[static_cast<size_t>(lists.E + threadIdx.x) * T + t] = t * lists.S + lists.k + threadIdx.x;
-    if (t == 0)
-      for (int i = threadIdx.x; i < lists.n_sets * lists.G; i += blockDim.x)
-        lists.counts[i] = (i % lists.G) < lists.E ? 0 : T;
+  if (sets.masks != nullptr) {
+    // the blocks clear the mask sets of every layer between them
+    const int n = sets.n_sets * sets.E * sets.W;
+    for (int i = t * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) sets.masks[i] = 0ull;
   }
   int tok = tokens[t];
   tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
@@ -73,24 +71,29 @@ struct RouteArgs {
   int32_t* topk_idx;
   float* topk_w;
   float* logits_out;
-  int32_t* counts;       // expert lists (optional): per-group counts
-  int32_t* list;         //   and [G][T] pair lists
-  int S_pairs;           //   pair = t * S_pairs + slot
+  uint64_t* masks;       // token sets (optional): this layer's [E][W] masks
+  int2* pinfo;           //   and [T][E] pair entries {weight bits, slot}
+  int W;
 };
 
 // NCH = ceil(H / 256): 4-element chunks per lane per row, a compile-time count
 // so that every router-row load of a wave is in flight at once.
 // COMBINE: phase 0 first adds the previous layer's expert slots to the
 // residual (the same left-to-right slot order as the combine kernel, so the
-// bits are identical) and writes the new residual.
-// PRELOAD: the router rows are fetched into registers before phase 0 (as
-// fp32), so that fetch overlaps it; without PRELOAD each chunk of them is
-// fetched (as raw bf16 / fp32) inside the logit loop, which keeps the block
-// small enough for two per CU (8 waves per SIMD: the second launch bound):
-// while one block computes logits, the other
-// streams its residual rows and expert slots.  The arithmetic of every logit
-// is the same either way.
-template <typename WT, int NCH, bool COMBINE, int kRouteTPB, bool PRELOAD>
+// bits are identical) and writes the new residual; SL >= S bounds the
+// unrolled slot loads.
+// PRELOAD (decode sizes, one block per CU): every load of the block is
+// issued up front -- the small operands (bias, RMSNorm gain), the residual
+// rows and slots, then the router rows -- and the block's global stores
+// (new residual, normalised operand) wait until the logits are done, so no
+// wait for a load is also a wait for a store (the vector memory counter
+// counts both, in order).  Without PRELOAD each chunk of the router rows is
+// fetched inside the logit loop and the stores go out as soon as their
+// values exist, which keeps the block small enough for two per CU (8 waves
+// per SIMD: the second launch bound): while one block computes logits, the
+// other streams its residual rows and expert slots.  The arithmetic of every
+// logit is the same either way.
+template <typename WT, int NCH, bool COMBINE, int kRouteTPB, bool PRELOAD, int SL = kMaxSlots>
 __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(RouteArgs a) {
   extern __shared__ float smem[];
   const int H = a.H, E = a.E, k = a.k, T = a.T;
@@ -101,53 +104,77 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
   float* lg = smem + kRouteTPB * H;                             // [TPB][64]
   float* sel_v = lg + kRouteTPB * 64;                           // [TPB][64]
   int* sel_i = reinterpret_cast<int*>(sel_v + kRouteTPB * 64);  // [TPB][64]
-  const int wave = threadIdx.x >> 6;
+  int* rpart = sel_i + kRouteTPB * 64;                          // [TPB][kWpt][64]
+  // the wave index is uniform: expert indices and bias reads stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * kRouteTPB;
-
-  // router rows of this wave's experts, fetched before anything else so the
-  // fetch overlaps the RMSNorm phase
   const int e0 = wave * kExpertsPerWave;
+  const int nt = min(kRouteTPB, T - t0);
+  constexpr int kStageIt = (kRouteTPB * NCH * 64 + kRouteThreads - 1) / kRouteThreads;
+  constexpr bool kDefer = PRELOAD;  // stores after the logits
+  constexpr int kWpt = kRouteWaves / kRouteTPB;  // waves counting one token's ranks
+  constexpr int kEpw = 64 / kWpt;                // entries each of them compares
+  static_assert(kEpw % 4 == 0, "rank parts over whole float4 reads");
+
+  // bias entries of this wave's experts: read unconditionally (from the
+  // residual rows, T * H >= 64 floats, when there is no bias) and selected,
+  // so no branch waits for them here
+  const float* bsrc = a.bias != nullptr ? a.bias : a.h;
+  float bv[kExpertsPerWave];
+#pragma unroll
+  for (int u = 0; u < kExpertsPerWave; ++u) bv[u] = bsrc[min(e0 + u, E - 1)];
+  // RMSNorm gain for the waves that normalise a token, kept raw until used
+  typename Vec4<WT>::Raw graw[NCH];
+  const bool has_gain = norm_w != nullptr;
+  if (wave < kRouteTPB && has_gain) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) graw[c] = Vec4<WT>::load_raw(norm_w + min(lane * 4 + c * 256, H - 4));
+  }
   float4 wv[kExpertsPerWave][PRELOAD ? NCH : 1];
-  if constexpr (PRELOAD) {
+  auto preload_router = [&]() {
+    if constexpr (PRELOAD) {
 #pragma unroll
-    for (int u = 0; u < kExpertsPerWave; ++u) {
-      const int e = min(e0 + u, E - 1);
+      for (int u = 0; u < kExpertsPerWave; ++u) {
+        const int e = min(e0 + u, E - 1);
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int i = min(lane * 4 + c * 256, H - 4);
-        wv[u][c] = Vec4<WT>::load(wr + static_cast<size_t>(e) * H + i);
+        for (int c = 0; c < NCH; ++c) {
+          const int i = min(lane * 4 + c * 256, H - 4);
+          wv[u][c] = Vec4<WT>::load(wr + static_cast<size_t>(e) * H + i);
+        }
       }
     }
-  }
+  };
 
   // phase 0: all threads stage the block's residual rows into LDS (xs),
   // adding the previous layer's expert slots first when COMBINE; every slot
   // load of a thread is issued before the sum, which runs left to right in
   // slot order exactly as the combine kernel does
+  float4 hkeep[kDefer ? kStageIt : 1];  // new residual, stored after the logits
   {
-    const int nt0 = min(kRouteTPB, T - t0);
     const int h4 = H / 4;
-    // H <= 256 * NCH, so kStageIt passes cover the block's rows; a fixed
-    // count lets every pass's loads be issued before the first is used
-    constexpr int kStageIt = (kRouteTPB * NCH * 64 + kRouteThreads - 1) / kRouteThreads;
 #pragma unroll
     for (int it = 0; it < kStageIt; ++it) {
       const int f = threadIdx.x + it * kRouteThreads;
-      if (f >= nt0 * h4) break;
+      const bool live = f < nt * h4;
       const int tt = f / h4;
       const int i = (f - tt * h4) * 4;
       const size_t t = static_cast<size_t>(t0 + tt);
-      float4 v = *reinterpret_cast<const float4*>(a.h + t * H + i);
+      float4 v, sv[SL];
+      const float4* ys = reinterpret_cast<const float4*>(a.y + t * a.S * H + i);
+      if (live) {
+        v = *reinterpret_cast<const float4*>(a.h + t * H + i);
+        if (COMBINE && PRELOAD) load_slots<SL>(sv, ys, a.S, h4);
+      }
+      if (it == 0) preload_router();
+      if (!live) continue;
       if (COMBINE) {
-        const float4* ys = reinterpret_cast<const float4*>(a.y + t * a.S * H + i);
-        float4 acc;
         if constexpr (PRELOAD) {
-          v = add_slots<kMaxSlots>(v, ys, a.S, h4);
+          v = sum_slots<SL>(v, sv, a.S);
         } else {  // the same left-to-right sum, each slot added as it arrives
-          acc = ys[0];
+          float4 acc = ys[0];
 #pragma unroll
-          for (int sl = 1; sl < kMaxSlots; ++sl)
+          for (int sl = 1; sl < SL; ++sl)
             if (sl < a.S) {
               const float4 yv = ys[static_cast<size_t>(sl) * h4];
               acc.x += yv.x;
@@ -157,7 +184,8 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
             }
           v = make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
         }
-        *reinterpret_cast<float4*>(a.h_out + t * H + i) = v;
+        if constexpr (kDefer) hkeep[it] = v;
+        else *reinterpret_cast<float4*>(a.h_out + t * H + i) = v;
       }
       *reinterpret_cast<float4*>(xs + tt * H + i) = v;
     }
@@ -166,17 +194,16 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
 
   // phase 1: RMSNorm in place in LDS, wave w < TPB takes token t0 + w; the
   // logit row's entries past E are set to -inf (never ranked above a real one)
+  float4 xkeep[kDefer ? NCH : 1];  // normalised operand, stored after the logits
   if (wave < kRouteTPB) {
     const int t = t0 + wave;
     if (lane >= E) lg[wave * 64 + lane] = -INFINITY;
     if (t < T) {
-      float4 hv[NCH], gv[NCH];
+      float4 hv[NCH];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int i = lane * 4 + c * 256;
-        const bool in = i < H;
-        hv[c] = in ? *reinterpret_cast<const float4*>(xs + wave * H + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-        gv[c] = (in && norm_w) ? Vec4<WT>::load(norm_w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
+        hv[c] = i < H ? *reinterpret_cast<const float4*>(xs + wave * H + i) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
       float ss = 0.f;
 #pragma unroll
@@ -186,10 +213,12 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
       for (int c = 0; c < NCH; ++c) {
         const int i = lane * 4 + c * 256;
         if (i < H) {
-          const float4 v = hv[c], g = gv[c];
+          const float4 v = hv[c];
+          const float4 g = has_gain ? Vec4<WT>::from_raw(graw[c]) : make_float4(1.f, 1.f, 1.f, 1.f);
           const float4 x = make_float4(v.x * r * g.x, v.y * r * g.y, v.z * r * g.z, v.w * r * g.w);
           *reinterpret_cast<float4*>(xs + wave * H + i) = x;
-          Vec4<WT>::store(x_out + static_cast<size_t>(t) * H + i, x);
+          if constexpr (kDefer) xkeep[c] = x;
+          else Vec4<WT>::store(x_out + static_cast<size_t>(t) * H + i, x);
         }
       }
     }
@@ -198,7 +227,6 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
 
   // phase 2: router logits of this wave's experts for the block's tokens,
   // kRouteGroup tokens per pass (the same per-token arithmetic whatever TPB)
-  const int nt = min(kRouteTPB, T - t0);
   constexpr int kRouteGroup = kRouteTPB < kRouteGroupMax ? kRouteTPB : kRouteGroupMax;
   if (e0 < E) {
 #pragma unroll
@@ -231,7 +259,7 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
       for (int u = 0; u < kExpertsPerWave; ++u) {
         const int e = e0 + u;
         if (e < E) {
-          const float b = a.bias ? a.bias[e] : 0.f;
+          const float b = a.bias != nullptr ? bv[u] : 0.f;
 #pragma unroll
           for (int tt = 0; tt < kRouteGroup; ++tt) {
             const float s = wave_sum_lane63(acc[u][tt]);
@@ -243,17 +271,27 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
   }
   __syncthreads();
 
-  // phase 3: top-k + renormalised softmax, one wave per token, one lane per
-  // expert.  Each lane counts the experts that beat it (larger logit, or equal
-  // logit and lower index): that count is its rank, and the k lanes of rank
-  // < k file themselves into sel_* by rank.
+  // phase 3: top-k + renormalised softmax, one lane per expert.  Each lane's
+  // rank is the number of experts that beat it (larger logit, or equal logit
+  // and lower index); the kWpt waves of a token count it over kEpw entries
+  // each, then one wave per token adds the parts, and the k lanes of rank < k
+  // file themselves into sel_* by rank.
+  {
+    const int tt = wave / kWpt, pw = wave - tt * kWpt;
+    if (t0 + tt < T) {
+      const float* row = lg + tt * 64;
+      rpart[(tt * kWpt + pw) * 64 + lane] = logit_rank_part<kEpw>(row, pw * kEpw, row[lane], lane);
+    }
+  }
+  __syncthreads();
   if (wave < kRouteTPB) {
     const int t = t0 + wave;
     if (t < T) {
       const float* row = lg + wave * 64;
       const float v = row[lane];
-      if (a.logits_out != nullptr && lane < E) a.logits_out[static_cast<size_t>(t) * E + lane] = v;
-      const int rank = logit_rank(row, v, lane);
+      int rank = 0;
+#pragma unroll
+      for (int pw = 0; pw < kWpt; ++pw) rank += rpart[(wave * kWpt + pw) * 64 + lane];
       if (lane < E && rank < k) {
         sel_v[wave * 64 + rank] = v;
         sel_i[wave * 64 + rank] = lane;
@@ -261,27 +299,50 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // the ranks are a permutation for finite logits; the clamp keeps the
+      // token-set writes in bounds whatever the inputs
+      const int e = min(max(sel_i[wave * 64 + min(lane, k - 1)], 0), E - 1);
+      if (a.logits_out != nullptr && lane < E) a.logits_out[static_cast<size_t>(t) * E + lane] = v;
+      if constexpr (kDefer) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const int i = lane * 4 + c * 256;
+          if (i < H) Vec4<WT>::store(x_out + static_cast<size_t>(t) * H + i, xkeep[c]);
+        }
+      }
       if (lane < k) {
-        // the ranks are a permutation for finite logits; the clamp keeps the
-        // list append in bounds whatever the inputs
-        const int e = min(max(sel_i[wave * 64 + lane], 0), E - 1);
+        const float wgt = topk_weight(sel_v + wave * 64, k, lane);
         a.topk_idx[static_cast<size_t>(t) * k + lane] = e;
-        a.topk_w[static_cast<size_t>(t) * k + lane] = topk_weight(sel_v + wave * 64, k, lane);
-        if (a.list != nullptr) {
-          const int at = atomicAdd(a.counts + e, 1);
-          a.list[static_cast<size_t>(e) * T + at] = t * a.S_pairs + lane;
+        a.topk_w[static_cast<size_t>(t) * k + lane] = wgt;
+        if (a.masks != nullptr) {
+          // token t joins expert e's set (no value returned, nothing waits)
+          __hip_atomic_fetch_or(a.masks + static_cast<size_t>(e) * a.W + (t >> 6), 1ull << (t & 63),
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          a.pinfo[static_cast<size_t>(t) * E + e] = make_int2(__float_as_int(wgt), lane);
         }
       }
     }
   }
-
+  // the new residual (all staging threads), after the logits
+  if constexpr (kDefer && COMBINE) {
+    const int h4 = H / 4;
+#pragma unroll
+    for (int it = 0; it < kStageIt; ++it) {
+      const int f = threadIdx.x + it * kRouteThreads;
+      if (f < nt * h4) {
+        const int tt = f / h4;
+        const int i = (f - tt * h4) * 4;
+        *reinterpret_cast<float4*>(a.h_out + static_cast<size_t>(t0 + tt) * H + i) = hkeep[it];
+      }
+    }
+  }
 }
 
-template <typename WT, bool COMBINE, int TPB, bool PRELOAD>
+template <typename WT, bool COMBINE, int TPB, bool PRELOAD, int SL>
 void launch_route_t(int nch, dim3 grid, size_t lds, hipStream_t s, const RouteArgs& a) {
 #define MOEV_ROUTE_CASE(N)                                                               \
   case N:                                                                                \
-    route_kernel<WT, N, COMBINE, TPB, PRELOAD><<<grid, kRouteThreads, lds, s>>>(a);       \
+    route_kernel<WT, N, COMBINE, TPB, PRELOAD, SL><<<grid, kRouteThreads, lds, s>>>(a);   \
     break;
   switch (nch) {
     MOEV_ROUTE_CASE(1) MOEV_ROUTE_CASE(2) MOEV_ROUTE_CASE(3) MOEV_ROUTE_CASE(4)
@@ -296,10 +357,13 @@ void launch_route_t(int nch, dim3 grid, size_t lds, hipStream_t s, const RouteAr
 template <typename WT, int TPB, bool PRELOAD>
 void launch_route_tpb(const RouteArgs& a, hipStream_t s) {
   const dim3 grid((a.T + TPB - 1) / TPB);
-  const size_t lds = (static_cast<size_t>(TPB) * a.H + 3 * TPB * 64) * sizeof(float);
+  // xs, lg, sel_v, sel_i, then the rank parts [TPB][16 / TPB][64]
+  const size_t lds = (static_cast<size_t>(TPB) * a.H + 3 * TPB * 64 + 64 * kRouteWaves) * sizeof(float);
   const int nch = (a.H + 255) / 256;
-  if (a.y != nullptr) launch_route_t<WT, true, TPB, PRELOAD>(nch, grid, lds, s, a);
-  else launch_route_t<WT, false, TPB, PRELOAD>(nch, grid, lds, s, a);
+  // the slot loads of the fused combine are unrolled to a compile-time bound
+  if (a.y == nullptr) launch_route_t<WT, false, TPB, PRELOAD, 8>(nch, grid, lds, s, a);
+  else if (a.S <= 8) launch_route_t<WT, true, TPB, PRELOAD, 8>(nch, grid, lds, s, a);
+  else launch_route_t<WT, true, TPB, PRELOAD, kMaxSlots>(nch, grid, lds, s, a);
 }
 
 // Tokens per block: 1 for decode-sized batches (more blocks in flight, router
@@ -325,13 +389,13 @@ moev_status check_hidden(int H) {
 
 // Launchers shared with the whole-step driver (no validation).
 void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, int dt, float* h,
-                  hipStream_t s, const ExpertLists* lists) {
-  ExpertLists el{};
-  if (lists != nullptr) el = *lists;
+                  hipStream_t s, const TokenSets* sets) {
+  TokenSets ts{};
+  if (sets != nullptr) ts = *sets;
   if (dt == MOEV_BF16)
-    embed_kernel<u16><<<T, 256, 0, s>>>(tokens, static_cast<const u16*>(emb), T, H, V, h, el);
+    embed_kernel<u16><<<T, 256, 0, s>>>(tokens, static_cast<const u16*>(emb), T, H, V, h, ts);
   else
-    embed_kernel<float><<<T, 256, 0, s>>>(tokens, static_cast<const float*>(emb), T, H, V, h, el);
+    embed_kernel<float><<<T, 256, 0, s>>>(tokens, static_cast<const float*>(emb), T, H, V, h, ts);
 }
 
 void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,
@@ -358,12 +422,11 @@ void launch_route(const float* h, const void* norm_w, float eps, const void* w_r
 void launch_route_fused(const float* h, const float* y_prev, int S_prev, float* h_out,
                         const void* norm_w, float eps, const void* w_router, const float* bias,
                         int T, int H, int E, int k, int dt, void* x_out, int32_t* topk_idx,
-                        float* topk_w, hipStream_t s, int32_t* counts, int32_t* list,
-                        int S_pairs) {
+                        float* topk_w, hipStream_t s, uint64_t* masks, int2* pinfo) {
   RouteArgs a{};
-  a.counts = counts;
-  a.list = list;
-  a.S_pairs = S_pairs;
+  a.masks = masks;
+  a.pinfo = pinfo;
+  a.W = set_words(T);
   a.h = h;
   a.y = y_prev;
   a.S = S_prev;

@@ -12,11 +12,13 @@ namespace moev {
 
 template <typename WT> struct Vec4;
 template <> struct Vec4<u16> {
-  __device__ static float4 load(const u16* p) {
-    uint2 u = *reinterpret_cast<const uint2*>(p);
+  using Raw = uint2;  // four bf16 as loaded
+  __device__ static Raw load_raw(const u16* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ static float4 from_raw(uint2 u) {
     return make_float4(bf16_to_f32(u.x & 0xFFFF), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFF),
                        bf16_to_f32(u.y >> 16));
   }
+  __device__ static float4 load(const u16* p) { return from_raw(load_raw(p)); }
   __device__ static uint2 pack(float4 v) {
     uint2 u;
     u.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
@@ -26,6 +28,9 @@ template <> struct Vec4<u16> {
   __device__ static void store(u16* p, float4 v) { *reinterpret_cast<uint2*>(p) = pack(v); }
 };
 template <> struct Vec4<float> {
+  using Raw = float4;
+  __device__ static Raw load_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static float4 from_raw(float4 v) { return v; }
   __device__ static float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
   __device__ static void store(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 };
@@ -46,14 +51,19 @@ __device__ __forceinline__ float dot_step(float acc, float4 x, float4 w) {
   return fmaf(x.w, w.w, acc);
 }
 
-// h + the S expert slots ys[0], ys[h4], ... added left to right (the order
-// the combine kernel uses); every slot load is issued before the sum
+// The S expert slots ys[0], ys[h4], ... of one 4-element column (S <=
+// kMaxSlots), every load issued before any is used and none under a branch
+// (entries past S repeat slot S - 1 and are not summed).
 template <int kMaxSlots>
-__device__ __forceinline__ float4 add_slots(float4 h, const float4* ys, int S, size_t h4) {
-  float4 sv[kMaxSlots];
+__device__ __forceinline__ void load_slots(float4 (&sv)[kMaxSlots], const float4* ys, int S, size_t h4) {
 #pragma unroll
-  for (int sl = 0; sl < kMaxSlots; ++sl)
-    if (sl < S) sv[sl] = ys[static_cast<size_t>(sl) * h4];
+  for (int sl = 0; sl < kMaxSlots; ++sl) sv[sl] = ys[static_cast<size_t>(min(sl, S - 1)) * h4];
+}
+
+// h + the S loaded slots added left to right (the order the combine kernel
+// uses)
+template <int kMaxSlots>
+__device__ __forceinline__ float4 sum_slots(float4 h, const float4 (&sv)[kMaxSlots], int S) {
   float4 acc = sv[0];
 #pragma unroll
   for (int sl = 1; sl < kMaxSlots; ++sl)
@@ -72,18 +82,22 @@ __device__ __forceinline__ float rms_scale(float ss_lanes, int H, float eps) {
   return 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
 }
 
-// Rank of this lane's logit v among the 64 entries of an LDS row (entries
-// past the expert count hold -inf): the number of entries that beat it
-// (larger, or equal with a lower index).
-__device__ __forceinline__ int logit_rank(const float* row, float v, int lane) {
+// Part of the rank of this lane's logit v among the 64 entries of an LDS row
+// (entries past the expert count hold -inf): the number of entries j in
+// [j0, j0 + N) that beat it (larger, or equal with a lower index).  The rank
+// is the sum of the parts over a partition of the 64 entries.
+template <int N>
+__device__ __forceinline__ int logit_rank_part(const float* row, int j0, float v, int lane) {
+  static_assert(N % 4 == 0, "whole float4 reads");
   int rank = 0;
 #pragma unroll
-  for (int j4 = 0; j4 < 16; ++j4) {
-    const float4 r = reinterpret_cast<const float4*>(row)[j4];
-    rank += better(r.x, 4 * j4 + 0, v, lane) ? 1 : 0;
-    rank += better(r.y, 4 * j4 + 1, v, lane) ? 1 : 0;
-    rank += better(r.z, 4 * j4 + 2, v, lane) ? 1 : 0;
-    rank += better(r.w, 4 * j4 + 3, v, lane) ? 1 : 0;
+  for (int j4 = 0; j4 < N / 4; ++j4) {
+    const int j = j0 + 4 * j4;
+    const float4 r = *reinterpret_cast<const float4*>(row + j);
+    rank += better(r.x, j + 0, v, lane) ? 1 : 0;
+    rank += better(r.y, j + 1, v, lane) ? 1 : 0;
+    rank += better(r.z, j + 2, v, lane) ? 1 : 0;
+    rank += better(r.w, j + 3, v, lane) ? 1 : 0;
   }
   return rank;
 }

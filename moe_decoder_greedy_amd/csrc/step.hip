@@ -16,12 +16,12 @@ namespace moev {
 namespace {
 
 struct StepLayout {
-  size_t h, x, idx, w, offsets, sorted, counts, y, ffn, head, total;
+  size_t h, x, idx, w, offsets, sorted, masks, pinfo, y, ffn, head, total;
 };
 
-// Decode-sized steps route through expert lists filled by the router (no
+// Decode-sized steps route through token sets filled by the router (no
 // permute launch); larger ones through the sorted pair order.
-bool use_lists(int T) { return T <= kListMaxTokens; }
+bool use_sets(int T) { return T <= kSetMaxTokens; }
 
 size_t esz(int dt) { return dt == MOEV_BF16 ? 2 : 4; }
 
@@ -40,15 +40,17 @@ StepLayout layout(const moev_model& m, int T) {
   L.x = take(static_cast<size_t>(T) * m.hidden * esz(m.dtype));
   L.idx = take(static_cast<size_t>(T) * m.top_k * 4);
   L.w = take(static_cast<size_t>(T) * m.top_k * 4);
-  const bool lists = use_lists(T);
+  const bool sets = use_sets(T);
   L.offsets = take(static_cast<size_t>(G + 1) * 4);
-  // sorted pair order [P], or the expert lists [G][T]
-  L.sorted = take((lists ? static_cast<size_t>(G) * T : P) * 4);
-  L.counts = take(lists ? static_cast<size_t>(m.n_layers > 0 ? m.n_layers : 1) * G * 4 : 0);
+  // sorted pair order [P] (without token sets)
+  L.sorted = take(sets ? 0 : P * 4);
+  // token sets: one mask set [E][W] per layer, pair entries [T][E]
+  L.masks = take(sets ? static_cast<size_t>(m.n_layers > 0 ? m.n_layers : 1) * m.n_routed * set_words(T) * 8 : 0);
+  L.pinfo = take(sets ? static_cast<size_t>(T) * m.n_routed * 8 : 0);
   L.y = take(P * m.hidden * 4);
-  // gate/up activations: [P, I] in sorted order, or [G*T, I] by expert list
-  L.ffn = take(lists ? static_cast<size_t>(G) * T * m.inter * esz(m.dtype)
-                     : grouped_ffn_ws_bytes(T, m.inter, m.top_k, m.n_shared, m.dtype));
+  // gate/up activations: [P, I] in sorted order, or [G*T, I] by token set
+  L.ffn = take(sets ? static_cast<size_t>(G) * T * m.inter * esz(m.dtype)
+                    : grouped_ffn_ws_bytes(T, m.inter, m.top_k, m.n_shared, m.dtype));
   L.head = take(lmhead_ws_bytes(T, m.hidden, m.vocab, m.dtype));
   L.total = o;
   return L;
@@ -137,8 +139,6 @@ struct AttnHook {
   const moev_attn* a;
   int B, rows;
   const int32_t* pos;
-  int32_t* list;   // [T] = 0 .. T-1: every row in the one group of the dense GEMMs
-  int32_t* count;  // [1] = T
   float* qkv;      // [T, 3H]
   float* q;        // [T, H]
   float* ao;       // [T, H] the attention output's W_o projection, added to h by the router
@@ -146,14 +146,6 @@ struct AttnHook {
 };
 
 constexpr int kAttnRowThreads = 256;
-
-// list[t] = t, count[0] = T: the dense projections run on the expert-list
-// GEMM as one group holding every row.
-__global__ void dense_list_kernel(int32_t* list, int32_t* count, int T) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < T) list[t] = t;
-  if (t == 0) count[0] = T;
-}
 
 // Row t = b*rows + i of [q | k | v]: q to its own fp32 buffer, k and v rounded
 // to the cache type at position pos[b] + i of sequence b's head-major caches
@@ -193,10 +185,10 @@ void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h,
   const moev_attn_layer& al = at.a->layers[l];
   const int H = m->hidden, dt = m->dtype, T = at.B * at.rows;
   launch_norm_cast(h, y_prev, S, nullptr, m->eps, T, H, dt, x, h, s);
-  // dense projections: every 32-token pass of a row tile in its own workgroup
+  // dense projections (one group holding every row): every 32-token pass of
+  // a row tile in its own workgroup
   const int passes = (T + 31) / 32;
-  launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_qkv, T, 3 * H, H, 0, 0, 1, dt, at.qkv, s, true,
-                        passes);
+  launch_ffn_down_sets(x, nullptr, nullptr, al.w_qkv, T, 3 * H, H, 0, 0, 1, dt, at.qkv, s, true, passes);
   const int D = H / at.a->n_heads;
   if (dt == MOEV_BF16)
     kv_scatter_kernel<u16><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, D, at.q,
@@ -209,7 +201,7 @@ void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h,
   // the attention output goes straight into x in the operand type
   launch_attn_decode(at.q, al.k_cache, al.v_cache, at.pos, at.B, at.rows, at.a->max_len, H,
                      at.a->n_heads, dt, x, true, at.part, s);
-  launch_ffn_down_lists(x, at.list, at.count, nullptr, al.w_o, T, H, H, 0, 0, 1, dt, at.ao, s, true, passes);
+  launch_ffn_down_sets(x, nullptr, nullptr, al.w_o, T, H, H, 0, 0, 1, dt, at.ao, s, true, passes);
 }
 
 // Embedding and the decoder layers for T rows.  On return h holds the residual
@@ -224,7 +216,8 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
   float* w = reinterpret_cast<float*>(base + L.w);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
   int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
-  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  uint64_t* masks = reinterpret_cast<uint64_t*>(base + L.masks);
+  int2* pinfo = reinterpret_cast<int2*>(base + L.pinfo);
   float* y = reinterpret_cast<float*>(base + L.y);
   void* ffn_ws = base + L.ffn;
   const int H = m->hidden, E = m->n_routed, k = m->top_k, ns = m->n_shared, I = m->inter;
@@ -237,15 +230,15 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
   };
 
   // Launches per layer: router (with the previous layer's combine folded in),
-  // permute (only without expert lists), gate/up, down.  The last layer's
-  // combine happens inside the head's norm kernel.  With expert lists the
-  // embedding kernel resets one count set per layer and the router appends
-  // each pair to its expert's list.
+  // permute (only without token sets), gate/up, down.  The last layer's
+  // combine happens inside the head's norm kernel.  With token sets the
+  // embedding kernel clears one mask set per layer and the router adds each
+  // pair to its expert's set.
   const int S = k + ns;
-  const int G = E + ns;
-  const bool lists = use_lists(T);
-  ExpertLists el{counts, sorted, m->n_layers, E, G, k, S};
-  launch_embed(tokens, m->emb, T, H, m->vocab, dt, h, s, lists && m->n_layers > 0 ? &el : nullptr);
+  const bool sets = use_sets(T);
+  const int W = set_words(T);
+  TokenSets ts{masks, pinfo, m->n_layers, E, W};
+  launch_embed(tokens, m->emb, T, H, m->vocab, dt, h, s, sets && m->n_layers > 0 ? &ts : nullptr);
   for (int l = 0; l < m->n_layers; ++l) {
     const moev_layer_weights& lw = m->layers[l];
     const float* y_prev = l > 0 ? y : nullptr;
@@ -257,23 +250,23 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
       y_prev = at->ao;
       s_prev = 1;
     }
-    int32_t* cnt = counts + static_cast<size_t>(l) * G;
+    uint64_t* mk = masks + static_cast<size_t>(l) * E * W;
     mark(MOEV_STAGE_ROUTE, l, false);
     launch_route_fused(h, y_prev, s_prev, h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, dt, x,
-                       idx, w, s, lists ? cnt : nullptr, lists ? sorted : nullptr, S);
+                       idx, w, s, sets ? mk : nullptr, sets ? pinfo : nullptr);
     mark(MOEV_STAGE_ROUTE, l, true);
     mark(MOEV_STAGE_PERMUTE, l, false);
-    if (!lists) launch_permute(idx, T, k, E, ns, offsets, sorted, s);
+    if (!sets) launch_permute(idx, T, k, E, ns, offsets, sorted, s);
     mark(MOEV_STAGE_PERMUTE, l, true);
     mark(MOEV_STAGE_GATE_UP, l, false);
-    if (lists)
-      launch_ffn_gate_up_lists(x, sorted, cnt, lw.w_gate, lw.w_up, T, H, I, E, k, ns, dt, ffn_ws, s);
+    if (sets)
+      launch_ffn_gate_up_sets(x, mk, lw.w_gate, lw.w_up, T, H, I, E, k, ns, dt, ffn_ws, s);
     else
       launch_ffn_gate_up(x, sorted, offsets, lw.w_gate, lw.w_up, T, H, I, E, k, ns, dt, ffn_ws, s);
     mark(MOEV_STAGE_GATE_UP, l, true);
     mark(MOEV_STAGE_DOWN, l, false);
-    if (lists)
-      launch_ffn_down_lists(ffn_ws, sorted, cnt, w, lw.w_down, T, H, I, E, k, ns, dt, y, s);
+    if (sets)
+      launch_ffn_down_sets(ffn_ws, mk, pinfo, lw.w_down, T, H, I, E, k, ns, dt, y, s);
     else
       launch_ffn_down(ffn_ws, sorted, offsets, w, lw.w_down, T, H, I, E, k, ns, dt, y, s);
     mark(MOEV_STAGE_DOWN, l, true);
@@ -483,7 +476,7 @@ namespace {
 // Attention step workspace: the verify step's, then the dense-GEMM row list
 // and the attention sublayer's buffers.
 struct AttnLayout {
-  size_t list, count, qkv, q, ao, part, total;
+  size_t qkv, q, ao, part, total;
 };
 
 AttnLayout attn_layout(const moev_model& m, const moev_attn& a, int B, int K) {
@@ -496,8 +489,6 @@ AttnLayout attn_layout(const moev_model& m, const moev_attn& a, int B, int K) {
     o += align_up(bytes, 256);
     return at;
   };
-  A.list = take(static_cast<size_t>(T) * 4);
-  A.count = take(4);
   A.qkv = take(3 * rowf);
   A.q = take(rowf);
   A.ao = take(rowf);
@@ -506,7 +497,7 @@ AttnLayout attn_layout(const moev_model& m, const moev_attn& a, int B, int K) {
   return A;
 }
 
-// rows of one pass with attention (the dense projections' single list)
+// rows of one pass with attention
 constexpr int kAttnMaxRows = 512;
 
 moev_status validate_attn(const moev_model* m, const moev_attn* a, int B, int K) {
@@ -563,10 +554,8 @@ extern "C" moev_status moev_verify_step_attn(const moev_model* m, const moev_att
   const hipStream_t s = as_stream(stream);
   const int T = B * (K + 1);
   const AttnHook at{a, B, K + 1, pos,
-                    reinterpret_cast<int32_t*>(base + A.list), reinterpret_cast<int32_t*>(base + A.count),
                     reinterpret_cast<float*>(base + A.qkv), reinterpret_cast<float*>(base + A.q),
                     reinterpret_cast<float*>(base + A.ao), reinterpret_cast<float*>(base + A.part)};
-  dense_list_kernel<<<(T + 255) / 256, 256, 0, s>>>(at.list, at.count, T);
   if (moev_status st = run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last, ws,
                                 ws_bytes, nullptr, stream, nullptr, &at))
     return st;
