@@ -135,6 +135,10 @@ WORKLOADS: Dict[str, Workload] = {
 for _k in (0, 1, 2):
     _n = f"verify_step_b32k{_k}"
     WORKLOADS[_n] = Workload(_n, DECODER, batch=32, drafts=_k, accept=PAGE_ACCEPT[:_k], steps=64)
+# Larger batches of the same step (uniform routing): 64 and 128 sequences x (1+3).
+for _b in (64, 128):
+    _n = f"verify_step_b{_b}k3"
+    WORKLOADS[_n] = Workload(_n, DECODER, batch=_b, drafts=3, accept=PAGE_ACCEPT, steps=16)
 for _b in (1, 8, 32, 128):
     for _k, _acc in ((3, PAGE_ACCEPT), (1, PAGE_ACCEPT[:1])):
         _n = f"zipf_verify_b{_b}k{_k}"
