@@ -1083,7 +1083,9 @@ static_assert(tile_cols<kHead>() == 16 * kRtHead * kWavesHead, "head partial blo
 
 template <typename WT>
 void launch_tile_head(const GemmArgs& args, int n_ctiles, hipStream_t s) {
-  const int BT = (args.T >= 512 && (!TileCfg<WT, 256>::kXPair || args.K % 64 == 0)) ? 256 : 128;
+  // 256-token tiles (one workgroup per CU) above 128 tokens: each column tile's
+  // weights are then read once up to 256 tokens
+  const int BT = (args.T > 128 && (!TileCfg<WT, 256>::kXPair || args.K % 64 == 0)) ? 256 : 128;
   long long n = std::min<long long>(static_cast<long long>(n_ctiles) * ((args.T + BT - 1) / BT),
                                     static_cast<long long>(cu_count()) * (BT == 256 ? TileCfg<WT, 256>::kPerCu
                                                                                     : TileCfg<WT, 128>::kPerCu));

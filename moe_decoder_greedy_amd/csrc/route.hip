@@ -7,7 +7,7 @@
 // softmax renormalised over the selected experts, i.e. exp(l_r - l_max) over
 // the sum of the k chosen exp(l_j - l_max).
 //
-// Layout of one block (1024 threads = 16 wavefronts, TPB = 1, 4 or 8
+// Layout of one block (1024 threads = 16 wavefronts, TPB = 1, 2 or 8
 // tokens: more blocks in flight for small batches, more tokens per fetch of
 // the router matrix for large ones):
 //   phase 0  the block's residual rows (with the previous layer's expert
@@ -367,13 +367,13 @@ void launch_route_tpb(const RouteArgs& a, hipStream_t s) {
 }
 
 // Tokens per block: 1 for decode-sized batches (more blocks in flight, router
-// rows preloaded), 4 for mid-sized ones, and 8 once there are enough tokens
-// to fill the GPU with two blocks per CU (router rows fetched per chunk; the
-// LDS copy of 8 rows fits twice).
+// rows preloaded), 2 for mid-sized ones (256 blocks at 512 tokens), and 8
+// once there are enough tokens to fill the GPU with two blocks per CU (router
+// rows fetched per chunk; the LDS copy of 8 rows fits twice).
 template <typename WT>
 void launch_route_dispatch(const RouteArgs& a, hipStream_t s) {
   if (a.T >= 2048 && a.H <= 2048) launch_route_tpb<WT, 8, false>(a, s);
-  else if (a.T > 256) launch_route_tpb<WT, 4, true>(a, s);
+  else if (a.T > 256) launch_route_tpb<WT, 2, true>(a, s);
   else launch_route_tpb<WT, 1, true>(a, s);
 }
 
