@@ -141,6 +141,22 @@ __device__ __forceinline__ int set_token(const GemmArgs& a, const TokenSel& sel,
   return sel.masked ? min(nth_set_bit(sel.lo, sel.hi, m), a.T - 1) : m;
 }
 
+// Four gain elements as loaded (bf16 pairs or fp32), converted when used.
+template <typename WT> struct GainRaw;
+template <> struct GainRaw<u16> {
+  using T = uint2;
+  __device__ static uint2 load(const u16* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ static float4 to_f4(uint2 u) {
+    return make_float4(bf16_to_f32(u.x & 0xFFFF), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFF),
+                       bf16_to_f32(u.y >> 16));
+  }
+};
+template <> struct GainRaw<float> {
+  using T = float4;
+  __device__ static float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static float4 to_f4(float4 v) { return v; }
+};
+
 // Row of the operand matrix that token row `row` of this pass reads.
 template <int MODE>
 __device__ __forceinline__ long long operand_row(const GemmArgs& a, const TokenSel& sel, int off, int m0,
@@ -1127,36 +1143,47 @@ __global__ __launch_bounds__(256) void pack_kernel(const WT* __restrict__ src, W
   }
 }
 
-// Final RMSNorm of the head input, rounded to the operand type: one block of
-// 256 threads per 4 tokens.  With y (the last layer's expert slots) the
-// residual add happens first, in the same slot order as the combine kernel,
-// every slot load of a thread issued before the sum.
+// Final RMSNorm of the head input, rounded to the operand type.  With y (the
+// last layer's expert slots) the residual add happens first, in the same slot
+// order as the combine kernel.  TPB = 1 (decode sizes): 512 threads per
+// token, every load issued before any is used and none under a per-slot
+// branch (two staging passes cover H <= 4096; slot loads unrolled to SL >=
+// S, entries past S repeat slot S - 1 and are not summed), and the RMSNorm
+// gain requested first, kept raw until the scale is known.  TPB = 4: 256
+// threads stage four rows pass by pass.
 constexpr int kNormMaxSlots = 16;
+constexpr int kNormMaxChunks = 12;  // 256-wide chunks of a row, H <= 3072
 
-template <typename WT, int TPB>
-__global__ __launch_bounds__(256) void norm_cast_kernel(const float* __restrict__ h,
+template <int TPB> constexpr int norm_threads() { return TPB == 1 ? 512 : 256; }
+
+template <typename WT, int TPB, int SL>
+__global__ __launch_bounds__(512) void norm_cast_kernel(const float* __restrict__ h,
                                                         const float* __restrict__ y, int S,
                                                         const WT* __restrict__ gamma, float eps,
                                                         int T, int H, WT* __restrict__ xo,
                                                         float* __restrict__ h_out) {
   extern __shared__ float hs[];   // [TPB][H]
+  constexpr int kThreads = norm_threads<TPB>();
   const int t0 = blockIdx.x * TPB;
   const int nt = min(TPB, T - t0);
   const int h4 = H / 4;
-  for (int f = threadIdx.x; f < nt * h4; f += 256) {
-    const int tt = f / h4;
-    const int i = (f - tt * h4) * 4;
-    const long long t = t0 + tt;
-    float4 v = h != nullptr ? *reinterpret_cast<const float4*>(h + t * H + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-    if (y != nullptr) {
-      const float4* ys = reinterpret_cast<const float4*>(y + t * S * H + i);
-      float4 sv[kNormMaxSlots];
+  const int nch = (H + 255) / 256;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const bool norm_wave = wave < nt;
+  // gain of this wave's row: lane covers elements c*256 + lane*4 .. +3
+  typename GainRaw<WT>::T graw[kNormMaxChunks];
+  if (norm_wave && gamma != nullptr) {
 #pragma unroll
-      for (int sl = 0; sl < kNormMaxSlots; ++sl)
-        if (sl < S) sv[sl] = ys[static_cast<long long>(sl) * h4];
+    for (int c = 0; c < kNormMaxChunks; ++c)
+      if (c < nch) graw[c] = GainRaw<WT>::load(gamma + min(c * 256 + lane * 4, H - 4));
+  }
+  // residual (h, optional) plus the slots of row t at column i; returns it
+  auto stage = [&](float4 v, const float4 (&sv)[SL], long long t, int tt, int i, bool store_h) {
+    if (y != nullptr) {
       float4 acc = sv[0];
 #pragma unroll
-      for (int sl = 1; sl < kNormMaxSlots; ++sl)
+      for (int sl = 1; sl < SL; ++sl)
         if (sl < S) {
           acc.x += sv[sl].x;
           acc.y += sv[sl].y;
@@ -1165,13 +1192,50 @@ __global__ __launch_bounds__(256) void norm_cast_kernel(const float* __restrict_
         }
       v = h != nullptr ? make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w) : acc;
     }
-    if (h_out != nullptr) *reinterpret_cast<float4*>(h_out + t * H + i) = v;
+    if (store_h && h_out != nullptr) *reinterpret_cast<float4*>(h_out + t * H + i) = v;
     *reinterpret_cast<float4*>(hs + tt * H + i) = v;
+    return v;
+  };
+  auto load = [&](float4& v, float4 (&sv)[SL], long long t, int i) {
+    v = h != nullptr ? *reinterpret_cast<const float4*>(h + t * H + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (y != nullptr) {
+      const float4* ys = reinterpret_cast<const float4*>(y + t * S * H + i);
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) sv[sl] = ys[static_cast<long long>(min(sl, S - 1)) * h4];
+    }
+  };
+  // TPB = 1: the new residual is stored after the barrier (and, by the norm
+  // wave, after its output), so no wait for a load is also a wait for it
+  const int f0 = threadIdx.x, f1 = threadIdx.x + kThreads;
+  float4 hk0, hk1;
+  auto store_residual = [&]() {
+    if constexpr (TPB == 1) {
+      if (h_out != nullptr) {
+        if (f0 < h4) *reinterpret_cast<float4*>(h_out + static_cast<long long>(t0) * H + f0 * 4) = hk0;
+        if (f1 < h4) *reinterpret_cast<float4*>(h_out + static_cast<long long>(t0) * H + f1 * 4) = hk1;
+      }
+    }
+  };
+  if constexpr (TPB == 1) {
+    float4 v0, v1, s0[SL], s1[SL];
+    if (f0 < h4) load(v0, s0, t0, f0 * 4);
+    if (f1 < h4) load(v1, s1, t0, f1 * 4);
+    if (f0 < h4) hk0 = stage(v0, s0, t0, 0, f0 * 4, false);
+    if (f1 < h4) hk1 = stage(v1, s1, t0, 0, f1 * 4, false);
+  } else {
+    for (int f = threadIdx.x; f < nt * h4; f += kThreads) {
+      const int tt = f / h4;
+      const int i = (f - tt * h4) * 4;
+      float4 v, sv[SL];
+      load(v, sv, t0 + tt, i);
+      stage(v, sv, t0 + tt, tt, i, true);
+    }
   }
   __syncthreads();
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  if (wave >= nt) return;
+  if (!norm_wave) {
+    store_residual();
+    return;
+  }
   const float* hr = hs + wave * H;
   float ss = 0.f;
   for (int i = lane * 4; i < H; i += 256) {
@@ -1180,15 +1244,21 @@ __global__ __launch_bounds__(256) void norm_cast_kernel(const float* __restrict_
   }
   ss = lane63(wave_sum_lane63(ss));
   const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
-  for (int i = lane * 4; i < H; i += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(hr + i);
-    f32x4 o;
-    o[0] = v.x * r * (gamma ? to_f32<WT>(gamma[i + 0]) : 1.f);
-    o[1] = v.y * r * (gamma ? to_f32<WT>(gamma[i + 1]) : 1.f);
-    o[2] = v.z * r * (gamma ? to_f32<WT>(gamma[i + 2]) : 1.f);
-    o[3] = v.w * r * (gamma ? to_f32<WT>(gamma[i + 3]) : 1.f);
-    store4<WT>(xo + static_cast<long long>(t0 + wave) * H + i, o);
+#pragma unroll
+  for (int c = 0; c < kNormMaxChunks; ++c) {
+    const int i = c * 256 + lane * 4;
+    if (c < nch && i < H) {
+      const float4 v = *reinterpret_cast<const float4*>(hr + i);
+      const float4 g = gamma != nullptr ? GainRaw<WT>::to_f4(graw[c]) : make_float4(1.f, 1.f, 1.f, 1.f);
+      f32x4 o;
+      o[0] = v.x * r * g.x;
+      o[1] = v.y * r * g.y;
+      o[2] = v.z * r * g.z;
+      o[3] = v.w * r * g.w;
+      store4<WT>(xo + static_cast<long long>(t0 + wave) * H + i, o);
+    }
   }
+  store_residual();
 }
 
 // Second pass of the blocked arg max: one wavefront per token.
@@ -1449,20 +1519,23 @@ void launch_norm_cast(const float* h, const float* y, int S, const void* gamma, 
   const int tpb = T <= 512 ? 1 : 4;
   const int nb = (T + tpb - 1) / tpb;
   const size_t nlds = static_cast<size_t>(tpb) * H * sizeof(float);
+  const bool few = y == nullptr || S <= 8;  // slot loads unrolled to 8 or 16
+  auto go = [&](auto wt, auto tp, auto sl) {
+    using WT = decltype(wt);
+    norm_cast_kernel<WT, decltype(tp)::value, decltype(sl)::value>
+        <<<nb, norm_threads<decltype(tp)::value>(), nlds, s>>>(
+        h, y, S, static_cast<const WT*>(gamma), eps, T, H, static_cast<WT*>(xo), h_out);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I4 = std::integral_constant<int, 4>;
+  using S8 = std::integral_constant<int, 8>;
+  using S16 = std::integral_constant<int, kNormMaxSlots>;
   if (dt == MOEV_BF16) {
-    if (tpb == 1)
-      norm_cast_kernel<u16, 1><<<nb, 256, nlds, s>>>(h, y, S, static_cast<const u16*>(gamma), eps, T, H,
-                                                    static_cast<u16*>(xo), h_out);
-    else
-      norm_cast_kernel<u16, 4><<<nb, 256, nlds, s>>>(h, y, S, static_cast<const u16*>(gamma), eps, T, H,
-                                                    static_cast<u16*>(xo), h_out);
+    if (tpb == 1) few ? go(u16{}, I1{}, S8{}) : go(u16{}, I1{}, S16{});
+    else few ? go(u16{}, I4{}, S8{}) : go(u16{}, I4{}, S16{});
   } else {
-    if (tpb == 1)
-      norm_cast_kernel<float, 1><<<nb, 256, nlds, s>>>(h, y, S, static_cast<const float*>(gamma), eps, T,
-                                                      H, static_cast<float*>(xo), h_out);
-    else
-      norm_cast_kernel<float, 4><<<nb, 256, nlds, s>>>(h, y, S, static_cast<const float*>(gamma), eps, T,
-                                                      H, static_cast<float*>(xo), h_out);
+    if (tpb == 1) few ? go(float{}, I1{}, S8{}) : go(float{}, I1{}, S16{});
+    else few ? go(float{}, I4{}, S8{}) : go(float{}, I4{}, S16{});
   }
 }
 
