@@ -186,11 +186,19 @@ def cpu_baseline(wl, weights, tokens_np, budget_s, gpu_greedy=None):
     if n_l == shape.n_layers and gpu_greedy is not None:
         rf, hf = rgap < 1e-3, head["gap"] < 1e-2
         flagged = rf | hf
+        # unflagged positions whose router gap in some layer is below 5e-3: a
+        # routing flip there can change every later layer (the drift reading
+        # the GPU tests check layer by layer)
+        drift = ~flagged & (rgap < 5e-3)
+        rest = ~flagged & ~drift
         got = np.asarray(gpu_greedy).reshape(-1)
+        miss = got != head["argmax"]
         check = {"positions": int(T), "router_flagged": int(rf.sum()), "head_flagged": int(hf.sum()),
-                 "flagged": int(flagged.sum()),
-                 "mismatches_flagged": int((got[flagged] != head["argmax"][flagged]).sum()),
-                 "mismatches_unflagged": int((got[~flagged] != head["argmax"][~flagged]).sum()),
+                 "flagged": int(flagged.sum()), "drift_band": int(drift.sum()),
+                 "mismatches_flagged": int(miss[flagged].sum()),
+                 "mismatches_unflagged": int(miss[~flagged].sum()),
+                 "mismatches_drift_band": int(miss[drift].sum()),
+                 "mismatches_outside": int(miss[rest].sum()),
                  "source": "oracle pass of the cpu_baseline leg over the first timed step (bf16 operands)"}
     return base, check
 

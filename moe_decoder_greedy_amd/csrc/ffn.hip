@@ -157,12 +157,15 @@ template <> struct GainRaw<float> {
   __device__ static float4 to_f4(float4 v) { return v; }
 };
 
-// Row of the operand matrix that token row `row` of this pass reads.
-template <int MODE>
+// Row of the operand matrix that token row `row` of this pass reads.  SETS =
+// false (the tile schedule, which never runs on token sets) compiles the
+// sorted-order read only.
+template <int MODE, bool SETS = true>
 __device__ __forceinline__ long long operand_row(const GemmArgs& a, const TokenSel& sel, int off, int m0,
                                                  int row) {
   if (MODE == kGateUp)
-    return a.sets ? set_token(a, sel, m0 + row) : clampi(a.sorted_src[off + m0 + row], 0, a.P - 1) / a.S;
+    return (SETS && a.sets) ? set_token(a, sel, m0 + row)
+                            : clampi(a.sorted_src[off + m0 + row], 0, a.P - 1) / a.S;
   if (MODE == kDown) return off + m0 + row;
   return m0 + row;
 }
@@ -809,13 +812,13 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
         const int r = lane >> 3;
         const int row = min(ii * 8 + r, mp - 1);
         const int c = (lane & 7) ^ r ^ (ii & 1);
-        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, TokenSel{}, off, m0, row) * K + c * 8;
+        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE, false>(a, TokenSel{}, off, m0, row) * K + c * 8;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < kXPtr; ++i) {
         const int row = min((wave * TC::kXPerWave + i) * 16 + r16, mp - 1);
-        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE>(a, TokenSel{}, off, m0, row) * K + q * 8;
+        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE, false>(a, TokenSel{}, off, m0, row) * K + q * 8;
       }
     }
   };
