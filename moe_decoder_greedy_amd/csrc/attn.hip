@@ -17,13 +17,17 @@
 // state unchanged).  Each split writes its unnormalised softmax state
 // (maximum, sum, weighted values) to a workspace; attn_merge_kernel combines
 // the splits.  Splitting shortens each workgroup's chain of dependent chunk
-// loads, which bounds the kernel, and spreads the work over more CUs.  Per chunk: lane l scores position
-// c0 + l against every verify row's query (staged in LDS, rows masked
-// causally), each row's chunk maximum updates that row's running maximum of
-// an online softmax, and the values are accumulated position by position in
-// order, each lane holding D/64 adjacent output columns of every row,
-// so every key and value row is read once per workgroup with coalesced
-// loads.  At the end the waves' partial (maximum, sum, output) triples are
+// loads, which bounds the kernel, and spreads the work over more CUs.  Per
+// chunk: four lanes share a key row, each multiplying its D/4 adjacent
+// columns by every verify row's query (staged in LDS) and the four summing
+// their parts in a fixed order, so a load instruction covers 16 rows in
+// 64-byte pieces (one lane per row would touch 64 lines per instruction, and
+// more lanes per row cost more shuffles than they save); lane l then takes
+// position c0 + l's scores (rows masked causally), each row's chunk maximum
+// updates that row's running maximum of an online softmax, and the values
+// are accumulated position by position in order, each lane holding D/64
+// adjacent output columns of every row, so every key and value row is read
+// once per workgroup.  At the end the waves' partial (maximum, sum, output) triples are
 // merged in wave order through LDS.  All arithmetic is fp32; a row's result
 // depends only on its own query and cache.
 #include "launch.h"
@@ -116,6 +120,10 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
   const WT* vb = vc + blk;
   const int vg = lane / kLpk;           // this lane's position group
   const int vc0 = (lane % kLpk) * kEpl;  // and its columns vc0 .. vc0 + kEpl - 1
+  // key walk: kKL lanes per key row, each with kKC adjacent columns
+  constexpr int kKL = 4, kKC = D / kKL;
+  static_assert(kKC % kEpl == 0, "whole loads per key part");
+  const int kg = lane / kKL, kc0 = (lane % kKL) * kKC;
   float m_run[R], l_run[R], o[R][kEpl];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -127,35 +135,39 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
 
   const int split = blockIdx.z;
   for (int c0 = (split * kAttnWaves + wave) * kWave; c0 < hi; c0 += kAttnSplits * kAttnWaves * kWave) {
+    // scores: kKL lanes per key row, kKC columns each; position jj = it *
+    // (64 / kKL) + lane / kKL of the chunk.  The lanes' parts are summed in a
+    // fixed order (pairs, then the pair sums) and the first lane files them;
+    // positions past hi read the chunk's first row and are masked below
+#pragma unroll
+    for (int it = 0; it < kKL; ++it) {
+      const int jj = it * (kWave / kKL) + kg;
+      const int jr = c0 + jj < hi ? c0 + jj : c0;
+      float kv[kKC];
+#pragma unroll
+      for (int c = 0; c < kKC; c += kEpl) {
+        float t[kEpl];
+        ldn<WT, kEpl>(kb + static_cast<long long>(jr) * D + kc0 + c, t);
+#pragma unroll
+        for (int e = 0; e < kEpl; ++e) kv[c + e] = t[e];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < kKC; ++e) part = fmaf(q_s[r][kc0 + e], kv[e], part);
+        part += dpp_mov<0xb1>(part);  // quad_perm [1,0,3,2]
+        part += dpp_mov<0x4e>(part);  // quad_perm [2,3,0,1]
+        if (lane % kKL == 0) p_s[wave][r][jj] = part;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int j = c0 + lane;
     float s[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) s[r] = 0.f;
-    if (j < hi) {
-      const WT* kr = kb + static_cast<long long>(j) * D;
-#pragma unroll
-      for (int c = 0; c < D; c += 8) {
-        float kv[8];
-        if constexpr (sizeof(WT) == 2) {
-          const uint4 u = *reinterpret_cast<const uint4*>(kr + c);
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kv[2 * e] = bf16_to_f32(w[e] & 0xFFFF);
-            kv[2 * e + 1] = bf16_to_f32(w[e] >> 16);
-          }
-        } else {
-          const float4 a = *reinterpret_cast<const float4*>(kr + c);
-          const float4 bq = *reinterpret_cast<const float4*>(kr + c + 4);
-          kv[0] = a.x; kv[1] = a.y; kv[2] = a.z; kv[3] = a.w;
-          kv[4] = bq.x; kv[5] = bq.y; kv[6] = bq.z; kv[7] = bq.w;
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s[r] = fmaf(q_s[r][c + e], kv[e], s[r]);
-      }
-    }
+    for (int r = 0; r < R; ++r) s[r] = p_s[wave][r][lane];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const bool vis = j < hi && j <= p0 + r && r < rows;
