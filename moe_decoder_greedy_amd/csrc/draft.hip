@@ -10,7 +10,7 @@
 //   z_j = z' + W_down (SiLU(W_gate x) * (W_up x)),  x = RMSNorm(z') * norm_ffn
 //   t_j = arg max W_lm (RMSNorm(z_j) * norm_out)
 //
-// Every contraction runs on the grouped expert GEMMs in expert-list mode: the
+// Every contraction runs on the grouped expert GEMMs in token-set mode: the
 // projection is the down GEMM over 2 groups (the z half and the embedding half
 // of W_p, each holding every row, weight 1), summed in group order; the dense
 // SwiGLU of width n*I is the grouped FFN over its n intermediate slices, each

@@ -1,8 +1,8 @@
 """Verify steps captured as one HIP graph: several consecutive steps per
 graph, replayed several times with eager work and synchronisations between
 the replays; every replay must reproduce the eager outputs bit for bit.
-Covers the expert-list step (decode sizes, router atomics and the embedding
-kernel's count reset inside the graph) and the tiled head."""
+Covers the token-set step (decode sizes, the router's atomic mask updates and
+the embedding kernel's mask reset inside the graph) and the tiled head."""
 import numpy as np
 import pytest
 import torch

@@ -39,7 +39,7 @@ def _run(dm, w, n_seq, seq_len, operands, tol, sample_rows, chain_gap=ROUTE_GAP)
     np.testing.assert_array_equal(nt[~flagged], ref["argmax"][~flagged])
     rows = np.asarray(sample_rows)
     # the same tokens as a decode-sized prefill of one-token sequences (other
-    # schedules: streaming GEMMs, expert lists, one-token router blocks): the
+    # schedules: streaming GEMMs, token sets, one-token router blocks): the
     # final residual must be the same bits
     h_small = torch.empty((len(rows), H), dtype=torch.float32, device="cuda")
     dm.prefill(dev_i32(toks.reshape(-1)[rows].reshape(-1, 1)), h_out=h_small)
@@ -75,7 +75,7 @@ def test_prefill_decoder_pages(model_mod):
 
 
 def test_prefill_small_and_edge(model_mod):
-    """Decode-sized prefill (expert lists), seq_len = 1, and n_seq = 0."""
+    """Decode-sized prefill (token sets), seq_len = 1, and n_seq = 0."""
     w = synth.model_weights(synth.TINY)
     dm = model_mod.DeviceModel(w)
     _run(dm, w, n_seq=5, seq_len=7, operands="exact", tol=1e-4, sample_rows=[0, 6, 34])
