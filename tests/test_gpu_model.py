@@ -278,7 +278,7 @@ def zipf_pair(model_mod):
     return w, model_mod.DeviceModel(w)
 
 
-@pytest.mark.parametrize("B,K", [(1, 3), (8, 3), (128, 3), (1, 1), (32, 1)])
+@pytest.mark.parametrize("B,K", [(1, 3), (8, 3), (32, 3), (128, 3), (1, 1), (32, 1)])
 def test_zipf_step_matches_oracle(zipf_pair, B, K):
     """Skewed routing (per-layer Zipf(1.1) router bias, the load-skew sweep's
     model) through the whole 12-layer step at the sweep's batch sizes: every
@@ -307,23 +307,41 @@ def test_zipf_step_matches_oracle(zipf_pair, B, K):
     np.testing.assert_array_equal(host(out["commit"])[clear], ref["commit"][clear])
 
 
-def test_step_matches_stage_chain(decoder_pair):
-    """The whole-step driver (router fused with the previous combine and the
-    permute, head norm fused with the last combine) gives the same greedy
-    tokens, bit for bit, as chaining the per-stage entry points."""
+def _stage_chain_check(dm, seed, min_group=0):
+    """dm.verify_step's greedy tokens against chaining the per-stage entry
+    points, bit for bit; returns the largest routed group seen."""
     from moe_decoder_greedy_amd import ops
-    w, dm = decoder_pair
     shape = dm.shape
     B, K = 32, 3
-    toks = np.random.default_rng(13).integers(0, shape.vocab, size=(B, K + 1)).astype(np.int32)
+    toks = np.random.default_rng(seed).integers(0, shape.vocab, size=(B, K + 1)).astype(np.int32)
     td = dev_i32(toks)
     fused = host(dm.verify_step(td)["greedy"]).reshape(-1)
     h = ops.moe_embed(td.reshape(-1), dm.emb)
+    biggest = 0
     for L in dm.layers:
         x, idx, wts, _ = ops.moe_route(h, L["norm"], shape.eps, L["w_router"], L["bias"], shape.top_k)
+        biggest = max(biggest, int(np.bincount(host(idx).reshape(-1), minlength=shape.n_routed).max()))
         off, src = ops.moe_permute(idx, shape.n_routed, shape.n_shared)
         y = ops.moe_grouped_ffn(x, src, off, wts, L["w_gate"], L["w_up"], L["w_down"], shape.n_routed,
                                 shape.top_k, shape.n_shared)
         h = ops.moe_combine(y, h)
     am, _, _ = ops.lmhead_argmax(h, dm.norm_f, shape.eps, dm.w_lm, vocab=shape.vocab)
     np.testing.assert_array_equal(host(am), fused)
+    return biggest
+
+
+def test_step_matches_stage_chain(decoder_pair):
+    """The whole-step driver (router fused with the previous combine and the
+    token sets, head norm fused with the last combine) gives the same greedy
+    tokens, bit for bit, as chaining the per-stage entry points (the sorted
+    pair order of moe_permute)."""
+    _stage_chain_check(decoder_pair[1], 13)
+
+
+def test_step_matches_stage_chain_skewed(zipf_pair):
+    """The same with skewed routing (per-layer Zipf(1.1) router bias), where
+    some routed expert holds more than 32 of the 128 tokens: its token set
+    then takes the GEMMs' LDS-staged passes, rows found from the mask."""
+    biggest = _stage_chain_check(zipf_pair[1], 17)
+    report("stage_chain_skewed", biggest_group=biggest)
+    assert biggest > 32
