@@ -83,6 +83,8 @@ struct GemmArgs {
   void* out;                // gate/up: act [P, N] WT; down: y [P, N] fp32; head: pmax
   int32_t* out_idx;         // head: partial arg max [T, blocks]
   float* logits;            // head: optional logits [T, N]
+  QkvScatter scatter;       // down: where a fused Q/K/V projection's rows go
+  bool scattered;           //   (instead of out) when set
 };
 
 // SwiGLU combination silu(g) * u = g / (1 + e^-g) * u from the hardware
@@ -212,9 +214,34 @@ __device__ __forceinline__ void load_meta(const GemmArgs& a, const TokenSel& sel
   }
 }
 
+// Four adjacent output columns col.. of row t of a fused Q/K/V projection
+// (N = 3H): q columns to the fp32 q rows, key and value columns to the
+// caches at the row's position, rounded like every other cache write.  The
+// four columns share one head (D and H are multiples of 4).
+template <typename WT>
+__device__ __forceinline__ void qkv_store(const GemmArgs& a, int t, int col, f32x4 o) {
+  const QkvScatter& sc = a.scatter;
+  const int H = a.N / 3;
+  const int b = t / sc.rows, i = t - b * sc.rows;
+  const int p0 = sc.pos[b];
+  if (p0 < 0 || p0 > sc.max_len - sc.rows) return;
+  if (col < H) {
+    store4<float>(sc.q + static_cast<long long>(t) * H + col, o);
+    return;
+  }
+  const bool key = col < 2 * H;
+  const int c = col - (key ? H : 2 * H);
+  const int sh = __ffs(sc.D) - 1;  // D is a power of two
+  const int hd = c >> sh, d = c & (sc.D - 1);
+  const long long dst = ((static_cast<long long>(b) * (H >> sh) + hd) * sc.max_len + p0 + i) * sc.D + d;
+  store4<WT>(static_cast<WT*>(key ? sc.k_cache : sc.v_cache) + dst, o);
+}
+
 // Epilogue of one pass: lane (r16, q) holds rows rowbase[rt] + 4q + v of
 // token column j*16 + r16.
-template <typename WT, int MODE, int RT, int MT, int NTX, int W>
+// SCATTER: the build may write a fused Q/K/V projection's rows (split-K
+// dense projections only; the expert GEMMs never do).
+template <typename WT, int MODE, int RT, int MT, int NTX, int W, bool SCATTER = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, unsigned char* __restrict__ lds,
                                          const f32x4 (&acc)[RT][NTX], int off, int m0, int mp,
                                          const int (&rowbase)[RT], const PairMeta (&meta)[NTX]) {
@@ -250,7 +277,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, unsigned char* __res
           f32x4 o = acc[rt][j];
 #pragma unroll
           for (int v = 0; v < 4; ++v) o[v] *= wgt;
-          store4<float>(y + static_cast<long long>(p) * a.N + rowbase[rt] + 4 * q, o);
+          if (SCATTER && a.scattered) qkv_store<WT>(a, p, rowbase[rt] + 4 * q, o);
+          else store4<float>(y + static_cast<long long>(p) * a.N + rowbase[rt] + 4 * q, o);
         }
       }
     }
@@ -390,7 +418,7 @@ __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned cha
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[rt][j][v] += o[v];
           }
-      epilogue<WT, MODE, RT, MT, NTX, W>(a, lds, acc, off, m0, mp, rowbase, meta);
+      epilogue<WT, MODE, RT, MT, NTX, W, true>(a, lds, acc, off, m0, mp, rowbase, meta);
     }
     __syncthreads();  // red is free for the next pass
   } else {
@@ -1472,7 +1500,8 @@ void launch_ffn_gate_up_sets(const void* x, const uint64_t* masks, const void* w
 
 void launch_ffn_down_sets(const void* act, const uint64_t* masks, const int2* pinfo,
                           const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
-                          float* y_slots, hipStream_t s, bool split_k, int pass_split) {
+                          float* y_slots, hipStream_t s, bool split_k, int pass_split,
+                          const QkvScatter* scatter) {
   GemmArgs dn = set_args(masks, pinfo, T, H, I, E, k, ns);
   dn.w0 = w_down;
   dn.w_group = static_cast<long long>(H) * I;
@@ -1480,6 +1509,10 @@ void launch_ffn_down_sets(const void* act, const uint64_t* masks, const int2* pi
   dn.K = I;
   dn.x = act;
   dn.out = y_slots;
+  if (scatter != nullptr) {
+    dn.scatter = *scatter;
+    dn.scattered = true;
+  }
   // dense projections of a whole batch (pass_split > 1): two 16-row tiles per
   // workgroup halve the operand rows' L2 re-reads; the K order of every output
   // is unchanged

@@ -75,12 +75,29 @@ void run_draft(const moev_model& m, const moev_draft_weights& d, const float* z_
 void launch_ffn_gate_up_sets(const void* x, const uint64_t* masks, const void* w_gate,
                              const void* w_up, int T, int H, int I, int E, int k, int ns, int dt,
                              void* act, hipStream_t s, bool split_k = false);
+// Destination of a fused Q/K/V projection (one dense group, output width 3H):
+// row t = b*rows + i, columns [0, H) go to q [T, H] (fp32), [H, 2H) and
+// [2H, 3H) to the head-major key and value caches [B, H/D, max_len, D] (D a
+// power of two) at
+// position pos[b] + i, rounded to the cache type.  A sequence whose cache has
+// no room for the pass (pos[b] < 0 or pos[b] + rows > max_len) gets none of
+// its rows written.
+struct QkvScatter {
+  const int32_t* pos;
+  int rows, max_len, D;
+  float* q;
+  void* k_cache;
+  void* v_cache;
+};
 // pass_split (split_k only): the 32-token passes are spread over this many
 // workgroups per row tile (grid z), for dense projections of a whole batch;
 // with pass_split > 1 a workgroup takes two 16-row tiles (H % 32 == 0).
+// scatter (optional, E = 0 with one group): the epilogue writes the rows
+// there instead of y_slots (NULL then).
 void launch_ffn_down_sets(const void* act, const uint64_t* masks, const int2* pinfo,
                           const void* w_down, int T, int H, int I, int E, int k, int ns, int dt,
-                          float* y_slots, hipStream_t s, bool split_k = false, int pass_split = 1);
+                          float* y_slots, hipStream_t s, bool split_k = false, int pass_split = 1,
+                          const QkvScatter* scatter = nullptr);
 void launch_combine(const float* y, const float* h_in, int T, int H, int S, float* h_out,
                     hipStream_t s);
 // out[i] = h[t] + the sum of y's S slots of row t (y may be NULL), t = the

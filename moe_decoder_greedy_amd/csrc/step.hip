@@ -139,38 +139,10 @@ struct AttnHook {
   const moev_attn* a;
   int B, rows;
   const int32_t* pos;
-  float* qkv;      // [T, 3H]
   float* q;        // [T, H]
   float* ao;       // [T, H] the attention output's W_o projection, added to h by the router
   float* part;     // attention's per-split softmax states
 };
-
-constexpr int kAttnRowThreads = 256;
-
-// Row t = b*rows + i of [q | k | v]: q to its own fp32 buffer, k and v rounded
-// to the cache type at position pos[b] + i of sequence b's head-major caches
-// [B, n_heads, max_len, D].  A sequence whose cache has no room for the pass
-// (pos[b] < 0 or pos[b] + rows > max_len) writes nothing: the step commits
-// nothing for it and leaves its position.
-template <typename WT>
-__global__ __launch_bounds__(kAttnRowThreads) void kv_scatter_kernel(
-    const float* __restrict__ qkv, const int32_t* __restrict__ pos, int rows, int max_len, int H, int D,
-    float* __restrict__ q, WT* __restrict__ kc, WT* __restrict__ vc) {
-  const int t = blockIdx.x;
-  const int b = t / rows, i = t - b * rows;
-  const int p0 = pos[b];
-  if (p0 < 0 || p0 > max_len - rows) return;
-  const int p = p0 + i;
-  const float* src = qkv + static_cast<long long>(t) * 3 * H;
-  const int n_heads = H / D;
-  for (int c = threadIdx.x; c < H; c += kAttnRowThreads) {
-    const int hd = c / D, d = c - hd * D;
-    const long long dst = ((static_cast<long long>(b) * n_heads + hd) * max_len + p) * D + d;
-    q[static_cast<long long>(t) * H + c] = src[c];
-    kc[dst] = from_f32<WT>(src[H + c]);
-    vc[dst] = from_f32<WT>(src[2 * H + c]);
-  }
-}
 
 __global__ void pos_advance_kernel(int32_t* pos, const int32_t* commit_len, int B) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -188,16 +160,10 @@ void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h,
   // dense projections (one group holding every row): every 32-token pass of
   // a row tile in its own workgroup
   const int passes = (T + 31) / 32;
-  launch_ffn_down_sets(x, nullptr, nullptr, al.w_qkv, T, 3 * H, H, 0, 0, 1, dt, at.qkv, s, true, passes);
-  const int D = H / at.a->n_heads;
-  if (dt == MOEV_BF16)
-    kv_scatter_kernel<u16><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, D, at.q,
-                                                         static_cast<u16*>(al.k_cache),
-                                                         static_cast<u16*>(al.v_cache));
-  else
-    kv_scatter_kernel<float><<<T, kAttnRowThreads, 0, s>>>(at.qkv, at.pos, at.rows, at.a->max_len, H, D, at.q,
-                                                           static_cast<float*>(al.k_cache),
-                                                           static_cast<float*>(al.v_cache));
+  // the Q/K/V projection's epilogue writes q, and the pass's keys and values
+  // into the caches at pos[b] + i
+  const QkvScatter qkv{at.pos, at.rows, at.a->max_len, H / at.a->n_heads, at.q, al.k_cache, al.v_cache};
+  launch_ffn_down_sets(x, nullptr, nullptr, al.w_qkv, T, 3 * H, H, 0, 0, 1, dt, nullptr, s, true, passes, &qkv);
   // the attention output goes straight into x in the operand type
   launch_attn_decode(at.q, al.k_cache, al.v_cache, at.pos, at.B, at.rows, at.a->max_len, H,
                      at.a->n_heads, dt, x, true, at.part, s);
@@ -476,7 +442,7 @@ namespace {
 // Attention step workspace: the verify step's, then the dense-GEMM row list
 // and the attention sublayer's buffers.
 struct AttnLayout {
-  size_t qkv, q, ao, part, total;
+  size_t q, ao, part, total;
 };
 
 AttnLayout attn_layout(const moev_model& m, const moev_attn& a, int B, int K) {
@@ -489,7 +455,6 @@ AttnLayout attn_layout(const moev_model& m, const moev_attn& a, int B, int K) {
     o += align_up(bytes, 256);
     return at;
   };
-  A.qkv = take(3 * rowf);
   A.q = take(rowf);
   A.ao = take(rowf);
   A.part = take(a.n_heads >= 1 ? attn_ws_bytes(B, K + 1, m.hidden, a.n_heads) : 0);
@@ -553,8 +518,7 @@ extern "C" moev_status moev_verify_step_attn(const moev_model* m, const moev_att
   unsigned char* base = static_cast<unsigned char*>(ws);
   const hipStream_t s = as_stream(stream);
   const int T = B * (K + 1);
-  const AttnHook at{a, B, K + 1, pos,
-                    reinterpret_cast<float*>(base + A.qkv), reinterpret_cast<float*>(base + A.q),
+  const AttnHook at{a, B, K + 1, pos, reinterpret_cast<float*>(base + A.q),
                     reinterpret_cast<float*>(base + A.ao), reinterpret_cast<float*>(base + A.part)};
   if (moev_status st = run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last, ws,
                                 ws_bytes, nullptr, stream, nullptr, &at))
