@@ -931,9 +931,9 @@ def run_layer(args, torch, np):
         ach = gu_bytes / (dur["gate_up"] * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
-    # the schedule moe_ffn_gate_up takes at this size (tiles above 512 tokens,
+    # the schedule moe_ffn_gate_up takes at this size (tiles above 128 tokens,
     # 256-token tiles once routed groups average 384 tokens)
-    if T > 512:
+    if T > 128:
         bt = 256 if T * k >= 384 * E else 128
         kname = f"tile_gemm<bf16, gate/up, {bt}> (moe_ffn_gate_up)"
     else:
