@@ -16,7 +16,8 @@
 // depend on the number of rows in the pass (chunks a row cannot see leave its
 // state unchanged).  Each split writes its unnormalised softmax state
 // (maximum, sum, weighted values) to a workspace; attn_merge_kernel combines
-// the splits.  Splitting shortens each workgroup's chain of dependent chunk
+// the splits (in the verify step the last split of a (sequence, head) to
+// finish does, see attn_decode_kernel's FUSE).  Splitting shortens each workgroup's chain of dependent chunk
 // loads, which bounds the kernel, and spreads the work over more CUs.  Per
 // chunk: four lanes share a key row, each multiplying its D/4 adjacent
 // columns by every verify row's query (staged in LDS) and the four summing
@@ -73,12 +74,50 @@ template <typename WT, int N> __device__ __forceinline__ void ldn(const WT* p, f
 constexpr int kAttnWaves = 4;   // wavefronts per workgroup
 constexpr int kAttnSplits = 3;  // workgroups per (sequence, head)
 
+// Row r, column c of one (sequence, head)'s output: its splits' states
+// (po: [kAttnSplits, rows, D] weighted values, pml: [kAttnSplits, rows, 2]
+// maximum and sum) merged in split order and normalised.  LD reads one
+// state value.  Both merge paths use this one expression.
+template <typename LD>
+__device__ __forceinline__ float merge_splits(const float* po, const float* pml, int rows, int D, int r, int c,
+                                              LD ld) {
+#pragma clang fp contract(off)
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kAttnSplits; ++sp) M = fmaxf(M, ld(pml + (sp * rows + r) * 2));
+  float L = 0.f, O = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < kAttnSplits; ++sp) {
+    const float m = ld(pml + (sp * rows + r) * 2);
+    const float f = m == -INFINITY ? 0.f : expf(m - M);
+    L = fmaf(ld(pml + (sp * rows + r) * 2 + 1), f, L);
+    O = fmaf(ld(po + (static_cast<long long>(sp) * rows + r) * D + c), f, O);
+  }
+  return O / L;
+}
+
+// Device-coherent (agent-scope) loads and stores of split states: they
+// bypass a stale copy in another XCD's L2, so a state written by one
+// workgroup is read by another within one launch without cache maintenance.
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // part: the splits' states, [B, n_heads, kAttnSplits, rows, D] weighted
 // values, then [B, n_heads, kAttnSplits, rows, 2] (maximum, sum)
-template <typename WT, int D, int R>
+// FUSE: each split writes its state with device-coherent stores, waits for
+// them, then counts itself in cnt[b, h] (an agent-scope atomic, no waiting on
+// anyone); the split that counts last merges the three states, read back in
+// split order with device-coherent loads, into out [B*rows, H] (rounded to
+// WT once) and resets the count.  Which split merges does not change a bit.
+template <typename WT, int D, int R, bool FUSE>
 __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
     const float* __restrict__ q, const WT* __restrict__ kc, const WT* __restrict__ vc,
-    const int32_t* __restrict__ pos, int rows, int max_len, int H, float scale, float* __restrict__ part) {
+    const int32_t* __restrict__ pos, int rows, int max_len, int H, float scale, float* __restrict__ part,
+    int* __restrict__ cnt, WT* __restrict__ out) {
   // Every fused multiply-add below is written out and no other is formed, so
   // the instantiations for different row counts round identically (the
   // compiler may otherwise fuse a*b + c*d either way round).
@@ -240,10 +279,38 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
       L = fmaf(l_s[w][r], f, L);
       O = fmaf(o_s[w][r][c], f, O);
     }
-    po[r * D + c] = O;
-    if (c == 0) {
-      pml[2 * r] = M;
-      pml[2 * r + 1] = L;
+    if constexpr (FUSE) {
+      st_agent(po + r * D + c, O);
+      if (c == 0) {
+        st_agent(pml + 2 * r, M);
+        st_agent(pml + 2 * r + 1, L);
+      }
+    } else {
+      po[r * D + c] = O;
+      if (c == 0) {
+        pml[2 * r] = M;
+        pml[2 * r + 1] = L;
+      }
+    }
+  }
+  if constexpr (FUSE) {
+    __shared__ int last;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's state stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(cnt + b * gridDim.y + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             kAttnSplits - 1;
+    __syncthreads();
+    if (last) {
+      const long long slot0 = slot - split;
+      const float* po0 = part + slot0 * rows * D;
+      const float* pml0 = part + static_cast<long long>(gridDim.x) * gridDim.y * kAttnSplits * rows * D + slot0 * rows * 2;
+      for (int i = threadIdx.x; i < rows * D; i += blockDim.x) {
+        const int r = i / D, c = i - r * D;
+        out[(static_cast<long long>(b) * rows + r) * H + h * D + c] =
+            from_f32<WT>(merge_splits(po0, pml0, rows, D, r, c, ld_agent));
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(cnt + b * gridDim.y + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -261,47 +328,39 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   const float* pml = part + static_cast<long long>(gridDim.x) * gridDim.y * kAttnSplits * rows * D + slot0 * rows * 2;
   for (int i = threadIdx.x; i < rows * D; i += 256) {
     const int r = i / D, c = i - r * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int sp = 0; sp < kAttnSplits; ++sp) M = fmaxf(M, pml[(sp * rows + r) * 2]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < kAttnSplits; ++sp) {
-      const float m = pml[(sp * rows + r) * 2];
-      const float f = m == -INFINITY ? 0.f : expf(m - M);
-      L = fmaf(pml[(sp * rows + r) * 2 + 1], f, L);
-      O = fmaf(po[(static_cast<long long>(sp) * rows + r) * D + c], f, O);
-    }
-    out[(static_cast<long long>(b) * rows + r) * H + h * D + c] = from_f32<OT>(O / L);
+    out[(static_cast<long long>(b) * rows + r) * H + h * D + c] =
+        from_f32<OT>(merge_splits(po, pml, rows, D, r, c, [](const float* p) { return *p; }));
   }
 }
 
-template <typename WT, int D>
+template <typename WT, int D, bool FUSE>
 void launch_attn_d(const float* q, const WT* k, const WT* v, const int32_t* pos, int B, int rows, int max_len,
-                   int H, int n_heads, float scale, float* part, hipStream_t s) {
+                   int H, int n_heads, float scale, float* part, int* cnt, WT* out, hipStream_t s) {
   const dim3 grid(B, n_heads, kAttnSplits);
   const dim3 block(kWave * kAttnWaves);
   if (rows <= 1)
-    attn_decode_kernel<WT, D, 1><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part);
+    attn_decode_kernel<WT, D, 1, FUSE><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part, cnt, out);
   else if (rows <= 4)
-    attn_decode_kernel<WT, D, 4><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part);
+    attn_decode_kernel<WT, D, 4, FUSE><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part, cnt, out);
   else if (rows <= 8)
-    attn_decode_kernel<WT, D, 8><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part);
+    attn_decode_kernel<WT, D, 8, FUSE><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part, cnt, out);
   else
-    attn_decode_kernel<WT, D, 16><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part);
+    attn_decode_kernel<WT, D, 16, FUSE><<<grid, block, 0, s>>>(q, k, v, pos, rows, max_len, H, scale, part, cnt,
+                                                               out);
 }
 
-template <typename WT>
+template <typename WT, bool FUSE>
 void launch_attn_t(const float* q, const void* kc, const void* vc, const int32_t* pos, int B, int rows,
-                   int max_len, int H, int n_heads, float* part, hipStream_t s) {
+                   int max_len, int H, int n_heads, float* part, int* cnt, void* out, hipStream_t s) {
   const int D = H / n_heads;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const WT* k = static_cast<const WT*>(kc);
   const WT* v = static_cast<const WT*>(vc);
+  WT* o = static_cast<WT*>(out);
   switch (D) {
-    case 64: launch_attn_d<WT, 64>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, part, s); break;
-    case 128: launch_attn_d<WT, 128>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, part, s); break;
-    case 256: launch_attn_d<WT, 256>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, part, s); break;
+    case 64: launch_attn_d<WT, 64, FUSE>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, part, cnt, o, s); break;
+    case 128: launch_attn_d<WT, 128, FUSE>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, part, cnt, o, s); break;
+    case 256: launch_attn_d<WT, 256, FUSE>(q, k, v, pos, B, rows, max_len, H, n_heads, scale, part, cnt, o, s); break;
     default: break;  // validated
   }
 }
@@ -314,11 +373,19 @@ size_t attn_ws_bytes(int B, int rows, int H, int n_heads) {
 
 void launch_attn_decode(const float* q, const void* k_cache, const void* v_cache, const int32_t* pos,
                         int B, int rows, int max_len, int H, int n_heads, int dt, void* out, bool out_dt,
-                        float* part, hipStream_t s) {
+                        float* part, hipStream_t s, int* fuse_cnt) {
+  if (fuse_cnt != nullptr && out_dt) {
+    // the last split of each (sequence, head) merges: no second launch
+    if (dt == MOEV_BF16)
+      launch_attn_t<u16, true>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, part, fuse_cnt, out, s);
+    else
+      launch_attn_t<float, true>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, part, fuse_cnt, out, s);
+    return;
+  }
   if (dt == MOEV_BF16)
-    launch_attn_t<u16>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, part, s);
+    launch_attn_t<u16, false>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, part, nullptr, nullptr, s);
   else
-    launch_attn_t<float>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, part, s);
+    launch_attn_t<float, false>(q, k_cache, v_cache, pos, B, rows, max_len, H, n_heads, part, nullptr, nullptr, s);
   const dim3 grid(B, n_heads);
   const int D = H / n_heads;
   if (out_dt && dt == MOEV_BF16)

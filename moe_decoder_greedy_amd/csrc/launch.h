@@ -25,9 +25,10 @@ struct TokenSets {
 constexpr int kSetMaxTokens = 128;
 constexpr int set_words(int T) { return (T + 63) / 64; }
 
-// sets != NULL: also clears every mask set.
+// sets != NULL: also clears every mask set; zero[0 .. n_zero) is cleared too
+// (the attention step's merge counts).
 void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, int dt, float* h,
-                  hipStream_t s, const TokenSets* sets = nullptr);
+                  hipStream_t s, const TokenSets* sets = nullptr, int* zero = nullptr, int n_zero = 0);
 void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,
                   const float* bias, int T, int H, int E, int k, int dt, void* x_out,
                   int32_t* topk_idx, float* topk_w, float* logits_out, hipStream_t s);
@@ -137,11 +138,13 @@ void launch_verify(const int32_t* tokens, const int32_t* greedy, int B, int K, i
 
 // Decode attention (moev_attn_decode's kernels, arguments already checked).
 // out: fp32, or dt when out_dt (the operand of the output projection); part:
-// attn_ws_bytes() of fp32 workspace for the splits' states.
+// attn_ws_bytes() of fp32 workspace for the splits' states.  fuse_cnt (with
+// out_dt): B * n_heads counts, zero before the call and zero again after it;
+// the last split of each (sequence, head) merges, so there is one launch.
 size_t attn_ws_bytes(int B, int rows, int H, int n_heads);
 void launch_attn_decode(const float* q, const void* k_cache, const void* v_cache, const int32_t* pos,
                         int B, int rows, int max_len, int H, int n_heads, int dt, void* out, bool out_dt,
-                        float* part, hipStream_t s);
+                        float* part, hipStream_t s, int* fuse_cnt = nullptr);
 
 size_t grouped_ffn_ws_bytes(int T, int I, int k, int ns, int dt);
 // moe_grouped_ffn's argument checks (ws_bytes: the workspace's size)

@@ -42,13 +42,15 @@ constexpr int kMaxSlots = 16;         // k + ns limit of the fused combine
 template <typename WT>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
                                                     const WT* __restrict__ emb, int T, int H, int V,
-                                                    float* __restrict__ h, TokenSets sets) {
+                                                    float* __restrict__ h, TokenSets sets, int* zero,
+                                                    int n_zero) {
   const int t = blockIdx.x;
   if (sets.masks != nullptr) {
     // the blocks clear the mask sets of every layer between them
     const int n = sets.n_sets * sets.E * sets.W;
     for (int i = t * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) sets.masks[i] = 0ull;
   }
+  for (int i = t * blockDim.x + threadIdx.x; i < n_zero; i += gridDim.x * blockDim.x) zero[i] = 0;
   int tok = tokens[t];
   tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
   const WT* src = emb + static_cast<size_t>(tok) * H;
@@ -389,13 +391,14 @@ moev_status check_hidden(int H) {
 
 // Launchers shared with the whole-step driver (no validation).
 void launch_embed(const int32_t* tokens, const void* emb, int T, int H, int V, int dt, float* h,
-                  hipStream_t s, const TokenSets* sets) {
+                  hipStream_t s, const TokenSets* sets, int* zero, int n_zero) {
   TokenSets ts{};
   if (sets != nullptr) ts = *sets;
+  if (zero == nullptr) n_zero = 0;
   if (dt == MOEV_BF16)
-    embed_kernel<u16><<<T, 256, 0, s>>>(tokens, static_cast<const u16*>(emb), T, H, V, h, ts);
+    embed_kernel<u16><<<T, 256, 0, s>>>(tokens, static_cast<const u16*>(emb), T, H, V, h, ts, zero, n_zero);
   else
-    embed_kernel<float><<<T, 256, 0, s>>>(tokens, static_cast<const float*>(emb), T, H, V, h, ts);
+    embed_kernel<float><<<T, 256, 0, s>>>(tokens, static_cast<const float*>(emb), T, H, V, h, ts, zero, n_zero);
 }
 
 void launch_route(const float* h, const void* norm_w, float eps, const void* w_router,

@@ -142,6 +142,7 @@ struct AttnHook {
   float* q;        // [T, H]
   float* ao;       // [T, H] the attention output's W_o projection, added to h by the router
   float* part;     // attention's per-split softmax states
+  int* cnt;        // [B, n_heads] split counts of the fused merge (cleared by the embedding)
 };
 
 __global__ void pos_advance_kernel(int32_t* pos, const int32_t* commit_len, int B) {
@@ -166,7 +167,7 @@ void run_attn_sublayer(const moev_model* m, const AttnHook& at, int l, float* h,
   launch_ffn_down_sets(x, nullptr, nullptr, al.w_qkv, T, 3 * H, H, 0, 0, 1, dt, nullptr, s, true, passes, &qkv);
   // the attention output goes straight into x in the operand type
   launch_attn_decode(at.q, al.k_cache, al.v_cache, at.pos, at.B, at.rows, at.a->max_len, H,
-                     at.a->n_heads, dt, x, true, at.part, s);
+                     at.a->n_heads, dt, x, true, at.part, s, at.cnt);
   launch_ffn_down_sets(x, nullptr, nullptr, al.w_o, T, H, H, 0, 0, 1, dt, at.ao, s, true, passes);
 }
 
@@ -204,7 +205,8 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
   const bool sets = use_sets(T);
   const int W = set_words(T);
   TokenSets ts{masks, pinfo, m->n_layers, E, W};
-  launch_embed(tokens, m->emb, T, H, m->vocab, dt, h, s, sets && m->n_layers > 0 ? &ts : nullptr);
+  launch_embed(tokens, m->emb, T, H, m->vocab, dt, h, s, sets && m->n_layers > 0 ? &ts : nullptr,
+               at != nullptr ? at->cnt : nullptr, at != nullptr ? at->B * at->a->n_heads : 0);
   for (int l = 0; l < m->n_layers; ++l) {
     const moev_layer_weights& lw = m->layers[l];
     const float* y_prev = l > 0 ? y : nullptr;
@@ -442,7 +444,7 @@ namespace {
 // Attention step workspace: the verify step's, then the dense-GEMM row list
 // and the attention sublayer's buffers.
 struct AttnLayout {
-  size_t q, ao, part, total;
+  size_t q, ao, part, cnt, total;
 };
 
 AttnLayout attn_layout(const moev_model& m, const moev_attn& a, int B, int K) {
@@ -458,6 +460,7 @@ AttnLayout attn_layout(const moev_model& m, const moev_attn& a, int B, int K) {
   A.q = take(rowf);
   A.ao = take(rowf);
   A.part = take(a.n_heads >= 1 ? attn_ws_bytes(B, K + 1, m.hidden, a.n_heads) : 0);
+  A.cnt = take(static_cast<size_t>(B) * (a.n_heads >= 1 ? a.n_heads : 0) * sizeof(int));
   A.total = o;
   return A;
 }
@@ -519,7 +522,8 @@ extern "C" moev_status moev_verify_step_attn(const moev_model* m, const moev_att
   const hipStream_t s = as_stream(stream);
   const int T = B * (K + 1);
   const AttnHook at{a, B, K + 1, pos, reinterpret_cast<float*>(base + A.q),
-                    reinterpret_cast<float*>(base + A.ao), reinterpret_cast<float*>(base + A.part)};
+                    reinterpret_cast<float*>(base + A.ao), reinterpret_cast<float*>(base + A.part),
+                    reinterpret_cast<int*>(base + A.cnt)};
   if (moev_status st = run_step(m, tokens, B, K, greedy, n_accept, commit, commit_len, next_last, ws,
                                 ws_bytes, nullptr, stream, nullptr, &at))
     return st;
