@@ -17,8 +17,9 @@
 // state unchanged).  Each split writes its unnormalised softmax state
 // (maximum, sum, weighted values) to a workspace; attn_merge_kernel combines
 // the splits (in the verify step the last split of a (sequence, head) to
-// finish does, see attn_decode_kernel's FUSE).  Splitting shortens each workgroup's chain of dependent chunk
-// loads, which bounds the kernel, and spreads the work over more CUs.  Per
+// finish does, see attn_decode_kernel's FUSE).  Splitting shortens each
+// workgroup's chain of dependent chunk loads, which bounds the kernel, and
+// spreads the work over more CUs.  Per
 // chunk: four lanes share a key row, each multiplying its D/4 adjacent
 // columns by every verify row's query (staged in LDS) and the four summing
 // their parts in a fixed order, so a load instruction covers 16 rows in
@@ -304,13 +305,15 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
     if (last) {
       const long long slot0 = slot - split;
       const float* po0 = part + slot0 * rows * D;
-      const float* pml0 = part + static_cast<long long>(gridDim.x) * gridDim.y * kAttnSplits * rows * D + slot0 * rows * 2;
+      const float* pml0 =
+          part + static_cast<long long>(gridDim.x) * gridDim.y * kAttnSplits * rows * D + slot0 * rows * 2;
       for (int i = threadIdx.x; i < rows * D; i += blockDim.x) {
         const int r = i / D, c = i - r * D;
         out[(static_cast<long long>(b) * rows + r) * H + h * D + c] =
             from_f32<WT>(merge_splits(po0, pml0, rows, D, r, c, ld_agent));
       }
-      if (threadIdx.x == 0) __hip_atomic_store(cnt + b * gridDim.y + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0)
+        __hip_atomic_store(cnt + b * gridDim.y + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
