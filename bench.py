@@ -754,6 +754,21 @@ def run_verify(args, torch, np):
         log(f"graph: {t_graph * 1e3:.3f} ms/step, commits as expected: {graph_ok}")
         del g
 
+    # per-step distribution (eager launches, outside the timed region): HIP
+    # events on the step's stream around each of the timed steps' inputs
+    ev_pairs = []
+    for s in range(args.warmup, n_steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dm.verify_step(inputs_d[s], out=step_out(s))
+        e1.record()
+        ev_pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev_pairs])
+    step_pct = {"p10": round(float(np.percentile(step_ms, 10)), 4),
+                "p50": round(float(np.percentile(step_ms, 50)), 4),
+                "p90": round(float(np.percentile(step_ms, 90)), 4)}
+
     if args.launch == "eager" or t_graph is None:
         t_step, launch = t_eager, "eager"
     elif args.launch == "graph":
@@ -832,6 +847,7 @@ def run_verify(args, torch, np):
         "committed_tokens_per_s": round(committed / t_step, 1), "tau": round(tau, 4),
         "lossless_commits": lossless,
         "ms_per_step_eager": round(t_eager * 1e3, 4),
+        "ms_per_step_eager_percentiles": step_pct,
         "ms_per_step_graph": None if t_graph is None else round(t_graph * 1e3, 4),
         "step_roofline": {"bound": "hbm", "bytes_per_step": int(step_bytes), "achieved": round(step_gbs, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
