@@ -140,6 +140,26 @@ def copy_probe(torch, mib: int):
     log(f"copy probe: {mib} MiB read + {mib} MiB written per copy, 3 copies")
 
 
+def copy_ceiling_gbs(torch, mib: int = 1024, reps: int = 5) -> float:
+    """Achievable-bandwidth reference: a plain device-to-device copy of mib
+    MiB (read + written bytes per copy) timed with HIP events, best of reps."""
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return 2 * n / (best * 1e-3) / 1e9
+
+
 def cpu_baseline(wl, weights, tokens_np, budget_s, gpu_greedy=None):
     """The oracle as it stands, on this host's cores, over one verify step of
     the same batch: layers are timed one by one until the budget is spent and
@@ -854,12 +874,16 @@ def run_verify(args, torch, np):
                           "bytes": "algorithmic: router weights, every touched expert's three matrices once, "
                                    "residual in and out per layer; head weights, its input rows and tokens"},
         "roofline": roofline,
+        "hbm_copy_ceiling": {"gbs": round(copy_ceiling_gbs(torch), 1), "frac_of_peak": None,
+                             "note": "1 GiB device-to-device copy, read + written bytes, best of 5 (HIP events): "
+                                     "the achievable rate for a plain streamed read and write on this GPU"},
         "kernel_avg_us": {n: round(v, 2) for n, v in dur_us.items()},
         "kernel_avg_us_note": "HIP events recorded by the step driver around each stage's launches, averaged "
                               "over layers; each event pair adds a few us, so the stages sum to more than "
                               "ms_per_step; route includes the previous layer's combine, head its norm and "
                               "the prefix accept",
     }
+    result["hbm_copy_ceiling"]["frac_of_peak"] = round(result["hbm_copy_ceiling"]["gbs"] / HBM_PEAK_GBS, 4)
     result["near_ties"] = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
