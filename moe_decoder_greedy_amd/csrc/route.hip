@@ -166,26 +166,12 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
       const float4* ys = reinterpret_cast<const float4*>(a.y + t * a.S * H + i);
       if (live) {
         v = *reinterpret_cast<const float4*>(a.h + t * H + i);
-        if (COMBINE && PRELOAD) load_slots<SL>(sv, ys, a.S, h4);
+        if (COMBINE) load_slots<SL>(sv, ys, a.S, h4);
       }
       if (it == 0) preload_router();
       if (!live) continue;
       if (COMBINE) {
-        if constexpr (PRELOAD) {
-          v = sum_slots<SL>(v, sv, a.S);
-        } else {  // the same left-to-right sum, each slot added as it arrives
-          float4 acc = ys[0];
-#pragma unroll
-          for (int sl = 1; sl < SL; ++sl)
-            if (sl < a.S) {
-              const float4 yv = ys[static_cast<size_t>(sl) * h4];
-              acc.x += yv.x;
-              acc.y += yv.y;
-              acc.z += yv.z;
-              acc.w += yv.w;
-            }
-          v = make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
-        }
+        v = sum_slots<SL>(v, sv, a.S);
         if constexpr (kDefer) hkeep[it] = v;
         else *reinterpret_cast<float4*>(a.h_out + t * H + i) = v;
       }
