@@ -295,6 +295,15 @@ __global__ __launch_bounds__(kWave * kAttnWaves) void attn_decode_kernel(
     }
   }
   if constexpr (FUSE) {
+    // Ordering, stated for the hardware rather than through C++ fences (an
+    // agent-scope release or acquire fence would write back or invalidate
+    // the whole L2 of the XCD): (1) the state stores above are agent-scope
+    // atomic stores, written through to the device's coherence point; (2)
+    // s_waitcnt(0) returns only once every one of them is acknowledged, and
+    // the barrier makes that hold for all threads before (3) thread 0's
+    // atomic add, which is performed at the coherence point too; (4) the
+    // merging split issues its agent-scope loads only after its own add has
+    // returned the count of the other two, so they read the completed states.
     __shared__ int last;
     __builtin_amdgcn_s_waitcnt(0);  // this thread's state stores are complete
     __syncthreads();
