@@ -63,14 +63,17 @@ def _gpu_cache(A, key):
     return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy().astype(np.float64)
 
 
-def test_attn_step_tiny_matches_oracle(model_mod):
-    """The tiny fp32 model, 3 sequences, K = 3, four passes: unflagged greedy
-    tokens equal the oracle's, acceptance follows them, every cache row the
-    passes wrote matches the oracle's, and pos advances by commit_len."""
+@pytest.mark.parametrize("K", [3, 7, 15])
+def test_attn_step_tiny_matches_oracle(model_mod, K):
+    """The tiny fp32 model, 3 sequences, K drafts (4, 8 and 16 rows per
+    sequence: every row-count build of the attention kernel, whose last split
+    merges the states), four passes: unflagged greedy tokens equal the
+    oracle's, acceptance follows them, every cache row the passes wrote
+    matches the oracle's, and pos advances by commit_len."""
     shape, heads = synth.TINY, 2
     w = synth.model_weights(shape)
     attn = synth.attention_weights(shape)
-    B, K, L = 3, 3, 48
+    B, L = 3, 24 + 4 * (K + 1)
     raw, pos = _prefix_caches(shape, B, K + 1, L, (0, 20), seed=41)
     dm = model_mod.DeviceModel(w)
     dm.attach_attention(attn, heads, B, L)
@@ -115,7 +118,7 @@ def _rollout(dm, last, pos0, n):
     return np.stack(seq, axis=1)
 
 
-@pytest.mark.parametrize("B,K", [(8, 1), (8, 3), (32, 1), (32, 3)])
+@pytest.mark.parametrize("B,K", [(8, 1), (8, 3), (8, 7), (32, 1), (32, 3)])
 def test_attn_step_is_lossless(model_mod, B, K):
     """Speculative passes with drafts right with probability 0.7 commit exactly
     the tokens of one-row greedy decoding from the same caches, bit for bit,
