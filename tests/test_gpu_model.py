@@ -284,7 +284,19 @@ def test_zipf_step_matches_oracle(zipf_pair, B, K):
     model) through the whole 12-layer step at the sweep's batch sizes: every
     position's greedy token against the oracle, acceptance and commits
     against the oracle's where positions 0..n are unflagged."""
-    w, dm = zipf_pair
+    _step_matches_oracle(*zipf_pair, B, K, f"zipf_step_b{B}k{K}")
+
+
+@pytest.mark.parametrize("B", [64, 128])
+def test_step_larger_batches_match_oracle(decoder_pair, B):
+    """Uniform routing above 128 rows (B = 64 and 128, K = 3: 256 and 512
+    rows, every routed group touched): the sorted pair order, the tiled expert
+    GEMMs, the two-token router blocks and the 256-token head tiles, every
+    position against the oracle as in the skewed case."""
+    _step_matches_oracle(*decoder_pair, B, 3, f"step_b{B}k3")
+
+
+def _step_matches_oracle(w, dm, B, K, tag):
     V = w["shape"].vocab
     last = synth.initial_tokens(B, V, seed=20 + B)
     rng = np.random.default_rng(30 + B + K)
@@ -294,8 +306,7 @@ def test_zipf_step_matches_oracle(zipf_pair, B, K):
     out = dm.verify_step(dev_i32(tokens))
     gg = host(out["greedy"])
     ref = oracle.verify_step(tokens[:, 0], tokens[:, 1:], w, operands="bf16")
-    flagged, flips = _check_greedy(dm, w, tokens, gg, ref["greedy"], ref["gap"], ref["router_gap"],
-                                   f"zipf_step_b{B}k{K}")
+    flagged, flips = _check_greedy(dm, w, tokens, gg, ref["greedy"], ref["gap"], ref["router_gap"], tag)
     flagged = flagged.reshape(B, K + 1)
     for t, _, _ in flips:
         flagged |= tokens == t
