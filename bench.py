@@ -803,9 +803,10 @@ def run_verify(args, torch, np):
     # run on, right around the launches of one stage per pass, so the GPU is
     # never waiting on the host between the two events.
     # (the step driver folds each combine into the next router launch)
-    # decode-sized steps (T <= 128) fill token sets in the router and
-    # launch no permute kernel, so that stage is only timed above
-    stages = ("route", "gate_up", "down", "head") if T <= 128 else ("route", "permute", "gate_up", "down", "head")
+    # steps of up to 512 rows (this decoder's shape tiles both expert GEMMs)
+    # fill token sets in the router and launch no permute kernel, so that
+    # stage is only timed above
+    stages = ("route", "gate_up", "down", "head") if T <= 512 else ("route", "permute", "gate_up", "down", "head")
     dur_us = {}
     for st in stages:
         n_ev = 1 if st == "head" else shape.n_layers

@@ -45,7 +45,8 @@ constexpr int kRtHead = 2;           // 16-row tiles per wave, LM head
 constexpr int kWavesFfn = 4;         // wavefronts per workgroup, expert GEMMs
 constexpr int kTileMinTokens = 128;  // larger batches use the tile schedule
 constexpr int kWavesHead = 8;        // wavefronts per workgroup, LM head
-static_assert(kTileMinTokens == kSetMaxTokens, "the step's token-set mode is the streaming schedule's range");
+static_assert(kTileMinTokens <= 128 && kSetMaxTokens <= 512,
+              "token sets: two mask words on the streaming schedule, at most eight on the tiled one");
 
 // MT = tokens per pass (32, 64 or 128 = 2, 4 or 8 MFMA column tiles).  The
 // variant only changes how many accumulators and LDS rows a workgroup holds;
@@ -143,6 +144,27 @@ __device__ __forceinline__ int set_token(const GemmArgs& a, const TokenSel& sel,
   return sel.masked ? min(nth_set_bit(sel.lo, sel.hi, m), a.T - 1) : m;
 }
 
+// Token sets on the tiled schedule (up to eight mask words): the size of
+// routed group g's set, and its m-th token (clamped to a row).
+__device__ __forceinline__ int set_size(const GemmArgs& a, int g) {
+  const uint64_t* mk = a.masks + static_cast<long long>(g) * a.W;
+  int n = 0;
+  for (int w = 0; w < a.W; ++w) n += __popcll(mk[w]);
+  return min(n, a.T);
+}
+__device__ __forceinline__ int set_nth(const GemmArgs& a, int g, int m) {
+  const uint64_t* mk = a.masks + static_cast<long long>(g) * a.W;
+  int base = 0;
+  for (int w = 0; w < a.W; ++w) {
+    const uint64_t x = mk[w];
+    const int c = __popcll(x);
+    if (m < c) return min(base + nth_set_bit(x, 0ull, m), a.T - 1);
+    m -= c;
+    base += 64;
+  }
+  return a.T - 1;
+}
+
 // Four gain elements as loaded (bf16 pairs or fp32), converted when used.
 template <typename WT> struct GainRaw;
 template <> struct GainRaw<u16> {
@@ -170,6 +192,14 @@ __device__ __forceinline__ long long operand_row(const GemmArgs& a, const TokenS
                             : clampi(a.sorted_src[off + m0 + row], 0, a.P - 1) / a.S;
   if (MODE == kDown) return off + m0 + row;
   return m0 + row;
+}
+
+// Operand row of token row `row` of a tile pass (the tiled schedule): with
+// token sets a gate/up tile of routed group g reads its m-th token's row.
+template <int MODE, bool SETS>
+__device__ __forceinline__ long long tile_row(const GemmArgs& a, int g, int off, int m0, int row) {
+  if constexpr (SETS && MODE == kGateUp) return g < a.E ? set_nth(a, g, m0 + row) : m0 + row;
+  else return operand_row<MODE, false>(a, TokenSel{}, off, m0, row);
 }
 
 // Down projection: output pair and router weight of token row m of a pass,
@@ -714,7 +744,9 @@ template <typename WT, int BT, int P> __device__ __forceinline__ unsigned char* 
   else return x1;
 }
 
-template <typename WT, int MODE, int BT>
+// SETS: the groups are token sets (routed group g's rows from its mask,
+// pairs from pinfo, act rows g*T + m) instead of moe_permute's order.
+template <typename WT, int MODE, int BT, bool SETS = false>
 __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPerCu)) void tile_gemm(
     GemmArgs a, int n_ctiles, int G) {
   using TC = TileCfg<WT, BT>;
@@ -739,7 +771,11 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   // LM head is one group of T tokens.
   if (tid < ng) {
     int M = a.T;
-    if (MODE != kHead) M = max(0, min(a.offsets[tid + 1], a.P) - max(min(a.offsets[tid], a.P), 0));
+    if constexpr (SETS) {
+      if (tid < a.E) M = set_size(a, tid);
+    } else if (MODE != kHead) {
+      M = max(0, min(a.offsets[tid + 1], a.P) - max(min(a.offsets[tid], a.P), 0));
+    }
     const int mt = (M + BT - 1) / BT;
     group_mt[tid] = mt;
     group_tiles[tid] = mt * n_ctiles;
@@ -812,8 +848,14 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
   auto setup = [&](int buf) {
     g = tile_info[buf][0];
     ct = tile_info[buf][1];
-    off = MODE == kHead ? 0 : clampi(a.offsets[g], 0, a.P);
-    const int M = MODE == kHead ? a.T : clampi(a.offsets[g + 1], off, a.P) - off;
+    int M;
+    if constexpr (SETS) {
+      off = g * a.T;
+      M = g < a.E ? set_size(a, g) : a.T;
+    } else {
+      off = MODE == kHead ? 0 : clampi(a.offsets[g], 0, a.P);
+      M = MODE == kHead ? a.T : clampi(a.offsets[g + 1], off, a.P) - off;
+    }
     m0 = tile_info[buf][2] * BT;
     mp = min(BT, M - m0);
 #pragma unroll
@@ -840,13 +882,13 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
         const int r = lane >> 3;
         const int row = min(ii * 8 + r, mp - 1);
         const int c = (lane & 7) ^ r ^ (ii & 1);
-        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE, false>(a, TokenSel{}, off, m0, row) * K + c * 8;
+        xsrc[i] = static_cast<const WT*>(a.x) + tile_row<MODE, SETS>(a, g, off, m0, row) * K + c * 8;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < kXPtr; ++i) {
         const int row = min((wave * TC::kXPerWave + i) * 16 + r16, mp - 1);
-        xsrc[i] = static_cast<const WT*>(a.x) + operand_row<MODE, false>(a, TokenSel{}, off, m0, row) * K + q * 8;
+        xsrc[i] = static_cast<const WT*>(a.x) + tile_row<MODE, SETS>(a, g, off, m0, row) * K + q * 8;
       }
     }
   };
@@ -1064,10 +1106,27 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
       for (int j = 0; j < 4; ++j) {
         const int m = wt * 64 + j * 16 + r16;
         if (m < e_mp) {
-          const int p = clampi(a.sorted_src[e_off + e_m0 + m], 0, a.P - 1);
-          const int t = p / a.S;
-          const int slot = p - t * a.S;
-          const float wgt = slot < a.k ? a.topk_w[static_cast<long long>(t) * a.k + slot] : 1.0f;
+          int p;
+          float wgt;
+          if constexpr (SETS) {
+            int t, slot;
+            wgt = 1.0f;
+            if (e_g < a.E) {
+              t = set_nth(a, e_g, e_m0 + m);
+              const int2 pi = a.pinfo[static_cast<long long>(t) * a.E + e_g];
+              slot = clampi(pi.y, 0, a.k - 1);
+              wgt = __int_as_float(pi.x);
+            } else {
+              t = e_m0 + m;
+              slot = a.k + e_g - a.E;
+            }
+            p = t * a.S + slot;
+          } else {
+            p = clampi(a.sorted_src[e_off + e_m0 + m], 0, a.P - 1);
+            const int t = p / a.S;
+            const int slot = p - t * a.S;
+            wgt = slot < a.k ? a.topk_w[static_cast<long long>(t) * a.k + slot] : 1.0f;
+          }
 #pragma unroll
           for (int rt = 0; rt < 8; ++rt) {
             f32x4 o = acc[rt][j];
@@ -1112,14 +1171,15 @@ int tile_grid(int T, int k, int ns, int E, int n_ctiles, int BT, int per_cu) {
 
 // 256-token tiles once routed groups average 384 tokens or more (less
 // padding in ragged last tiles below that).
-template <typename WT, int MODE>
+template <typename WT, int MODE, bool SETS = false>
 void launch_tile(const GemmArgs& args, int n_ctiles, int G, int E, int k, int ns, hipStream_t s) {
-  if (static_cast<long long>(args.T) * k >= 384LL * E && (!TileCfg<WT, 256>::kXPair || args.K % 64 == 0)) {
+  // token sets reach at most kSetMaxTokens rows: always 128-token tiles
+  if (!SETS && static_cast<long long>(args.T) * k >= 384LL * E && (!TileCfg<WT, 256>::kXPair || args.K % 64 == 0)) {
     const int grid = tile_grid(args.T, k, ns, E, n_ctiles, 256, TileCfg<WT, 256>::kPerCu);
     tile_gemm<WT, MODE, 256><<<grid, TileCfg<WT, 256>::kThreads, 0, s>>>(args, n_ctiles, G);
   } else {
     const int grid = tile_grid(args.T, k, ns, E, n_ctiles, 128, TileCfg<WT, 128>::kPerCu);
-    tile_gemm<WT, MODE, 128><<<grid, TileCfg<WT, 128>::kThreads, 0, s>>>(args, n_ctiles, G);
+    tile_gemm<WT, MODE, 128, SETS><<<grid, TileCfg<WT, 128>::kThreads, 0, s>>>(args, n_ctiles, G);
   }
 }
 
@@ -1491,6 +1551,12 @@ void launch_ffn_gate_up_sets(const void* x, const uint64_t* masks, const void* w
       stream_gemm<float, kGateUp, 2, 32, kWavesFfn, kWavesFfn><<<grid, kWavesFfn * 64, 0, s>>>(up);
     return;
   }
+  if (T > kTileMinTokens) {  // sets_fit: I is a whole number of column tiles
+    const int nct = I / tile_cols<kGateUp>();
+    if (dt == MOEV_BF16) launch_tile<u16, kGateUp, true>(up, nct, E + ns, E, k, ns, s);
+    else launch_tile<float, kGateUp, true>(up, nct, E + ns, E, k, ns, s);
+    return;
+  }
   const dim3 grid(I / (16 * kWavesFfn), E + ns);
   if (dt == MOEV_BF16)
     launch_gemm<u16, kGateUp, 2, kWavesFfn>(up, grid, s);
@@ -1534,11 +1600,22 @@ void launch_ffn_down_sets(const void* act, const uint64_t* masks, const int2* pi
       stream_gemm<float, kDown, kRtDown, 32, kWavesFfn, kWavesFfn><<<grid, kWavesFfn * 64, 0, s>>>(dn);
     return;
   }
+  if (T > kTileMinTokens) {  // sets_fit: H is a whole number of column tiles
+    const int nct = H / tile_cols<kDown>();
+    if (dt == MOEV_BF16) launch_tile<u16, kDown, true>(dn, nct, E + ns, E, k, ns, s);
+    else launch_tile<float, kDown, true>(dn, nct, E + ns, E, k, ns, s);
+    return;
+  }
   const dim3 grid(H / (16 * kRtDown * kWavesFfn), E + ns);
   if (dt == MOEV_BF16)
     launch_gemm<u16, kDown, kRtDown, kWavesFfn>(dn, grid, s);
   else
     launch_gemm<float, kDown, kRtDown, kWavesFfn>(dn, grid, s);
+}
+
+bool sets_fit(int T, int H, int I) {
+  return T <= kTileMinTokens ||
+         (T <= kSetMaxTokens && I % tile_cols<kGateUp>() == 0 && H % tile_cols<kDown>() == 0);
 }
 
 void launch_grouped_ffn(const void* x, const int32_t* sorted_src, const int32_t* offsets,

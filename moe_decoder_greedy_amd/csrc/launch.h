@@ -7,7 +7,7 @@
 namespace moev {
 
 // Token sets (the whole-step driver's replacement for the sorted pair order
-// at decode sizes, T <= kSetMaxTokens): routed group g < E holds the tokens
+// up to kSetMaxTokens rows, see sets_fit): routed group g < E holds the tokens
 // whose bit is set in masks[g*W ..] (bit t % 64 of word t / 64, W =
 // ceil(T / 64)), in increasing token order, and pair (t, g) has pinfo[t*E +
 // g] = {bits of its renormalised router weight, its slot}.  The router sets
@@ -20,10 +20,13 @@ struct TokenSets {
   int2* pinfo;      // [T][E]
   int n_sets, E, W;
 };
-// token-set mode only on the streaming GEMM schedule; above this many tokens
-// the tiled schedule is faster (and a set fits two 64-bit words)
-constexpr int kSetMaxTokens = 128;
+// Token sets serve the streaming GEMM schedule (up to 128 rows, a set in two
+// 64-bit words) and the tiled one above it, up to this many rows (8 words)
+constexpr int kSetMaxTokens = 512;
 constexpr int set_words(int T) { return (T + 63) / 64; }
+// Whether a step of T rows runs on token sets: up to 128 rows always, above
+// that when both expert GEMMs take the tiled schedule at this shape.
+bool sets_fit(int T, int H, int I);
 
 // sets != NULL: also clears every mask set; zero[0 .. n_zero) is cleared too
 // (the attention step's merge counts).
@@ -68,7 +71,7 @@ void run_draft(const moev_model& m, const moev_draft_weights& d, const float* z_
                int out_stride, int out_col0, int32_t* t0_copy, float* z_out, unsigned char* ws,
                hipStream_t s);
 
-// Expert GEMMs over token sets (T <= kSetMaxTokens; masks and pinfo may be
+// Expert GEMMs over token sets (sets_fit(T, H, I); masks and pinfo may be
 // NULL when E = 0): act holds G*T rows.  split_k: each workgroup's waves split
 // one row tile's K range (passes of at most 32 tokens, every size): several
 // times the workgroups for GEMMs over a few groups, with rounding that

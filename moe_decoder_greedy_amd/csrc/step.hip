@@ -21,7 +21,7 @@ struct StepLayout {
 
 // Decode-sized steps route through token sets filled by the router (no
 // permute launch); larger ones through the sorted pair order.
-bool use_sets(int T) { return T <= kSetMaxTokens; }
+bool use_sets(const moev_model& m, int T) { return sets_fit(T, m.hidden, m.inter); }
 
 size_t esz(int dt) { return dt == MOEV_BF16 ? 2 : 4; }
 
@@ -40,7 +40,7 @@ StepLayout layout(const moev_model& m, int T) {
   L.x = take(static_cast<size_t>(T) * m.hidden * esz(m.dtype));
   L.idx = take(static_cast<size_t>(T) * m.top_k * 4);
   L.w = take(static_cast<size_t>(T) * m.top_k * 4);
-  const bool sets = use_sets(T);
+  const bool sets = use_sets(m, T);
   L.offsets = take(static_cast<size_t>(G + 1) * 4);
   // sorted pair order [P] (without token sets)
   L.sorted = take(sets ? 0 : P * 4);
@@ -202,7 +202,7 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
   // embedding kernel clears one mask set per layer and the router adds each
   // pair to its expert's set.
   const int S = k + ns;
-  const bool sets = use_sets(T);
+  const bool sets = use_sets(*m, T);
   const int W = set_words(T);
   TokenSets ts{masks, pinfo, m->n_layers, E, W};
   launch_embed(tokens, m->emb, T, H, m->vocab, dt, h, s, sets && m->n_layers > 0 ? &ts : nullptr,

@@ -318,12 +318,12 @@ def _step_matches_oracle(w, dm, B, K, tag):
     np.testing.assert_array_equal(host(out["commit"])[clear], ref["commit"][clear])
 
 
-def _stage_chain_check(dm, seed, min_group=0):
+def _stage_chain_check(dm, seed, min_group=0, B=32):
     """dm.verify_step's greedy tokens against chaining the per-stage entry
     points, bit for bit; returns the largest routed group seen."""
     from moe_decoder_greedy_amd import ops
     shape = dm.shape
-    B, K = 32, 3
+    K = 3
     toks = np.random.default_rng(seed).integers(0, shape.vocab, size=(B, K + 1)).astype(np.int32)
     td = dev_i32(toks)
     fused = host(dm.verify_step(td)["greedy"]).reshape(-1)
@@ -347,6 +347,16 @@ def test_step_matches_stage_chain(decoder_pair):
     tokens, bit for bit, as chaining the per-stage entry points (the sorted
     pair order of moe_permute)."""
     _stage_chain_check(decoder_pair[1], 13)
+
+
+@pytest.mark.parametrize("B", [64, 128])
+def test_step_matches_stage_chain_tiled_sets(decoder_pair, zipf_pair, B):
+    """Above 128 rows (256 and 512) the step's expert GEMMs take the tiled
+    schedule on the router's token sets (rows found from the masks, pairs from
+    the pair table); the per-stage chain takes it on moe_permute's order.
+    Same bits, with uniform and with skewed routing."""
+    _stage_chain_check(decoder_pair[1], 19 + B, B=B)
+    _stage_chain_check(zipf_pair[1], 23 + B, B=B)
 
 
 def test_step_matches_stage_chain_skewed(zipf_pair):
