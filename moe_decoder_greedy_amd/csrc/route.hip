@@ -115,6 +115,12 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
   const int nt = min(kRouteTPB, T - t0);
   constexpr int kStageIt = (kRouteTPB * NCH * 64 + kRouteThreads - 1) / kRouteThreads;
   constexpr bool kDefer = PRELOAD;  // stores after the logits
+  static_assert(64 % kRouteTPB == 0, "a block's tokens share one 64-bit mask word");
+  // with several tokens per block: their token-set bits per expert, gathered
+  // here and sent with one global OR per expert (fewer atomics on a hot
+  // expert's mask words when the routing is skewed)
+  __shared__ unsigned long long blk_bits[kRouteTPB > 1 ? 64 : 1];
+  if (kRouteTPB > 1 && threadIdx.x < 64) blk_bits[threadIdx.x] = 0ull;
   constexpr int kWpt = kRouteWaves / kRouteTPB;  // waves counting one token's ranks
   constexpr int kEpw = 64 / kWpt;                // entries each of them compares
   static_assert(kEpw % 4 == 0, "rank parts over whole float4 reads");
@@ -304,10 +310,24 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
         a.topk_w[static_cast<size_t>(t) * k + lane] = wgt;
         if (a.masks != nullptr) {
           // token t joins expert e's set (no value returned, nothing waits)
-          __hip_atomic_fetch_or(a.masks + static_cast<size_t>(e) * a.W + (t >> 6), 1ull << (t & 63),
-                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if constexpr (kRouteTPB > 1)
+            __hip_atomic_fetch_or(&blk_bits[e], 1ull << (t & 63), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          else
+            __hip_atomic_fetch_or(a.masks + static_cast<size_t>(e) * a.W + (t >> 6), 1ull << (t & 63),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           a.pinfo[static_cast<size_t>(t) * E + e] = make_int2(__float_as_int(wgt), lane);
         }
+      }
+    }
+  }
+  if constexpr (kRouteTPB > 1) {
+    if (a.masks != nullptr) {
+      __syncthreads();
+      if (threadIdx.x < E) {
+        const unsigned long long bits = blk_bits[threadIdx.x];
+        if (bits != 0ull)
+          __hip_atomic_fetch_or(a.masks + static_cast<size_t>(threadIdx.x) * a.W + (t0 >> 6), bits,
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
