@@ -69,12 +69,12 @@ struct GemmArgs {
   const void* x;            // operand rows
   const int32_t* offsets;   // [G+1] (gate/up, down)
   const int32_t* sorted_src;
-  // token-set mode (streaming schedule only, T <= 128): routed group g < E
-  // holds the tokens whose bit is set in masks[g*W ..], shared groups every
+  // token-set mode: routed group g < E holds the tokens whose bit is set in
+  // its mask words (masks[set_word(E, g, w)]), shared groups every
   // token; group g's m-th token has act row g*T + m (see TokenSets)
   bool sets;
   int E, W;
-  const uint64_t* masks;    // [E][W]
+  const uint64_t* masks;    // [W][E]
   const int2* pinfo;        // [T][E] (down): {bits of the pair's weight, slot}
 
   int S, k, P, T;           // slots, routed slots, pairs, tokens
@@ -145,20 +145,31 @@ __device__ __forceinline__ int set_token(const GemmArgs& a, const TokenSel& sel,
 }
 
 // Token sets on the tiled schedule (up to eight mask words): the size of
-// routed group g's set, and its m-th token (clamped to a row).
+// routed group g's set, and its m-th token (clamped to a row).  Both load
+// every word up front (clamped to the last one, so all loads are in bounds and
+// independent) and then count in registers.
+constexpr int kSetMaxWords = kSetMaxTokens / 64;
+__device__ __forceinline__ void set_load(const GemmArgs& a, int g, uint64_t (&x)[kSetMaxWords]) {
+#pragma unroll
+  for (int w = 0; w < kSetMaxWords; ++w) x[w] = a.masks[set_word(a.E, g, min(w, a.W - 1))];
+}
 __device__ __forceinline__ int set_size(const GemmArgs& a, int g) {
-  const uint64_t* mk = a.masks + static_cast<long long>(g) * a.W;
+  uint64_t x[kSetMaxWords];
+  set_load(a, g, x);
   int n = 0;
-  for (int w = 0; w < a.W; ++w) n += __popcll(mk[w]);
+#pragma unroll
+  for (int w = 0; w < kSetMaxWords; ++w) n += w < a.W ? __popcll(x[w]) : 0;
   return min(n, a.T);
 }
 __device__ __forceinline__ int set_nth(const GemmArgs& a, int g, int m) {
-  const uint64_t* mk = a.masks + static_cast<long long>(g) * a.W;
+  uint64_t x[kSetMaxWords];
+  set_load(a, g, x);
   int base = 0;
-  for (int w = 0; w < a.W; ++w) {
-    const uint64_t x = mk[w];
-    const int c = __popcll(x);
-    if (m < c) return min(base + nth_set_bit(x, 0ull, m), a.T - 1);
+#pragma unroll
+  for (int w = 0; w < kSetMaxWords; ++w) {
+    if (w >= a.W) break;
+    const int c = __popcll(x[w]);
+    if (m < c) return min(base + nth_set_bit(x[w], 0ull, m), a.T - 1);
     m -= c;
     base += 64;
   }
@@ -575,9 +586,8 @@ __device__ __forceinline__ void stream_gemm_wg(const GemmArgs& a, int bx, int by
       off = g * a.T;
       M = a.T;
       if (g < a.E) {
-        const uint64_t* mk = a.masks + static_cast<long long>(g) * a.W;
-        sel.lo = mk[0];
-        sel.hi = a.W > 1 ? mk[1] : 0ull;
+        sel.lo = a.masks[set_word(a.E, g, 0)];
+        sel.hi = a.W > 1 ? a.masks[set_word(a.E, g, 1)] : 0ull;
         sel.masked = true;
         M = min(__popcll(sel.lo) + __popcll(sel.hi), a.T);
       }

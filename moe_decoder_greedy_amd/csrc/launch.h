@@ -8,15 +8,16 @@ namespace moev {
 
 // Token sets (the whole-step driver's replacement for the sorted pair order
 // up to kSetMaxTokens rows, see sets_fit): routed group g < E holds the tokens
-// whose bit is set in masks[g*W ..] (bit t % 64 of word t / 64, W =
-// ceil(T / 64)), in increasing token order, and pair (t, g) has pinfo[t*E +
-// g] = {bits of its renormalised router weight, its slot}.  The router sets
-// both with no returned value to wait for (an atomic OR and a store).
+// whose bit is set in its mask words (bit t % 64 of word t / 64, W =
+// ceil(T / 64); word w of group g at masks[set_word(E, g, w)]), in increasing
+// token order, and pair (t, g) has pinfo[t*E + g] = {bits of its renormalised
+// router weight, its slot}.  The router sets both with no returned value to
+// wait for (an atomic OR and a store).
 // Groups g >= E (the shared experts, and every group of a dense projection,
 // E = 0) hold every token in order, slot k + g - E, weight 1.  Group g's m-th
 // token has act row g*T + m.
 struct TokenSets {
-  uint64_t* masks;  // [n_sets][E][W]: one set per layer
+  uint64_t* masks;  // [n_sets][W][E]: one set per layer
   int2* pinfo;      // [T][E]
   int n_sets, E, W;
 };
@@ -24,6 +25,12 @@ struct TokenSets {
 // 64-bit words) and the tiled one above it, up to this many rows (8 words)
 constexpr int kSetMaxTokens = 512;
 constexpr int set_words(int T) { return (T + 63) / 64; }
+// Mask words are stored word-major ([W][E]): the words of one heavily routed
+// expert sit in different cache lines, so under skewed routing its atomic ORs
+// do not all queue on one line.
+__host__ __device__ constexpr size_t set_word(int E, int g, int w) { return static_cast<size_t>(w) * E + g; }
+// 64-bit words of one layer's token sets
+__host__ __device__ constexpr size_t set_layer_words(int E, int T) { return static_cast<size_t>(set_words(T)) * E; }
 // Whether a step of T rows runs on token sets: up to 128 rows always, above
 // that when both expert GEMMs take the tiled schedule at this shape.
 bool sets_fit(int T, int H, int I);

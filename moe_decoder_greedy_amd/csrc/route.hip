@@ -47,8 +47,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   const int t = blockIdx.x;
   if (sets.masks != nullptr) {
     // the blocks clear the mask sets of every layer between them
-    const int n = sets.n_sets * sets.E * sets.W;
-    for (int i = t * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) sets.masks[i] = 0ull;
+    const size_t n = sets.n_sets * set_layer_words(sets.E, sets.W * 64);
+    for (size_t i = t * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) sets.masks[i] = 0ull;
   }
   for (int i = t * blockDim.x + threadIdx.x; i < n_zero; i += gridDim.x * blockDim.x) zero[i] = 0;
   int tok = tokens[t];
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
           if constexpr (kRouteTPB > 1)
             __hip_atomic_fetch_or(&blk_bits[e], 1ull << (t & 63), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           else
-            __hip_atomic_fetch_or(a.masks + static_cast<size_t>(e) * a.W + (t >> 6), 1ull << (t & 63),
+            __hip_atomic_fetch_or(a.masks + set_word(a.E, e, t >> 6), 1ull << (t & 63),
                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           a.pinfo[static_cast<size_t>(t) * E + e] = make_int2(__float_as_int(wgt), lane);
         }
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kRouteThreads, PRELOAD ? 1 : 8) void route_kernel(R
       if (threadIdx.x < E) {
         const unsigned long long bits = blk_bits[threadIdx.x];
         if (bits != 0ull)
-          __hip_atomic_fetch_or(a.masks + static_cast<size_t>(threadIdx.x) * a.W + (t0 >> 6), bits,
+          __hip_atomic_fetch_or(a.masks + set_word(a.E, threadIdx.x, t0 >> 6), bits,
                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }

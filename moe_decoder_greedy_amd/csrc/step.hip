@@ -45,7 +45,7 @@ StepLayout layout(const moev_model& m, int T) {
   // sorted pair order [P] (without token sets)
   L.sorted = take(sets ? 0 : P * 4);
   // token sets: one mask set [E][W] per layer, pair entries [T][E]
-  L.masks = take(sets ? static_cast<size_t>(m.n_layers > 0 ? m.n_layers : 1) * m.n_routed * set_words(T) * 8 : 0);
+  L.masks = take(sets ? static_cast<size_t>(m.n_layers > 0 ? m.n_layers : 1) * set_layer_words(m.n_routed, T) * 8 : 0);
   L.pinfo = take(sets ? static_cast<size_t>(T) * m.n_routed * 8 : 0);
   L.y = take(P * m.hidden * 4);
   // gate/up activations: [P, I] in sorted order, or [G*T, I] by token set
@@ -193,7 +193,8 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
   // probe events around one stage (index = layer, or 0 for the head)
   auto mark = [&](int stage, int index, bool after) {
     if (probe == nullptr || probe->stage != stage || index >= probe->n) return;
-    hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
+    // a failed record stays in the runtime's last error, which launch_status reports
+    (void)hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
   };
 
   // Launches per layer: router (with the previous layer's combine folded in),
@@ -218,7 +219,7 @@ void run_layers(const moev_model* m, const int32_t* tokens, int T, const StepLay
       y_prev = at->ao;
       s_prev = 1;
     }
-    uint64_t* mk = masks + static_cast<size_t>(l) * E * W;
+    uint64_t* mk = masks + static_cast<size_t>(l) * set_layer_words(E, T);
     mark(MOEV_STAGE_ROUTE, l, false);
     launch_route_fused(h, y_prev, s_prev, h, lw.norm, m->eps, lw.w_router, lw.bias, T, H, E, k, dt, x,
                        idx, w, s, sets ? mk : nullptr, sets ? pinfo : nullptr);
@@ -271,7 +272,8 @@ moev_status run_step(const moev_model* m, const int32_t* tokens, int B, int K, i
   void* head_ws = base + L.head;
   auto mark = [&](int stage, int index, bool after) {
     if (probe == nullptr || probe->stage != stage || index >= probe->n) return;
-    hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
+    // a failed record stays in the runtime's last error, which launch_status reports
+    (void)hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
   };
   const int H = m->hidden, dt = m->dtype;
   // the head's last kernel also applies the prefix acceptance
@@ -324,12 +326,15 @@ moev_status run_prefill(const moev_model* m, const int32_t* tokens, int n_seq, i
   // residual stream, else only for the rows the head reads
   if (h_out != nullptr) {
     if (y != nullptr) launch_combine(y, h, T, m->hidden, S, h_out, s);
-    else hipMemcpyAsync(h_out, h, static_cast<size_t>(T) * m->hidden * 4, hipMemcpyDeviceToDevice, s);
+    else if (hipMemcpyAsync(h_out, h, static_cast<size_t>(T) * m->hidden * 4, hipMemcpyDeviceToDevice, s) !=
+             hipSuccess)
+      return launch_status("moev_prefill");
   }
   launch_gather_last(h, y, S, m->hidden, n_seq, seq_len, h_last, s);
   auto mark = [&](int stage, int index, bool after) {
     if (probe == nullptr || probe->stage != stage || index >= probe->n) return;
-    hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
+    // a failed record stays in the runtime's last error, which launch_status reports
+    (void)hipEventRecord(static_cast<hipEvent_t>(after ? probe->after[index] : probe->before[index]), s);
   };
   mark(MOEV_STAGE_HEAD, 0, false);
   launch_lmhead(h_last, m->norm_f, m->eps, m->w_lm, n_seq, m->hidden, m->vocab, m->dtype, next_token,
@@ -520,7 +525,6 @@ extern "C" moev_status moev_verify_step_attn(const moev_model* m, const moev_att
                A.total);
   unsigned char* base = static_cast<unsigned char*>(ws);
   const hipStream_t s = as_stream(stream);
-  const int T = B * (K + 1);
   const AttnHook at{a, B, K + 1, pos, reinterpret_cast<float*>(base + A.q),
                     reinterpret_cast<float*>(base + A.ao), reinterpret_cast<float*>(base + A.part),
                     reinterpret_cast<int*>(base + A.cnt)};
