@@ -73,7 +73,7 @@ struct RouteArgs {
   int32_t* topk_idx;
   float* topk_w;
   float* logits_out;
-  uint64_t* masks;       // token sets (optional): this layer's [E][W] masks
+  uint64_t* masks;       // token sets (optional): this layer's [W][E] mask words
   int2* pinfo;           //   and [T][E] pair entries {weight bits, slot}
   int W;
 };
