@@ -359,6 +359,16 @@ def test_step_matches_stage_chain_tiled_sets(decoder_pair, zipf_pair, B):
     _stage_chain_check(zipf_pair[1], 23 + B, B=B)
 
 
+@pytest.mark.parametrize("B", [25, 33, 75, 127])
+def test_step_matches_stage_chain_ragged_sets(decoder_pair, zipf_pair, B):
+    """Row counts that leave the last 64-bit mask word partly empty: 100 rows
+    (streaming schedule, two words), 132, 300 and 508 rows (tiled schedule,
+    three, five and eight words).  Same bits as the per-stage chain."""
+    _stage_chain_check(decoder_pair[1], 29 + B, B=B)
+    if B in (75, 127):
+        _stage_chain_check(zipf_pair[1], 31 + B, B=B)
+
+
 def test_step_matches_stage_chain_skewed(zipf_pair):
     """The same with skewed routing (per-layer Zipf(1.1) router bias), where
     some routed expert holds more than 32 of the 128 tokens: its token set

@@ -75,6 +75,10 @@ def test_prefill_decoder_pages(model_mod):
     # logits by a few 1e-3, so a row whose smallest 6th-vs-7th logit gap over
     # the layers is below 5e-3 may take another expert set and is not compared.
     _run(dm, w, n_seq=8, seq_len=1220, operands="bf16", tol=2.4e-2, sample_rows=rows, chain_gap=5e-3)
+    # 3 x 100 = 300 rows: the tiled schedule on the router's token sets (five
+    # mask words, the last one partly empty), same bounds
+    _run(dm, w, n_seq=3, seq_len=100, operands="bf16", tol=2.4e-2, sample_rows=[0, 99, 150, 251, 299],
+         chain_gap=5e-3)
 
 
 def test_prefill_small_and_edge(model_mod):
