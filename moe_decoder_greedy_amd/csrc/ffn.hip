@@ -1001,12 +1001,27 @@ __global__ __launch_bounds__((TileCfg<WT, BT>::kThreads), (TileCfg<WT, BT>::kPer
 #pragma unroll
       for (int j = 0; j < 4; ++j) frag(st, 16 + wt * 4 + j, B[j]);
     }
+    // While direct-to-LDS loads are in flight (always, in this loop) the
+    // compiler waits for every outstanding LDS read before an MFMA that needs
+    // one, so the weight fragments are read in batches ahead of their MFMAs:
+    // kAhead row tiles ahead (two for 256-token tiles, all eight up front for
+    // 128-token tiles; the fastest of 2, 3, 4 and 8 measured for each).  The
+    // group barriers keep that order.
+    constexpr int kAhead = BT == 256 ? 2 : 8;
+    constexpr int kRd = sizeof(WT) == 2 ? 1 : 2;  // LDS reads per fragment
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) frag(st, wr * 8 + rt, A[rt]);
+    for (int rt = 0; rt < kAhead; ++rt) frag(st, wr * 8 + rt, A[rt]);
+    __builtin_amdgcn_sched_group_barrier(0x100, (4 + kAhead) * kRd, 0);  // DS reads
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int rt = 0; rt < 8; ++rt) {
+      if (rt + kAhead < 8) {
+        frag(st, wr * 8 + rt + kAhead, A[rt + kAhead]);
+        __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[rt][j] = mma(A[rt], B[j], acc[rt][j]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMAs
+    }
     stage_barrier<(u % 2 == 0) ? kWaitEven : kWaitOdd>();
   };
 
