@@ -510,14 +510,21 @@ __device__ __forceinline__ void gemm_pass_lds(const GemmArgs& a, unsigned char* 
 #pragma unroll
     for (int j = 0; j < NTX; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Ring loads skipped past the last chunk make the number of loads in flight
+  // depend on the path, and the compiler then waits for all of them at the
+  // top of every ring round.  The down projection loads every slot instead
+  // (clamped to the last chunk), so its waits cover one slot's loads; for
+  // gate/up that measured slower at uniform routing, so it keeps the skips.
+  constexpr bool kAllLoads = MODE == kDown;
+  const int last = nchunks - 1;
   Frag<WT> ring[kNB][RT][kKB];
 #pragma unroll
   for (int u = 0; u < kNB; ++u)
-    if (u < nchunks)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int kk = 0; kk < kKB; ++kk) ring[u][rt][kk].load(wp[rt] + (u * kKB + kk) * kFrag);
+      for (int kk = 0; kk < kKB; ++kk)
+        if (kAllLoads || u < nchunks) ring[u][rt][kk].load(wp[rt] + (min(u, last) * kKB + kk) * kFrag);
 
   for (int c0 = 0; c0 < nchunks; c0 += kNB) {
 #pragma unroll
@@ -548,13 +555,12 @@ __device__ __forceinline__ void gemm_pass_lds(const GemmArgs& a, unsigned char* 
             for (int rt = 0; rt < RT; ++rt) acc[rt][j] = mma(ring[u][rt][kk], b, acc[rt][j]);
           }
         }
-        if (c + kNB < nchunks) {
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int kk = 0; kk < kKB; ++kk)
-              ring[u][rt][kk].load(wp[rt] + ((c + kNB) * kKB + kk) * kFrag);
-        }
+          for (int kk = 0; kk < kKB; ++kk)
+            if (kAllLoads || c + kNB < nchunks)
+              ring[u][rt][kk].load(wp[rt] + (min(c + kNB, last) * kKB + kk) * kFrag);
       }
     }
   }
