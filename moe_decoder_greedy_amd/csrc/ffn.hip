@@ -412,15 +412,21 @@ __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned cha
 #pragma unroll
     for (int j = 0; j < NTX; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // bf16 down projection: the steady-state loop below (the prologue then
+  // loads every slot, clamped to the range)
+  constexpr bool kSteady = sizeof(WT) == 2 && MODE == kDown;
   Frag<WT> rw[kNBD][RT], rx[kNBD][NTX];
 #pragma unroll
   for (int u = 0; u < kNBD; ++u)
-    if (kb_lo + u < nkb) {
+    if (kSteady || kb_lo + u < nkb) {
+      const int kb = min(kb_lo + u, nkb - 1);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) rw[u][rt].load(wp[rt] + (kb_lo + u) * kFrag);
+      for (int rt = 0; rt < RT; ++rt) rw[u][rt].load(wp[rt] + kb * kFrag);
 #pragma unroll
-      for (int j = 0; j < NTX; ++j) rx[u][j].load(xp[j] + (kb_lo + u) * 32);
+      for (int j = 0; j < NTX; ++j) rx[u][j].load(xp[j] + kb * 32);
     }
+  // the K loop as a ring of kNBD slots, loads skipped past the range
+  auto ring_loop = [&]() __attribute__((always_inline)) {
   for (int kb0 = kb_lo; kb0 < nkb; kb0 += kNBD) {
 #pragma unroll
     for (int u = 0; u < kNBD; ++u) {
@@ -438,6 +444,45 @@ __device__ __forceinline__ void gemm_pass_direct(const GemmArgs& a, unsigned cha
         }
       }
     }
+  }
+  };
+  if constexpr (kSteady) {
+    if ((nkb - kb_lo) % kNBD == 0) {
+      // Steady state: every round loads all of the next round's slots (all
+      // in range), so each wait covers one slot, and the last round loads
+      // nothing.  (The ring loop's skipped loads make the count of loads in
+      // flight path-dependent, and the compiler then drains the ring at the
+      // top of every round; for gate/up that drained loop measured faster,
+      // and this one does not fit its registers at two waves per SIMD.)
+      int kb0 = kb_lo;
+      for (; kb0 + kNBD < nkb; kb0 += kNBD) {
+#pragma unroll
+        for (int u = 0; u < kNBD; ++u) {
+#pragma unroll
+          for (int j = 0; j < NTX; ++j)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) acc[rt][j] = mma(rw[u][rt], rx[u][j], acc[rt][j]);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) rw[u][rt].load(wp[rt] + (kb0 + u + kNBD) * kFrag);
+#pragma unroll
+          for (int j = 0; j < NTX; ++j) rx[u][j].load(xp[j] + (kb0 + u + kNBD) * 32);
+          // each slot's loads right after its MFMAs (the scheduler would
+          // otherwise sink a round's loads to its end)
+          __builtin_amdgcn_sched_group_barrier(0x008, RT * NTX, 0);  // MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x020, RT + NTX, 0);  // vector memory reads
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kNBD; ++u)
+#pragma unroll
+        for (int j = 0; j < NTX; ++j)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt][j] = mma(rw[u][rt], rx[u][j], acc[rt][j]);
+    } else {
+      ring_loop();
+    }
+  } else {
+    ring_loop();
   }
   if constexpr (KS > 1) {
     __shared__ f32x4 red[KS - 1][RT][NTX][kWave];
