@@ -223,6 +223,31 @@ def test_grouped_ffn_tile_remainder(ops):
     assert np.array_equal(y_s.view(np.uint32), y[:Ts].view(np.uint32))
 
 
+@pytest.mark.parametrize("inter", [64, 128, 192])
+@pytest.mark.parametrize("T", [16, 100])
+def test_grouped_ffn_ring_ranges(ops, inter, T):
+    """bf16 down projections whose contraction is 2, 4 or 6 K blocks: shorter
+    than the weight ring, exactly one ring round (the steady-state loop with
+    only its last round), and not a whole number of rounds (the ring loop after
+    a clamped prologue); 16 tokens take the direct passes, 100 the shared
+    expert's LDS-staged pass (its ring loads clamped to the last chunk)."""
+    shape = dataclasses.replace(synth.DECODER, name=f"ring_i{inter}", hidden=256, n_routed=8, top_k=2,
+                                n_shared=1, inter=inter, n_layers=1)
+    L = synth.model_weights(shape, head=False)["layers"][0]
+    dt = "bf16"
+    report("grouped_ffn_ring_ranges", inter=inter, T=T)
+    x_op, idx, w32, off, src = _ffn_case(shape, L, dt, T, seed=29 + inter + T)
+    wg, wu, wd = (ops.pack_weights(dev_bits(L[key], dt)) for key in ("w_gate", "w_up", "w_down"))
+    y = host(ops.moe_grouped_ffn(dev_operand(x_op, dt), dev_i32(src), dev_i32(off), dev_f32(w32), wg, wu, wd,
+                                 shape.n_routed, shape.top_k, shape.n_shared))
+    args = (x_op, src, off, w32, L["w_gate"], L["w_up"], L["w_down"], dt, shape.top_k, shape.n_shared)
+    e_tight = max_abs(y, oracle.grouped_ffn(*args, round_act=True))
+    e_exact = max_abs(y, oracle.grouped_ffn(*args, round_act=False))
+    report("grouped_ffn_ring_ranges", inter=inter, T=T, err_vs_bf16_operands=e_tight, err_vs_exact=e_exact)
+    assert e_exact < BAR[dt]
+    assert e_tight < 1e-3
+
+
 # ------------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("T,S,H", [(128, 8, 1280), (37, 3, 128), (1, 1, 64)])
